@@ -1,0 +1,178 @@
+/*
+ * kv_quant.h -- C ABI of libkvq: single-token decode over a paged KV cache stored as packed
+ * symmetric INT2 / INT4 / INT8 codes with a bit-width chosen per layer, for AMD MI355X (gfx950).
+ *
+ * The operations follow three web pages on mixed-precision KV-cache quantization:
+ *   [EchoKV]  "EchoKV: watching a language model decide its own precision"
+ *   [RoleKV]  "Behavior-Guided KV-Cache Quantization"
+ *   [Kaizen]  "KV-Kaizen: Learning Context-Adaptive Cache Compression Choices" (summary)
+ *
+ * Conventions for every call:
+ *   - Plain C99 types only. fp16 values travel as uint16_t bit patterns.
+ *   - "dev" pointers are HIP device memory owned by the caller; the library never allocates,
+ *     frees or retains device memory. "host" pointers are ordinary host memory.
+ *   - Kernel calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL = the null
+ *     stream). The caller synchronizes before reading results on the host.
+ *   - Every argument is checked on the host before anything is launched; on error the call
+ *     returns a nonzero kv_status, launches nothing and changes nothing. kv_last_error() then
+ *     holds a one-line description (thread-local). Contents of device buffers (block handles,
+ *     lengths) are not checked on the hot path: out-of-range contents give undefined results.
+ *   - Inputs are finite fp16 values; a product |q_c| * max|K_c| / qmax beyond the fp16 range is
+ *     outside the supported domain.
+ *
+ * Storage format (the pages fix none of it; it is this library's):
+ *   tier 0, 1, 2  <->  b = 2, 4, 8 bits;  qmax_b = 2^(b-1) - 1;  codes q in [-qmax_b, qmax_b].
+ *   block handle = (tier << 30) | block_index;  KV_NO_BLOCK = 0xFFFFFFFF.
+ *   One block = one page of P tokens of one layer, all KV heads: H_kv sections of
+ *   S_b = P*D*b/4 + 2*D + 2*P bytes (head h at h*S_b); block j of a tier pool is at j*H_kv*S_b.
+ *   A section holds, in order:
+ *     K codes  P*D*b/8 bytes, code sequence index of (token t, channel c) = t*D + c
+ *     K scales D fp16, one per channel over the page's tokens      ([RoleKV] keys per channel)
+ *     V codes  P*D*b/8 bytes, code sequence index of (t, c) = ((t/4)*D + c)*4 + t%4
+ *     V scales P fp16, one per token over its D channels           ([RoleKV] values per token)
+ *   A code sequence is stored as little-endian 32-bit words of 32/b codes; code k of a word is
+ *   the unsigned field q + 2^(b-1) at bit 16*(k%2) + b*(k/2). Token slots of a page that hold
+ *   no token carry the zero code and a zero scale.
+ *   Quantizer over a group with absolute maximum a: scale s = smallest fp16 >= a/qmax_b
+ *   (0 if a == 0), code = round-half-even(x/s); both decided in IEEE binary32, which equals the
+ *   exact rational result for fp16 inputs ([Kaizen] "symmetric uniform quantization").
+ */
+#ifndef KV_QUANT_H
+#define KV_QUANT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KV_ABI_VERSION 1
+#define KV_NO_BLOCK 0xFFFFFFFFu
+
+typedef enum {
+    KV_OK = 0,
+    KV_EINVAL = 1,        /* an argument is out of range or a pointer is NULL */
+    KV_ENOBLOCKS = 2,     /* a tier pool has too few free blocks (allocator unchanged) */
+    KV_EUNSUPPORTED = 3,  /* valid but not built: head_dim not 64/128, GQA group > 16, ... */
+    KV_EHIP = 4           /* the HIP runtime reported an error; see kv_last_error() */
+} kv_status;
+
+typedef struct {
+    int32_t num_layers;
+    int32_t num_q_heads;        /* H_q; a multiple of num_kv_heads, group H_q/H_kv <= 16 */
+    int32_t num_kv_heads;       /* H_kv */
+    int32_t head_dim;           /* D: 64 or 128 */
+    int32_t page_size;          /* P: 16 */
+    int32_t ring_size;          /* R: FP16 key ring per sequence, a multiple of P, P..128 */
+    int32_t max_seqs;           /* rows of a block table / ring */
+    int32_t max_pages_per_seq;  /* columns of a block table */
+} kv_geometry;
+
+/* the three tier pools of one layer: base[t] holds capacity[t] blocks of kv_block_bytes(g, b_t);
+   each base is 16-byte aligned device memory (or NULL with capacity 0) */
+typedef struct {
+    void* base[3];
+    uint32_t capacity[3];
+} kv_layer_pools;
+
+/* ---------------------------------------------------------------- version, errors, sizes */
+int         kv_abi_version(void);
+const char* kv_strerror(kv_status status);
+const char* kv_last_error(void);                    /* thread-local; "" when none */
+kv_status   kv_validate(const kv_geometry* g);
+uint32_t    kv_handle(int bits, uint32_t index);     /* KV_NO_BLOCK for bad bits or index */
+size_t      kv_block_bytes(const kv_geometry* g, int bits);  /* one block, all KV heads; 0 if invalid */
+size_t      kv_ring_bytes(const kv_geometry* g);    /* one layer's ring: max_seqs*R*H_kv*D*2 */
+/* bytes of cache per token over all layers, bits_per_layer[l] in {2,4,8} or 16 (plain fp16);
+   [Kaizen] "Action Space and Cost Model": C0 = L*2*n_kv*d_h*16 bits for the fp16 cache */
+double      kv_cache_bytes_per_token(const kv_geometry* g, const int* bits_per_layer);
+
+/* ---------------------------------------------------------------- tier / block-table setup
+ * Host-side block allocator ([EchoKV] "How EchoKV works": the tier vector routes future blocks
+ * to the right pool; "What happens to old blocks...": already-allocated blocks keep their
+ * admit-time width). One pool per (layer, tier); each hands out its blocks in a seeded random
+ * order (shuffled physical block tables). Not thread-safe; the library owns the object.
+ * Block tables are host arrays bt_host[L][max_seqs][max_pages_per_seq] of handles; the caller
+ * copies the rows it needs to the device (one [max_seqs][max_pages_per_seq] table per layer). */
+typedef struct kv_alloc kv_alloc;
+
+/* capacity[l*3 + t] blocks in pool (l, t); bits[l] in {2,4,8} is layer l's current tier */
+kv_status kv_alloc_create(const kv_geometry* g, const uint32_t* capacity, const int* bits,
+                          uint64_t shuffle_seed, kv_alloc** out);
+/* forward-only: later pages of the layer come from the new tier's pool; existing blocks,
+   including the page being filled, keep their tier */
+kv_status kv_alloc_set_layer_bits(kv_alloc* a, int layer, int bits);
+/* grow sequence `seq` to new_len tokens in every layer (all-or-nothing: KV_ENOBLOCKS leaves
+   the allocator and bt_host untouched); writes the new handles into bt_host */
+kv_status kv_alloc_extend(kv_alloc* a, int seq, int32_t new_len, uint32_t* bt_host);
+/* return every block of `seq` to its pool and reset its bt_host rows to KV_NO_BLOCK */
+kv_status kv_alloc_free_seq(kv_alloc* a, int seq, uint32_t* bt_host);
+int32_t   kv_alloc_seq_len(const kv_alloc* a, int seq);              /* -1 if seq invalid */
+int64_t   kv_alloc_free_blocks(const kv_alloc* a, int layer, int bits); /* -1 if invalid */
+int       kv_alloc_layer_bits(const kv_alloc* a, int layer);          /* 0 if invalid */
+void      kv_alloc_destroy(kv_alloc* a);
+/* CPU check of a host block table against the allocator: every page below the sequence
+   length holds a valid handle, no block is used twice, every other entry is KV_NO_BLOCK */
+kv_status kv_check_block_table(const kv_alloc* a, const uint32_t* bt_host);
+
+/* ---------------------------------------------------------------- quantize-on-write
+ * [EchoKV] "How EchoKV works": each step's key is written into the layer's FP16 ring before it
+ * is quantized into the paged cache. [RoleKV] "K/V Role-Aware Low-Bit Quantization": keys per
+ * channel, values per token; "Online inference": write quantized KV = pack and store.
+ *
+ * One layer, `batch` sequences (rows 0..batch-1 of bt, pos, ring), n_new tokens each:
+ *   bt     dev uint32 [max_seqs][max_pages_per_seq]  handles; every page touched must be allocated
+ *   pos    dev int32  [batch]      tokens already cached in each sequence
+ *   k_new, v_new  dev fp16 [batch][n_new][H_kv][D]
+ *   ring   dev fp16 [max_seqs][R][H_kv][D], in/out: position p lives in slot p % R
+ * For every page touched, the K scales and codes of all its present tokens are recomputed from
+ * their FP16 originals (ring for positions < pos, k_new after), so writing token by token gives
+ * the same bytes as writing at once. Each new value vector gets its own scale; codes of earlier
+ * tokens are kept. Afterwards the ring holds the new keys. n_new == 0 is a no-op. */
+kv_status kv_quant_write(const kv_geometry* g, const kv_layer_pools* pools, const uint32_t* bt,
+                         const int32_t* pos, int batch, int n_new, const uint16_t* k_new,
+                         const uint16_t* v_new, uint16_t* ring, void* stream);
+
+/* ---------------------------------------------------------------- decode attention
+ * [EchoKV] "What happens to old blocks...": paged attention reads each block at its stored
+ * width, so one layer may mix widths. [RoleKV] "Storage savings": GQA head mapping; query head
+ * h reads KV head h / (H_q/H_kv).
+ *   out[s][h][:] = sum_t w_t V^_t / sum_t w_t,  w_t = exp(l_t - max l),
+ *   l_t = softmax_scale * sum_c q[s][h][c] K^_t[c],  t in [0, ctx_len[s]),
+ *   K^_t[c] = code * K scale of (page of t, c),  V^_t[c] = code * V scale of t.
+ *   ctx_len  dev int32 [batch], each in [0, max_ctx_len]; a zero length gives a zero row
+ *   q        dev fp16 [batch][H_q][D];  out  dev fp32 [batch][H_q][D]
+ *   max_ctx_len    host upper bound on ctx_len, sizes the launch (<= max_pages_per_seq * P)
+ *   pages_per_split  pages one workgroup reads (a multiple of 16); 0 = chosen by the library
+ *   workspace  dev, >= kv_decode_workspace_bytes(...) bytes, zero-filled before its first use;
+ *              the call leaves it ready for the next call. One workspace per in-flight call.
+ * The split-K partials are merged in a fixed order, so results are bitwise reproducible. */
+size_t    kv_decode_workspace_bytes(const kv_geometry* g, int batch, int max_ctx_len,
+                                    int pages_per_split);
+int       kv_decode_pages_per_split(const kv_geometry* g, int batch, int max_ctx_len);
+kv_status kv_decode_attn(const kv_geometry* g, const kv_layer_pools* pools, const uint32_t* bt,
+                         const int32_t* ctx_len, int batch, int max_ctx_len, const uint16_t* q,
+                         float softmax_scale, float* out, void* workspace,
+                         size_t workspace_bytes, int pages_per_split, void* stream);
+
+/* ---------------------------------------------------------------- canary
+ * [EchoKV] "Show the math": delta_b = KL(softmax(Q K_ref^T) || softmax(Q quant_b(K_ref)^T)),
+ * summed over keys, averaged over queries; one number per b in {2, 4, 8}. K_ref is the ring:
+ * for each sequence the n = min(seq_len[s], R) newest keys (positions seq_len-n .. seq_len-1).
+ * quant_b is the cache's own quantizer, grouped by each key's page (one scale per page and
+ * channel); the copies are temporary. Rows use the softmax_scale of attention.
+ *   ring     dev fp16 [max_seqs][R][H_kv][D];  seq_len dev int32 [batch], >= 0
+ *   q        dev fp16 [batch][H_q][D]
+ *   kl_out   dev fp32 [3]: mean over batch*H_q rows for b = 2, 4, 8
+ *   kl_rows  dev fp32 [batch][H_q][3] or NULL
+ *   workspace dev, >= kv_canary_workspace_bytes(g, batch), zero-filled before its first use */
+size_t    kv_canary_workspace_bytes(const kv_geometry* g, int batch);
+kv_status kv_canary_kl(const kv_geometry* g, const uint16_t* ring, const int32_t* seq_len,
+                       int batch, const uint16_t* q, float softmax_scale, float* kl_out,
+                       float* kl_rows, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KV_QUANT_H */

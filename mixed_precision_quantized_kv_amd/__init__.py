@@ -1,0 +1,243 @@
+"""Thin ctypes binding of libkvq (include/kv_quant.h), the MI355X mixed-precision quantized
+KV-cache decode path. Names match the C ABI; this module only marshals arguments.
+
+Device buffers are passed as torch tensors (their data_ptr()) or raw integer addresses; the
+stream defaults to torch's current stream. Every nonzero status raises KVError with the
+library's own message. The library is loaded on first use and its absence is an error: there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvq.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "kv_quant.h")
+
+KV_OK, KV_EINVAL, KV_ENOBLOCKS, KV_EUNSUPPORTED, KV_EHIP = range(5)
+KV_NO_BLOCK = 0xFFFFFFFF
+TIER_BITS = (2, 4, 8)
+
+
+class KVError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[{status}] {msg}")
+        self.status = status
+
+
+class Geometry(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_layers", "num_q_heads", "num_kv_heads", "head_dim", "page_size", "ring_size",
+        "max_seqs", "max_pages_per_seq")]
+
+
+class LayerPools(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p * 3), ("capacity", ctypes.c_uint32 * 3)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m mixed_precision_quantized_kv_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, u32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint32, ctypes.c_size_t
+        G = ctypes.POINTER(Geometry)
+        sigs = {
+            "kv_abi_version": (i32, []),
+            "kv_strerror": (ctypes.c_char_p, [i32]),
+            "kv_last_error": (ctypes.c_char_p, []),
+            "kv_validate": (i32, [G]),
+            "kv_handle": (u32, [i32, u32]),
+            "kv_block_bytes": (sz, [G, i32]),
+            "kv_ring_bytes": (sz, [G]),
+            "kv_cache_bytes_per_token": (ctypes.c_double, [G, P]),
+            "kv_alloc_create": (i32, [G, P, P, ctypes.c_uint64, ctypes.POINTER(P)]),
+            "kv_alloc_set_layer_bits": (i32, [P, i32, i32]),
+            "kv_alloc_extend": (i32, [P, i32, ctypes.c_int32, P]),
+            "kv_alloc_free_seq": (i32, [P, i32, P]),
+            "kv_alloc_seq_len": (ctypes.c_int32, [P, i32]),
+            "kv_alloc_free_blocks": (ctypes.c_int64, [P, i32, i32]),
+            "kv_alloc_layer_bits": (i32, [P, i32]),
+            "kv_alloc_destroy": (None, [P]),
+            "kv_check_block_table": (i32, [P, P]),
+            "kv_quant_write": (i32, [G, ctypes.POINTER(LayerPools), P, P, i32, i32, P, P, P, P]),
+            "kv_decode_workspace_bytes": (sz, [G, i32, i32, i32]),
+            "kv_decode_pages_per_split": (i32, [G, i32, i32]),
+            "kv_decode_attn": (i32, [G, ctypes.POINTER(LayerPools), P, P, i32, i32, P,
+                                     ctypes.c_float, P, P, sz, i32, P]),
+            "kv_canary_workspace_bytes": (sz, [G, i32]),
+            "kv_canary_kl": (i32, [G, P, P, i32, P, ctypes.c_float, P, P, P, sz, P]),
+        }
+        for name, (res, args) in sigs.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def header_symbols() -> list:
+    """Every function the public header declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(kv_[a-z_0-9]+)\s*\(", text)) - {"kv_alloc"})
+
+
+def _check(status: int) -> None:
+    if status != KV_OK:
+        raise KVError(status, lib().kv_last_error().decode() or lib().kv_strerror(status).decode())
+
+
+def _addr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if hasattr(x, "ctypes"):                    # numpy (host arrays)
+        return x.ctypes.data
+    raise TypeError(f"cannot take the address of {type(x)}")
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def geometry(num_layers, num_q_heads, num_kv_heads, head_dim, max_seqs, max_pages_per_seq,
+             page_size=16, ring_size=64) -> Geometry:
+    return Geometry(num_layers, num_q_heads, num_kv_heads, head_dim, page_size, ring_size,
+                    max_seqs, max_pages_per_seq)
+
+
+def layer_pools(bases, capacities) -> LayerPools:
+    p = LayerPools()
+    for t in range(3):
+        p.base[t] = _addr(bases[t]) or None
+        p.capacity[t] = int(capacities[t])
+    return p
+
+
+# ------------------------------------------------------------------ sizes and validation
+def kv_abi_version() -> int:
+    return lib().kv_abi_version()
+
+
+def kv_validate(g: Geometry) -> None:
+    _check(lib().kv_validate(ctypes.byref(g)))
+
+
+def kv_handle(bits: int, index: int) -> int:
+    return lib().kv_handle(bits, index)
+
+
+def kv_block_bytes(g: Geometry, bits: int) -> int:
+    return lib().kv_block_bytes(ctypes.byref(g), bits)
+
+
+def kv_ring_bytes(g: Geometry) -> int:
+    return lib().kv_ring_bytes(ctypes.byref(g))
+
+
+def kv_cache_bytes_per_token(g: Geometry, bits_per_layer) -> float:
+    arr = (ctypes.c_int * len(bits_per_layer))(*bits_per_layer)
+    return lib().kv_cache_bytes_per_token(ctypes.byref(g), arr)
+
+
+def kv_decode_workspace_bytes(g: Geometry, batch: int, max_ctx_len: int, pages_per_split=0) -> int:
+    return lib().kv_decode_workspace_bytes(ctypes.byref(g), batch, max_ctx_len, pages_per_split)
+
+
+def kv_decode_pages_per_split(g: Geometry, batch: int, max_ctx_len: int) -> int:
+    return lib().kv_decode_pages_per_split(ctypes.byref(g), batch, max_ctx_len)
+
+
+def kv_canary_workspace_bytes(g: Geometry, batch: int) -> int:
+    return lib().kv_canary_workspace_bytes(ctypes.byref(g), batch)
+
+
+# ------------------------------------------------------------------ allocator
+class KVAlloc:
+    """kv_alloc_* on a host block table bt_host [L][max_seqs][max_pages] (numpy uint32)."""
+
+    def __init__(self, g: Geometry, capacity, bits, shuffle_seed: int = 0):
+        import numpy as np
+        self.g = g
+        cap = np.ascontiguousarray(capacity, dtype=np.uint32).reshape(-1)
+        b = np.ascontiguousarray(bits, dtype=np.int32)
+        h = ctypes.c_void_p()
+        _check(lib().kv_alloc_create(ctypes.byref(g), cap.ctypes.data, b.ctypes.data,
+                                     shuffle_seed, ctypes.byref(h)))
+        self.handle = h.value
+        self.bt = np.full((g.num_layers, g.max_seqs, g.max_pages_per_seq), KV_NO_BLOCK,
+                          dtype=np.uint32)
+
+    def kv_alloc_set_layer_bits(self, layer: int, bits: int) -> None:
+        _check(lib().kv_alloc_set_layer_bits(self.handle, layer, bits))
+
+    def kv_alloc_extend(self, seq: int, new_len: int) -> None:
+        _check(lib().kv_alloc_extend(self.handle, seq, new_len, self.bt.ctypes.data))
+
+    def kv_alloc_free_seq(self, seq: int) -> None:
+        _check(lib().kv_alloc_free_seq(self.handle, seq, self.bt.ctypes.data))
+
+    def kv_alloc_seq_len(self, seq: int) -> int:
+        return lib().kv_alloc_seq_len(self.handle, seq)
+
+    def kv_alloc_free_blocks(self, layer: int, bits: int) -> int:
+        return lib().kv_alloc_free_blocks(self.handle, layer, bits)
+
+    def kv_alloc_layer_bits(self, layer: int) -> int:
+        return lib().kv_alloc_layer_bits(self.handle, layer)
+
+    def kv_check_block_table(self, bt=None) -> None:
+        bt = self.bt if bt is None else bt
+        _check(lib().kv_check_block_table(self.handle, bt.ctypes.data))
+
+    def kv_alloc_destroy(self) -> None:
+        if self.handle:
+            lib().kv_alloc_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.kv_alloc_destroy()
+        except Exception:
+            pass
+
+
+# ------------------------------------------------------------------ the three kernels
+def kv_quant_write(g: Geometry, pools: LayerPools, bt, pos, batch: int, n_new: int, k_new, v_new,
+                   ring, stream=None) -> None:
+    _check(lib().kv_quant_write(ctypes.byref(g), ctypes.byref(pools), _addr(bt), _addr(pos), batch,
+                                n_new, _addr(k_new), _addr(v_new), _addr(ring), _stream(stream)))
+
+
+def kv_decode_attn(g: Geometry, pools: LayerPools, bt, ctx_len, batch: int, max_ctx_len: int, q,
+                   softmax_scale: float, out, workspace, workspace_bytes=None,
+                   pages_per_split: int = 0, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().kv_decode_attn(ctypes.byref(g), ctypes.byref(pools), _addr(bt), _addr(ctx_len),
+                                batch, max_ctx_len, _addr(q), softmax_scale, _addr(out),
+                                _addr(workspace), workspace_bytes, pages_per_split,
+                                _stream(stream)))
+
+
+def kv_canary_kl(g: Geometry, ring, seq_len, batch: int, q, softmax_scale: float, kl_out,
+                 kl_rows, workspace, workspace_bytes=None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().kv_canary_kl(ctypes.byref(g), _addr(ring), _addr(seq_len), batch, _addr(q),
+                              softmax_scale, _addr(kl_out), _addr(kl_rows), _addr(workspace),
+                              workspace_bytes, _stream(stream)))

@@ -1,0 +1,388 @@
+// kv_api.cpp -- the C ABI of libkvq (include/kv_quant.h): argument validation, byte sizes,
+// the host block allocator, and dispatch to the gfx950 kernels.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "kv_quant.h"
+#include "kvq_device.hpp"
+#include "kvq_launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+kv_status fail(kv_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+kv_status ok() {
+    g_last_error[0] = '\0';
+    return KV_OK;
+}
+
+kv_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(KV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int tier_of_bits(int bits) { return bits == 2 ? 0 : bits == 4 ? 1 : bits == 8 ? 2 : -1; }
+
+kv_status check_geometry(const kv_geometry* g) {
+    if (!g) return fail(KV_EINVAL, "geometry is NULL");
+    if (g->num_layers < 1 || g->num_q_heads < 1 || g->num_kv_heads < 1 || g->max_seqs < 1 ||
+        g->max_pages_per_seq < 1)
+        return fail(KV_EINVAL, "geometry counts must be positive");
+    if (g->num_q_heads % g->num_kv_heads != 0)
+        return fail(KV_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                    g->num_q_heads, g->num_kv_heads);
+    if (g->page_size != kvq::kPage) return fail(KV_EUNSUPPORTED, "page_size must be 16");
+    if (g->ring_size < g->page_size || g->ring_size > 128 || g->ring_size % g->page_size != 0)
+        return fail(KV_EINVAL, "ring_size %d must be a multiple of page_size in [16, 128]",
+                    g->ring_size);
+    if (g->head_dim != 64 && g->head_dim != 128)
+        return fail(KV_EUNSUPPORTED, "head_dim %d: only 64 and 128 are built", g->head_dim);
+    if (g->num_q_heads / g->num_kv_heads > kvq::kMaxGroup)
+        return fail(KV_EUNSUPPORTED, "GQA group %d exceeds 16", g->num_q_heads / g->num_kv_heads);
+    if ((int64_t)g->max_pages_per_seq * g->page_size > (int64_t)1 << 30)
+        return fail(KV_EINVAL, "max_pages_per_seq too large");
+    return ok();
+}
+
+kv_status check_pools(const kv_geometry* g, const kv_layer_pools* p) {
+    if (!p) return fail(KV_EINVAL, "pools is NULL");
+    for (int t = 0; t < 3; ++t) {
+        if (p->capacity[t] > 0x3fffffffu) return fail(KV_EINVAL, "pool %d capacity too large", t);
+        if (p->capacity[t] > 0 && !p->base[t]) return fail(KV_EINVAL, "pool %d base is NULL", t);
+        if (reinterpret_cast<uintptr_t>(p->base[t]) % 16 != 0)
+            return fail(KV_EINVAL, "pool %d base is not 16-byte aligned", t);
+    }
+    (void)g;
+    return ok();
+}
+
+kvq::PoolPtrs pool_ptrs(const kv_layer_pools* p) {
+    kvq::PoolPtrs r;
+    for (int t = 0; t < 3; ++t) r.base[t] = static_cast<uint8_t*>(p->base[t]);
+    return r;
+}
+
+// splitmix64: seeded shuffles of each pool's free list
+uint64_t splitmix64(uint64_t& x) {
+    uint64_t z = (x += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+int auto_pages_per_split(const kv_geometry& g, int batch, int max_pages) {
+    // enough workgroups to give each of the 256 CUs one, pairs of pages per wave, and at
+    // most 256 splits per (sequence, KV head)
+    const int64_t groups = (int64_t)batch * g.num_kv_heads;
+    int64_t want_wg = 256;
+    int64_t pps = (groups * max_pages + want_wg - 1) / want_wg;
+    pps = std::max<int64_t>(pps, 16);
+    pps = std::max<int64_t>(pps, (max_pages + 255) / 256);
+    pps = (pps + 15) / 16 * 16;
+    return (int)pps;
+}
+
+}  // namespace
+
+struct kv_alloc {
+    kv_geometry g;
+    std::vector<int> bits;                       // current tier of each layer
+    std::vector<uint32_t> capacity;              // [L][3]
+    std::vector<std::vector<uint32_t>> free;     // [L*3]: free block indices, next at back
+    std::vector<int32_t> len;                    // tokens per sequence
+};
+
+extern "C" {
+
+int kv_abi_version(void) { return KV_ABI_VERSION; }
+
+const char* kv_strerror(kv_status s) {
+    switch (s) {
+        case KV_OK: return "ok";
+        case KV_EINVAL: return "invalid argument";
+        case KV_ENOBLOCKS: return "pool exhausted";
+        case KV_EUNSUPPORTED: return "unsupported configuration";
+        case KV_EHIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* kv_last_error(void) { return g_last_error; }
+
+kv_status kv_validate(const kv_geometry* g) { return check_geometry(g); }
+
+uint32_t kv_handle(int bits, uint32_t index) {
+    const int t = tier_of_bits(bits);
+    if (t < 0 || index > 0x3fffffffu) return KV_NO_BLOCK;
+    return ((uint32_t)t << 30) | index;
+}
+
+size_t kv_block_bytes(const kv_geometry* g, int bits) {
+    if (check_geometry(g) != KV_OK || tier_of_bits(bits) < 0) return 0;
+    return (size_t)g->num_kv_heads * kvq::section_layout(g->head_dim, bits).bytes;
+}
+
+size_t kv_ring_bytes(const kv_geometry* g) {
+    if (check_geometry(g) != KV_OK) return 0;
+    return (size_t)g->max_seqs * g->ring_size * g->num_kv_heads * g->head_dim * 2;
+}
+
+double kv_cache_bytes_per_token(const kv_geometry* g, const int* bits) {
+    if (check_geometry(g) != KV_OK || !bits) return -1.0;
+    double total = 0.0;
+    for (int l = 0; l < g->num_layers; ++l) {
+        if (bits[l] == 16)
+            total += 4.0 * g->num_kv_heads * g->head_dim;
+        else if (tier_of_bits(bits[l]) >= 0)
+            total += (double)kv_block_bytes(g, bits[l]) / g->page_size;
+        else
+            return -1.0;
+    }
+    return total;
+}
+
+// ---------------------------------------------------------------- allocator
+kv_status kv_alloc_create(const kv_geometry* g, const uint32_t* capacity, const int* bits,
+                          uint64_t shuffle_seed, kv_alloc** out) {
+    kv_status st = check_geometry(g);
+    if (st != KV_OK) return st;
+    if (!capacity || !bits || !out) return fail(KV_EINVAL, "NULL argument");
+    for (int l = 0; l < g->num_layers; ++l) {
+        if (tier_of_bits(bits[l]) < 0) return fail(KV_EINVAL, "layer %d bits %d", l, bits[l]);
+        for (int t = 0; t < 3; ++t)
+            if (capacity[l * 3 + t] > 0x3fffffffu) return fail(KV_EINVAL, "capacity too large");
+    }
+    kv_alloc* a = new (std::nothrow) kv_alloc;
+    if (!a) return fail(KV_EINVAL, "out of host memory");
+    a->g = *g;
+    a->bits.assign(bits, bits + g->num_layers);
+    a->capacity.assign(capacity, capacity + 3 * g->num_layers);
+    a->free.resize(3 * (size_t)g->num_layers);
+    uint64_t x = shuffle_seed;
+    for (size_t i = 0; i < a->free.size(); ++i) {
+        std::vector<uint32_t>& f = a->free[i];
+        f.resize(a->capacity[i]);
+        for (uint32_t j = 0; j < a->capacity[i]; ++j) f[j] = j;
+        for (size_t j = f.size(); j > 1; --j) std::swap(f[j - 1], f[splitmix64(x) % j]);
+        std::reverse(f.begin(), f.end());     // handed out from the back
+    }
+    a->len.assign(g->max_seqs, 0);
+    *out = a;
+    return ok();
+}
+
+kv_status kv_alloc_set_layer_bits(kv_alloc* a, int layer, int bits) {
+    if (!a) return fail(KV_EINVAL, "allocator is NULL");
+    if (layer < 0 || layer >= a->g.num_layers) return fail(KV_EINVAL, "layer %d", layer);
+    if (tier_of_bits(bits) < 0) return fail(KV_EINVAL, "bits %d", bits);
+    a->bits[layer] = bits;
+    return ok();
+}
+
+kv_status kv_alloc_extend(kv_alloc* a, int seq, int32_t new_len, uint32_t* bt) {
+    if (!a || !bt) return fail(KV_EINVAL, "NULL argument");
+    const kv_geometry& g = a->g;
+    if (seq < 0 || seq >= g.max_seqs) return fail(KV_EINVAL, "seq %d", seq);
+    const int32_t old_len = a->len[seq];
+    if (new_len < old_len) return fail(KV_EINVAL, "new_len %d below current %d", new_len, old_len);
+    const int64_t old_pages = (old_len + g.page_size - 1) / g.page_size;
+    const int64_t new_pages = ((int64_t)new_len + g.page_size - 1) / g.page_size;
+    if (new_pages > g.max_pages_per_seq)
+        return fail(KV_EINVAL, "%lld pages exceed max_pages_per_seq", (long long)new_pages);
+    const int64_t need = new_pages - old_pages;
+    for (int l = 0; l < g.num_layers; ++l) {
+        const std::vector<uint32_t>& f = a->free[(size_t)l * 3 + tier_of_bits(a->bits[l])];
+        if ((int64_t)f.size() < need)
+            return fail(KV_ENOBLOCKS, "layer %d: %lld free INT%d blocks, %lld needed", l,
+                        (long long)f.size(), a->bits[l], (long long)need);
+    }
+    for (int l = 0; l < g.num_layers; ++l) {
+        const int t = tier_of_bits(a->bits[l]);
+        std::vector<uint32_t>& f = a->free[(size_t)l * 3 + t];
+        uint32_t* row = bt + ((size_t)l * g.max_seqs + seq) * g.max_pages_per_seq;
+        for (int64_t p = old_pages; p < new_pages; ++p) {
+            row[p] = ((uint32_t)t << 30) | f.back();
+            f.pop_back();
+        }
+    }
+    a->len[seq] = new_len;
+    return ok();
+}
+
+kv_status kv_alloc_free_seq(kv_alloc* a, int seq, uint32_t* bt) {
+    if (!a || !bt) return fail(KV_EINVAL, "NULL argument");
+    const kv_geometry& g = a->g;
+    if (seq < 0 || seq >= g.max_seqs) return fail(KV_EINVAL, "seq %d", seq);
+    const int64_t pages = (a->len[seq] + g.page_size - 1) / g.page_size;
+    for (int l = 0; l < g.num_layers; ++l) {
+        uint32_t* row = bt + ((size_t)l * g.max_seqs + seq) * g.max_pages_per_seq;
+        for (int64_t p = 0; p < pages; ++p) {
+            const uint32_t h = row[p];
+            if (h == KV_NO_BLOCK) continue;
+            const uint32_t t = h >> 30;
+            if (t < 3 && (h & 0x3fffffffu) < a->capacity[(size_t)l * 3 + t])
+                a->free[(size_t)l * 3 + t].push_back(h & 0x3fffffffu);
+        }
+        for (int64_t p = 0; p < g.max_pages_per_seq; ++p) row[p] = KV_NO_BLOCK;
+    }
+    a->len[seq] = 0;
+    return ok();
+}
+
+int32_t kv_alloc_seq_len(const kv_alloc* a, int seq) {
+    if (!a || seq < 0 || seq >= a->g.max_seqs) return -1;
+    return a->len[seq];
+}
+
+int64_t kv_alloc_free_blocks(const kv_alloc* a, int layer, int bits) {
+    if (!a || layer < 0 || layer >= a->g.num_layers || tier_of_bits(bits) < 0) return -1;
+    return (int64_t)a->free[(size_t)layer * 3 + tier_of_bits(bits)].size();
+}
+
+int kv_alloc_layer_bits(const kv_alloc* a, int layer) {
+    if (!a || layer < 0 || layer >= a->g.num_layers) return 0;
+    return a->bits[layer];
+}
+
+void kv_alloc_destroy(kv_alloc* a) { delete a; }
+
+kv_status kv_check_block_table(const kv_alloc* a, const uint32_t* bt) {
+    if (!a || !bt) return fail(KV_EINVAL, "NULL argument");
+    const kv_geometry& g = a->g;
+    for (int l = 0; l < g.num_layers; ++l) {
+        std::vector<std::vector<uint8_t>> used(3);
+        for (int t = 0; t < 3; ++t) used[t].assign(a->capacity[(size_t)l * 3 + t], 0);
+        for (int s = 0; s < g.max_seqs; ++s) {
+            const uint32_t* row = bt + ((size_t)l * g.max_seqs + s) * g.max_pages_per_seq;
+            const int64_t pages = (a->len[s] + g.page_size - 1) / g.page_size;
+            for (int64_t p = 0; p < g.max_pages_per_seq; ++p) {
+                const uint32_t h = row[p];
+                if (p >= pages) {
+                    if (h != KV_NO_BLOCK)
+                        return fail(KV_EINVAL, "layer %d seq %d page %lld: stale handle", l, s,
+                                    (long long)p);
+                    continue;
+                }
+                const uint32_t t = h >> 30, i = h & 0x3fffffffu;
+                if (h == KV_NO_BLOCK || t > 2 || i >= a->capacity[(size_t)l * 3 + t])
+                    return fail(KV_EINVAL, "layer %d seq %d page %lld: invalid handle 0x%08x", l,
+                                s, (long long)p, h);
+                if (used[t][i]++)
+                    return fail(KV_EINVAL, "layer %d: block %u of tier %u used twice", l, i, t);
+            }
+        }
+    }
+    return ok();
+}
+
+// ---------------------------------------------------------------- kernels
+kv_status kv_quant_write(const kv_geometry* g, const kv_layer_pools* pools, const uint32_t* bt,
+                         const int32_t* pos, int batch, int n_new, const uint16_t* k_new,
+                         const uint16_t* v_new, uint16_t* ring, void* stream) {
+    kv_status st = check_geometry(g);
+    if (st != KV_OK) return st;
+    if ((st = check_pools(g, pools)) != KV_OK) return st;
+    if (batch < 0 || batch > g->max_seqs) return fail(KV_EINVAL, "batch %d", batch);
+    if (n_new < 0 || (int64_t)n_new > (int64_t)g->max_pages_per_seq * g->page_size)
+        return fail(KV_EINVAL, "n_new %d", n_new);
+    if (batch == 0 || n_new == 0) return ok();
+    if (!bt || !pos || !k_new || !v_new || !ring) return fail(KV_EINVAL, "NULL device pointer");
+    if (reinterpret_cast<uintptr_t>(k_new) % 4 || reinterpret_cast<uintptr_t>(v_new) % 4 ||
+        reinterpret_cast<uintptr_t>(ring) % 4)
+        return fail(KV_EINVAL, "fp16 buffers must be 4-byte aligned");
+    return hip_status(kvq::launch_quant_write(*g, pool_ptrs(pools), bt, pos, batch, n_new, k_new,
+                                              v_new, ring, static_cast<hipStream_t>(stream)),
+                      "kv_quant_write");
+}
+
+int kv_decode_pages_per_split(const kv_geometry* g, int batch, int max_ctx_len) {
+    if (check_geometry(g) != KV_OK || batch < 1 || max_ctx_len < 0) return 0;
+    const int max_pages = std::max(1, (max_ctx_len + g->page_size - 1) / g->page_size);
+    return auto_pages_per_split(*g, batch, max_pages);
+}
+
+static kv_status decode_plan(const kv_geometry* g, int batch, int max_ctx_len, int pps_in,
+                             int* pps, int* splits) {
+    if (batch < 1 || batch > g->max_seqs) return fail(KV_EINVAL, "batch %d", batch);
+    if (max_ctx_len < 0 || (int64_t)max_ctx_len > (int64_t)g->max_pages_per_seq * g->page_size)
+        return fail(KV_EINVAL, "max_ctx_len %d", max_ctx_len);
+    const int max_pages = std::max(1, (max_ctx_len + g->page_size - 1) / g->page_size);
+    int p = pps_in ? pps_in : auto_pages_per_split(*g, batch, max_pages);
+    if (p < 16 || p % 16 != 0) return fail(KV_EINVAL, "pages_per_split %d: a multiple of 16", p);
+    const int s = (max_pages + p - 1) / p;
+    if (s > 256) return fail(KV_EINVAL, "pages_per_split %d gives %d splits (max 256)", p, s);
+    *pps = p;
+    *splits = s;
+    return ok();
+}
+
+size_t kv_decode_workspace_bytes(const kv_geometry* g, int batch, int max_ctx_len,
+                                 int pages_per_split) {
+    if (check_geometry(g) != KV_OK) return 0;
+    int pps, splits;
+    if (decode_plan(g, batch, max_ctx_len, pages_per_split, &pps, &splits) != KV_OK) return 0;
+    return kvq::decode_workspace_bytes(*g, batch, splits);
+}
+
+kv_status kv_decode_attn(const kv_geometry* g, const kv_layer_pools* pools, const uint32_t* bt,
+                         const int32_t* ctx_len, int batch, int max_ctx_len, const uint16_t* q,
+                         float softmax_scale, float* out, void* workspace,
+                         size_t workspace_bytes, int pages_per_split, void* stream) {
+    kv_status st = check_geometry(g);
+    if (st != KV_OK) return st;
+    if ((st = check_pools(g, pools)) != KV_OK) return st;
+    int pps, splits;
+    if ((st = decode_plan(g, batch, max_ctx_len, pages_per_split, &pps, &splits)) != KV_OK)
+        return st;
+    if (!bt || !ctx_len || !q || !out || !workspace) return fail(KV_EINVAL, "NULL device pointer");
+    if (reinterpret_cast<uintptr_t>(q) % 4 || reinterpret_cast<uintptr_t>(workspace) % 256)
+        return fail(KV_EINVAL, "q must be 4-byte and workspace 256-byte aligned");
+    const size_t need = kvq::decode_workspace_bytes(*g, batch, splits);
+    if (workspace_bytes < need)
+        return fail(KV_EINVAL, "workspace %zu bytes, %zu needed", workspace_bytes, need);
+    if (!(softmax_scale == softmax_scale)) return fail(KV_EINVAL, "softmax_scale is NaN");
+    return hip_status(kvq::launch_decode_attn(*g, pool_ptrs(pools), bt, ctx_len, batch, splits, pps,
+                                              q, softmax_scale, out, workspace,
+                                              static_cast<hipStream_t>(stream)),
+                      "kv_decode_attn");
+}
+
+size_t kv_canary_workspace_bytes(const kv_geometry* g, int batch) {
+    if (check_geometry(g) != KV_OK || batch < 1) return 0;
+    return kvq::canary_workspace_bytes(*g, batch);
+}
+
+kv_status kv_canary_kl(const kv_geometry* g, const uint16_t* ring, const int32_t* seq_len,
+                       int batch, const uint16_t* q, float softmax_scale, float* kl_out,
+                       float* kl_rows, void* workspace, size_t workspace_bytes, void* stream) {
+    kv_status st = check_geometry(g);
+    if (st != KV_OK) return st;
+    if (batch < 1 || batch > g->max_seqs) return fail(KV_EINVAL, "batch %d", batch);
+    if (!ring || !seq_len || !q || !kl_out || !workspace)
+        return fail(KV_EINVAL, "NULL device pointer");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+        return fail(KV_EINVAL, "workspace must be 256-byte aligned");
+    const size_t need = kvq::canary_workspace_bytes(*g, batch);
+    if (workspace_bytes < need)
+        return fail(KV_EINVAL, "workspace %zu bytes, %zu needed", workspace_bytes, need);
+    if (!(softmax_scale == softmax_scale)) return fail(KV_EINVAL, "softmax_scale is NaN");
+    return hip_status(kvq::launch_canary(*g, ring, seq_len, batch, q, softmax_scale, kl_out,
+                                         kl_rows, workspace, static_cast<hipStream_t>(stream)),
+                      "kv_canary_kl");
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// kvq_device.hpp -- layout arithmetic and device helpers shared by the gfx950 kernels of libkvq.
+//
+// Storage format: see include/kv_quant.h. Everything here is product code; the CPU oracle has
+// its own, independent implementation of the same format.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kPage = 16;
+constexpr int kMaxGroup = 16;   // query heads per KV head handled by one MFMA tile
+
+// byte layout of one (block, KV head) section for b-bit codes
+struct Section {
+    uint32_t code_bytes;   // P*D*b/8
+    uint32_t kscale_off;   // K scales (D fp16)
+    uint32_t vcode_off;    // V codes
+    uint32_t vscale_off;   // V scales (P fp16)
+    uint32_t bytes;        // whole section
+};
+
+__host__ __device__ inline Section section_layout(int D, int bits) {
+    Section s;
+    s.code_bytes = (uint32_t)(kPage * D * bits / 8);
+    s.kscale_off = s.code_bytes;
+    s.vcode_off = s.code_bytes + 2u * D;
+    s.vscale_off = 2u * s.code_bytes + 2u * D;
+    s.bytes = 2u * s.code_bytes + 2u * D + 2u * kPage;
+    return s;
+}
+
+__host__ __device__ inline int bits_of_tier(int tier) { return 2 << tier; }  // 0,1,2 -> 2,4,8
+
+// bit position of code k (0 .. 32/b-1) inside its 32-bit word: even codes fill the low half,
+// odd codes the high half, each half low-first. A word thus unpacks into consecutive fp16 pairs
+// (x0,x1), (x2,x3), ... with one shift and one mask per pair.
+__host__ __device__ inline int field_bit(int k, int bits) { return 16 * (k & 1) + bits * (k >> 1); }
+
+// ---------------------------------------------------------------- quantizer (binary32)
+__device__ inline uint16_t f16_bits(_Float16 h) { return __builtin_bit_cast(uint16_t, h); }
+__device__ inline float f16_val(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+// smallest fp16 >= x for finite x >= 0 (round to nearest, then one step up if below)
+__device__ inline uint16_t f32_to_f16_up(float x) {
+    _Float16 h = (_Float16)x;
+    uint16_t b = f16_bits(h);
+    if ((float)h < x) b = (uint16_t)(b + 1);
+    return b;
+}
+
+// scale of a group with absolute maximum `absmax` (0 for an all-zero group)
+__device__ inline uint16_t group_scale(float absmax, int bits) {
+    if (absmax == 0.0f) return 0;
+    const float qmax = (float)((1 << (bits - 1)) - 1);
+    return f32_to_f16_up(__fdiv_rn(absmax, qmax));
+}
+
+// code of x under scale s (s > 0), round half to even
+__device__ inline int quant_code(float x, float s, int bits) {
+    const float qmax = (float)((1 << (bits - 1)) - 1);
+    float q = rintf(__fdiv_rn(x, s));
+    q = fminf(fmaxf(q, -qmax), qmax);
+    return (int)q;
+}
+
+template <typename T>
+__device__ inline T wave_max(T v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
+template <typename T>
+__device__ inline T wave_sum(T v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+}  // namespace kvq

@@ -1,0 +1,34 @@
+// kvq_launch.hpp -- internal launch entry points (called by the C ABI in kv_api.cpp after all
+// arguments have been validated on the host).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kv_quant.h"
+
+namespace kvq {
+
+struct PoolPtrs {
+    uint8_t* base[3];
+};
+
+hipError_t launch_quant_write(const kv_geometry& g, PoolPtrs pools, const uint32_t* bt,
+                              const int32_t* pos, int batch, int n_new, const uint16_t* k_new,
+                              const uint16_t* v_new, uint16_t* ring, hipStream_t stream);
+
+// split-K decode attention; splits = ceil(max_pages / pages_per_split)
+hipError_t launch_decode_attn(const kv_geometry& g, PoolPtrs pools, const uint32_t* bt,
+                              const int32_t* ctx_len, int batch, int splits, int pages_per_split,
+                              const uint16_t* q, float softmax_scale, float* out,
+                              void* workspace, hipStream_t stream);
+
+// workspace layout of the decode attention (bytes)
+size_t decode_workspace_bytes(const kv_geometry& g, int batch, int splits);
+
+hipError_t launch_canary(const kv_geometry& g, const uint16_t* ring, const int32_t* seq_len,
+                         int batch, const uint16_t* q, float softmax_scale, float* kl_out,
+                         float* kl_rows, void* workspace, hipStream_t stream);
+size_t canary_workspace_bytes(const kv_geometry& g, int batch);
+
+}  // namespace kvq

@@ -1,0 +1,207 @@
+"""Host-side tests of the C ABI (no GPU work): exported symbols, argument validation, byte sizes,
+and the block allocator (forward-only tiers, all-or-nothing growth, seeded shuffle).
+
+EchoKV, "How EchoKV works": the tier vector routes future blocks to the right pool; "What
+happens to old blocks...": already-allocated blocks keep their admit-time width.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import mixed_precision_quantized_kv_amd as kvq
+
+LIB = kvq.LIB_PATH
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if not os.path.exists(LIB):
+        pytest.skip("libkvq.so not built (run __graft_entry__.build())")
+
+
+def test_exports_every_header_symbol():
+    names = kvq.header_symbols()
+    assert len(names) >= 20
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    L = kvq.lib()
+    for n in names:
+        assert getattr(L, n) is not None
+    assert kvq.kv_abi_version() == 1
+
+
+def geom(**kw):
+    base = dict(num_layers=2, num_q_heads=8, num_kv_heads=2, head_dim=64, max_seqs=4,
+                max_pages_per_seq=8)
+    base.update(kw)
+    return kvq.geometry(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), kvq.KV_EUNSUPPORTED),
+    (dict(num_q_heads=9), kvq.KV_EINVAL),
+    (dict(num_q_heads=34, num_kv_heads=2), kvq.KV_EUNSUPPORTED),
+    (dict(ring_size=24), kvq.KV_EINVAL),
+    (dict(ring_size=256), kvq.KV_EINVAL),
+    (dict(page_size=32), kvq.KV_EUNSUPPORTED),
+    (dict(max_seqs=0), kvq.KV_EINVAL),
+])
+def test_geometry_validation(kw, status):
+    with pytest.raises(kvq.KVError) as e:
+        kvq.kv_validate(geom(**kw))
+    assert e.value.status == status
+    assert kvq.lib().kv_last_error().decode()
+
+
+def test_sizes_match_format():
+    g = geom(head_dim=128, num_q_heads=40, num_kv_heads=8)
+    # S_b = P*D*b/4 + 2D + 2P per KV head
+    assert [kvq.kv_block_bytes(g, b) for b in (2, 4, 8)] == [8 * 1312, 8 * 2336, 8 * 4384]
+    assert kvq.kv_block_bytes(g, 3) == 0
+    assert kvq.kv_ring_bytes(g) == 4 * 64 * 8 * 128 * 2
+    assert kvq.kv_cache_bytes_per_token(g, [16, 16]) == 2 * 2 * 8 * 128 * 2
+    assert kvq.kv_cache_bytes_per_token(g, [2, 8]) == 8 * (82 + 274)
+    assert kvq.kv_handle(4, 7) == (1 << 30) | 7
+    assert kvq.kv_handle(3, 7) == kvq.KV_NO_BLOCK
+
+
+def test_sizes_agree_with_oracle(orc):
+    for hq, hkv, d in ((8, 2, 64), (40, 8, 128), (28, 4, 128)):
+        g = geom(num_q_heads=hq, num_kv_heads=hkv, head_dim=d)
+        og = orc.geom(hq, hkv, d)
+        for b in (2, 4, 8):
+            assert kvq.kv_block_bytes(g, b) == orc.block_bytes(og, b)
+        bits = [2, 16]
+        assert kvq.kv_cache_bytes_per_token(g, bits) == orc.cache_bytes_per_token(og, bits)
+
+
+def test_kernel_calls_reject_bad_arguments_without_launching():
+    g = geom()
+    pools = kvq.layer_pools([0, 0, 0], [0, 0, 0])
+    with pytest.raises(kvq.KVError) as e:           # NULL device pointers
+        kvq.kv_quant_write(g, pools, 0, 0, 1, 1, 0, 0, 0, stream=0)
+    assert e.value.status == kvq.KV_EINVAL
+    with pytest.raises(kvq.KVError):                # batch beyond max_seqs
+        kvq.kv_quant_write(g, pools, 16, 16, 5, 1, 16, 16, 16, stream=0)
+    bad = kvq.layer_pools([8, 0, 0], [1, 0, 0])     # misaligned pool
+    with pytest.raises(kvq.KVError):
+        kvq.kv_decode_attn(g, bad, 256, 256, 1, 16, 256, 0.1, 256, 256, 1 << 20, 0, stream=0)
+    need = kvq.kv_decode_workspace_bytes(g, 1, 100)
+    assert need > 0
+    with pytest.raises(kvq.KVError) as e:           # workspace too small
+        kvq.kv_decode_attn(g, pools, 256, 256, 1, 100, 256, 0.1, 256, 256, need - 1, 0, stream=0)
+    assert "workspace" in str(e.value)
+    with pytest.raises(kvq.KVError):                # pages_per_split not a multiple of 16
+        kvq.kv_decode_attn(g, pools, 256, 256, 1, 100, 256, 0.1, 256, 256, 1 << 20, 24, stream=0)
+    with pytest.raises(kvq.KVError):                # context beyond the table
+        kvq.kv_decode_attn(g, pools, 256, 256, 1, 8 * 16 + 1, 256, 0.1, 256, 256, 1 << 20, 0, stream=0)
+    with pytest.raises(kvq.KVError):
+        kvq.kv_canary_kl(g, 256, 256, 1, 256, 0.1, 256, None, 256, 4, stream=0)
+    kvq.kv_quant_write(g, pools, 0, 0, 1, 0, 0, 0, 0, stream=0)   # n_new == 0: a no-op
+
+
+def test_split_plan():
+    g = geom(head_dim=128, num_q_heads=40, num_kv_heads=8, max_seqs=1, max_pages_per_seq=2100)
+    pps = kvq.kv_decode_pages_per_split(g, 1, 32768)
+    assert pps % 16 == 0 and pps >= 16
+    assert -(-2048 // pps) * 8 >= 128            # enough workgroups to spread over the chip
+    g4 = geom(max_seqs=1, max_pages_per_seq=9000)
+    assert kvq.kv_decode_pages_per_split(g4, 1, 131072) * 256 >= 8192
+
+
+# ------------------------------------------------------------------ allocator
+def make_alloc(bits=(4, 8), cap=16, seed=1, **kw):
+    g = geom(num_layers=len(bits), **kw)
+    capacity = np.full((len(bits), 3), cap, dtype=np.uint32)
+    return kvq.KVAlloc(g, capacity, list(bits), seed)
+
+
+def test_extend_assigns_current_tier_and_checks():
+    a = make_alloc()
+    a.kv_alloc_extend(0, 40)                   # 3 pages per layer
+    assert a.kv_alloc_seq_len(0) == 40
+    for l, b in enumerate((4, 8)):
+        row = a.bt[l, 0]
+        assert all(int(h) >> 30 == {2: 0, 4: 1, 8: 2}[b] for h in row[:3])
+        assert np.all(row[3:] == kvq.KV_NO_BLOCK)
+        assert a.kv_alloc_free_blocks(l, b) == 13
+    a.kv_check_block_table()
+
+
+def test_tier_switch_is_forward_only():
+    a = make_alloc()
+    a.kv_alloc_extend(0, 20)                   # pages 0, 1 at INT4 (page 1 open)
+    before = a.bt.copy()
+    a.kv_alloc_set_layer_bits(0, 2)
+    assert a.kv_alloc_layer_bits(0) == 2
+    a.kv_alloc_extend(0, 32)                   # still page 1: nothing new
+    assert np.array_equal(a.bt, before)
+    a.kv_alloc_extend(0, 70)                   # pages 2..4 come from the INT2 pool
+    assert np.array_equal(a.bt[0, 0, :2], before[0, 0, :2])
+    assert all(int(h) >> 30 == 0 for h in a.bt[0, 0, 2:5])
+    assert all(int(h) >> 30 == 2 for h in a.bt[1, 0, :5])
+    a.kv_check_block_table()
+
+
+def test_exhaustion_is_all_or_nothing():
+    a = make_alloc(cap=4)
+    a.kv_alloc_extend(0, 48)                   # 3 of 4 blocks
+    snap = a.bt.copy()
+    with pytest.raises(kvq.KVError) as e:
+        a.kv_alloc_extend(1, 40)               # needs 3, only 1 left
+    assert e.value.status == kvq.KV_ENOBLOCKS
+    assert np.array_equal(a.bt, snap)
+    assert a.kv_alloc_seq_len(1) == 0
+    assert a.kv_alloc_free_blocks(0, 4) == 1
+    a.kv_alloc_extend(1, 16)
+    a.kv_alloc_free_seq(0)
+    assert np.all(a.bt[:, 0] == kvq.KV_NO_BLOCK)
+    assert a.kv_alloc_free_blocks(0, 4) == 3
+    a.kv_alloc_extend(0, 48)                   # freed blocks are reused
+    a.kv_check_block_table()
+
+
+def test_shuffle_is_seeded_and_a_permutation():
+    a1, a2, a3 = (make_alloc(seed=sd, max_pages_per_seq=16) for sd in (7, 7, 8))
+    for a in (a1, a2, a3):
+        a.kv_alloc_extend(0, 256)              # all 16 blocks
+    assert np.array_equal(a1.bt, a2.bt)
+    assert not np.array_equal(a1.bt, a3.bt)
+    idx = sorted(int(h) & 0x3FFFFFFF for h in a1.bt[0, 0, :16])
+    assert idx == list(range(16))
+
+
+def test_check_block_table_catches_corruption():
+    a = make_alloc()
+    a.kv_alloc_extend(0, 40)
+    a.kv_alloc_extend(1, 40)
+    bad = a.bt.copy()
+    bad[0, 1, 0] = bad[0, 0, 0]                # one block used twice
+    with pytest.raises(kvq.KVError):
+        a.kv_check_block_table(bad)
+    bad = a.bt.copy()
+    bad[0, 0, 5] = 3                           # handle past the sequence length
+    with pytest.raises(kvq.KVError):
+        a.kv_check_block_table(bad)
+    bad = a.bt.copy()
+    bad[1, 0, 0] = (2 << 30) | 99              # index beyond capacity
+    with pytest.raises(kvq.KVError):
+        a.kv_check_block_table(bad)
+
+
+def test_extend_argument_errors():
+    a = make_alloc()
+    with pytest.raises(kvq.KVError):
+        a.kv_alloc_extend(9, 10)
+    a.kv_alloc_extend(0, 30)
+    with pytest.raises(kvq.KVError):
+        a.kv_alloc_extend(0, 10)               # shrinking
+    with pytest.raises(kvq.KVError):
+        a.kv_alloc_extend(0, 8 * 16 + 1)       # beyond max_pages_per_seq
+    with pytest.raises(kvq.KVError):
+        a.kv_alloc_set_layer_bits(0, 3)

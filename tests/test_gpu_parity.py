@@ -1,0 +1,165 @@
+"""GPU parity: libkvq (HIP, gfx950) against the CPU oracle, element by element.
+
+Bar: packed codes, scales and the ring bit-exact; attention rows within 2e-3 of the oracle's
+fp64 result (per row: max |err| / max |ref|); canary KL within 1e-4 absolute, mean and rows.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from mixed_precision_quantized_kv_amd import synth
+
+from gpu_cases import LayerPair, rowwise_rel_err
+
+pytestmark = pytest.mark.gpu
+
+ATTN_TOL = 2e-3
+KL_TOL = 1e-4
+TINY = synth.WORKLOADS["tiny"]
+
+
+def case_banner(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def tiny_layer(layer: int, N: int = 512, chunks=(100, 16, 200, 195), seed=0):
+    """tiny workload layer: prefill N-1 tokens in chunks, then the decode-step token"""
+    bits = synth.layer_bits(TINY)[layer]
+    tier = synth.TIER_OF_BITS[bits]
+    pages = synth.pages_for(N)
+    L = LayerPair(8, 2, 64, 1, pages + 2, [[tier] * pages], seed=seed + layer)
+    K, V = synth.keys_values(TINY, layer, N, synth.S_PREFILL_K, synth.S_PREFILL_V)
+    p = 0
+    for n in list(chunks) + [N - 1 - sum(chunks)]:
+        if n > 0:
+            L.write(K[:, p:p + n], V[:, p:p + n])
+            p += n
+    L.write(K[:, p:p + 1], V[:, p:p + 1])          # the decode step's own token
+    return L
+
+
+@pytest.mark.parametrize("layer", [0, 1, 2, 3])
+def test_tiny_write_attention_canary(layer):
+    case_banner(f"tiny layer {layer}")
+    L = tiny_layer(layer)
+    bad, ring_ok = L.compare_bytes()
+    assert not bad, f"blocks differ: {bad[:5]}"
+    assert ring_ok
+    q = synth.queries(TINY, layer)
+    ref = L.oracle_attn(q)
+    for pps in (0, 16, 32):
+        got, _ = L.attn(q, pages_per_split=pps)
+        err = rowwise_rel_err(got, ref)
+        print(f"  attn pps={pps} max rel err {err.max():.3e}")
+        assert err.max() <= ATTN_TOL, (pps, err.max())
+    kl, rows = L.canary(q)
+    okl, orows = L.oracle_canary(q)
+    print(f"  canary {okl} max abs err {np.abs(rows - orows).max():.3e}")
+    assert np.abs(kl - okl).max() <= KL_TOL, (kl, okl)
+    assert np.abs(rows - orows).max() <= KL_TOL
+
+
+@pytest.mark.parametrize("tier", [0, 1, 2])
+def test_token_by_token_writes(tier):
+    case_banner(f"token-by-token tier {tier}")
+    L = LayerPair(8, 2, 64, 2, 8, [[tier] * 6] * 2, seed=tier)
+    g = np.random.default_rng(tier)
+    K = synth.normal_f16(g, (2, 90, 2, 64), np.where(np.arange(64) % 7 == 0, 10, 1).astype(np.float32))
+    V = synth.normal_f16(g, (2, 90, 2, 64))
+    for p in range(90):
+        L.write(K[:, p:p + 1], V[:, p:p + 1])
+        if p in (0, 1, 15, 16, 17, 63, 64, 65, 89):
+            bad, ring_ok = L.compare_bytes()
+            assert not bad and ring_ok, (p, bad[:3])
+
+
+def test_large_chunk_overwrites_ring():
+    """n_new > R - P: new keys overwrite ring slots that hold the open page's earlier keys"""
+    case_banner("large chunk")
+    L = LayerPair(8, 2, 128, 2, 16, [[1, 2, 0, 1, 2, 0, 1, 2, 0, 1]] * 2, seed=3)
+    g = np.random.default_rng(3)
+    K = synth.normal_f16(g, (2, 150, 2, 128))
+    V = synth.normal_f16(g, (2, 150, 2, 128))
+    L.write(K[:, :9], V[:, :9])
+    L.write(K[:, 9:140], V[:, 9:140])
+    L.write(K[:, 140:150], V[:, 140:150])
+    bad, ring_ok = L.compare_bytes()
+    assert not bad and ring_ok
+
+
+def test_striped_layer_and_short_context():
+    """a layer whose first 256 tokens are INT2 and the rest INT8; and N = 40 < R"""
+    case_banner("striped + short")
+    tiers = [0] * 16 + [2] * 16
+    L = LayerPair(8, 2, 64, 1, 34, [tiers], seed=5)
+    K, V = synth.keys_values(TINY, 1, 512, synth.S_PREFILL_K, synth.S_PREFILL_V)
+    L.write(K[:, :300], V[:, :300])
+    L.write(K[:, 300:512], V[:, 300:512])
+    bad, ring_ok = L.compare_bytes()
+    assert not bad and ring_ok
+    q = synth.queries(TINY, 1)
+    for ctx in (512, 256, 257, 40, 1):
+        got, _ = L.attn(q, ctx=[ctx])
+        assert rowwise_rel_err(got, L.oracle_attn(q, ctx=[ctx])).max() <= ATTN_TOL, ctx
+    S = LayerPair(8, 2, 64, 1, 4, [[1, 1, 1]], seed=6)
+    S.write(K[:, :40], V[:, :40])
+    got, _ = S.attn(q)
+    assert rowwise_rel_err(got, S.oracle_attn(q)).max() <= ATTN_TOL
+    kl, rows = S.canary(q)
+    okl, orows = S.oracle_canary(q)
+    assert np.abs(kl - okl).max() <= KL_TOL and np.abs(rows - orows).max() <= KL_TOL
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (40, 8, 128), (28, 4, 128), (64, 8, 128),
+                                      (16, 16, 64), (16, 1, 64)])
+def test_ragged_batch_gqa_shapes(hq, hkv, d):
+    """group sizes 1, 4, 5, 7, 8, 16; lengths 0, 1, 15, 16, 17, ragged; mixed tiers per page"""
+    case_banner(f"ragged hq={hq} hkv={hkv} d={d}")
+    lens = [0, 1, 15, 16, 17, 300, 1000, 777]
+    B = len(lens)
+    g = np.random.default_rng(hq * 100 + d)
+    tiers = [list(g.integers(0, 3, size=64)) for _ in range(B)]
+    L = LayerPair(hq, hkv, d, B, 64, tiers, seed=hq)
+    for s, n in enumerate(lens):
+        if n:
+            K = synth.normal_f16(g, (1, n, hkv, d), np.where(np.arange(d) % 11 == 0, 8, 1).astype(np.float32))
+            V = synth.normal_f16(g, (1, n, hkv, d))
+            L.write(K, V, rows=[s])
+    bad, ring_ok = L.compare_bytes()
+    assert not bad and ring_ok
+    q = synth.normal_f16(g, (B, hq, d))
+    ref = L.oracle_attn(q)
+    for pps in (0, 16):
+        got, _ = L.attn(q, pages_per_split=pps)
+        err = rowwise_rel_err(got, ref)
+        print(f"  attn pps={pps} max rel err {err.max():.3e}")
+        assert err.max() <= ATTN_TOL, (pps, err.max(), np.argmax(err.max(-1)))
+    assert not got[0].any()                       # the empty sequence gives a zero row
+    kl, rows = L.canary(q)
+    okl, orows = L.oracle_canary(q)
+    assert np.abs(kl - okl).max() <= KL_TOL and np.abs(rows - orows).max() <= KL_TOL
+
+
+def test_deterministic_and_workspace_reuse():
+    case_banner("determinism")
+    L = tiny_layer(2)
+    q = synth.queries(TINY, 2)
+    a, ws = L.attn(q, pages_per_split=16)
+    b, _ = L.attn(q, pages_per_split=16)
+    assert np.array_equal(a, b)
+    assert not ws[:256].any()                      # ticket counters are left at zero
+
+
+def test_softmax_scale_zero_and_identical_keys():
+    case_banner("closed forms")
+    key = synth.normal_f16(np.random.default_rng(1), (1, 1, 2, 64))
+    K = np.repeat(key, 200, axis=1)
+    V = synth.normal_f16(np.random.default_rng(2), (1, 200, 2, 64))
+    L = LayerPair(8, 2, 64, 1, 14, [[1] * 13], seed=9)
+    L.write(K, V)
+    q = synth.queries(TINY, 0)
+    for scale in (0.0, 0.125, 3.0):
+        got, _ = L.attn(q, scale=scale)
+        assert rowwise_rel_err(got, L.oracle_attn(q, scale=scale)).max() <= ATTN_TOL
