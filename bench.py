@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the mixed-precision quantized KV-cache path on one MI355X.
+
+A step is one pass of the whole hot path over one synthetic decode token: for every layer,
+quantize-on-write of the new key/value (kv_quant_write) followed by decode attention over the
+paged mixed-precision cache (kv_decode_attn); on every 64th step the KL canary runs for every
+layer (kv_canary_kl). Inputs are resident in HBM before timing starts.
+
+    python bench.py [--gpus 1] [--steps 256] [--warmup 10] [--workload qwen14b_32k]
+
+Prints one JSON line. `value` is the effective cache bytes the attention kernels must read per
+step divided by the wall time of the step (GB/s); steps/s is reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantized decode-attn achieved HBM GB/s + decode steps/s, 14B-shape @32K"
+HBM_PEAK_GBS = 8000.0
+CANARY_EVERY = 64
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qwen14b_32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=4, help="layers in the oracle's sample")
+    ap.add_argument("--pages-per-split", type=int, default=0)
+    return ap.parse_args()
+
+
+def attn_bytes(w, ctx: int, bits: int) -> int:
+    """bytes one attention launch must move for one sequence of length ctx: the valid tokens'
+    K and V codes and V scales, one K-scale vector per page, block-table entries, q and out"""
+    D, H = w.head_dim, w.num_kv_heads
+    pages = (ctx + 15) // 16
+    per_kv = ctx * (D * bits // 4 + 2) + pages * 2 * D
+    return H * per_kv + 4 * pages + w.num_q_heads * D * (2 + 4)
+
+
+class Model:
+    """All layers of one workload: pools, block tables (from the library's allocator), rings."""
+
+    def __init__(self, w, steps_total: int, torch, kvq, synth, dev):
+        self.w = w
+        self.torch = torch
+        L, B = w.num_layers, w.batch
+        self.lens0 = synth.seq_lengths(w)                 # tokens at the first decode step
+        self.max_ctx = int(self.lens0.max()) + steps_total * w.new_tokens
+        self.max_pages = (self.max_ctx + 15) // 16 + 1
+        self.bits = synth.layer_bits(w)
+        self.g = kvq.geometry(L, w.num_q_heads, w.num_kv_heads, w.head_dim, B, self.max_pages)
+        need = int(sum((int(n) + steps_total * w.new_tokens + 15) // 16 + 1 for n in self.lens0))
+        cap = np.zeros((L, 3), dtype=np.uint32)
+        for l, b in enumerate(self.bits):
+            cap[l, synth.TIER_OF_BITS[b]] = need
+        self.alloc = kvq.KVAlloc(self.g, cap, self.bits, shuffle_seed=12345)
+        for s in range(B):                               # reserve every page the run will use
+            self.alloc.kv_alloc_extend(s, int(self.lens0[s]) - 1 + steps_total * w.new_tokens)
+        self.alloc.kv_check_block_table()
+        self.bt = [torch.from_numpy(self.alloc.bt[l].view(np.int32).copy()).to(dev) for l in range(L)]
+        self.pools_t, self.pools = [], []
+        for l, b in enumerate(self.bits):
+            tiers = []
+            for t in range(3):
+                n = int(cap[l, t])
+                tiers.append(torch.empty(max(n * kvq.kv_block_bytes(self.g, kvq.TIER_BITS[t]), 256),
+                                         dtype=torch.uint8, device=dev))
+            self.pools_t.append(tiers)
+            self.pools.append(kvq.layer_pools([x if c else 0 for x, c in zip(tiers, cap[l])], cap[l]))
+        self.ring = [torch.zeros((B, w.ring_size, w.num_kv_heads, w.head_dim), dtype=torch.float16,
+                                 device=dev) for _ in range(L)]
+
+
+def gen_normal_f16(torch, shape, seed, dev, mult=None):
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    x = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+    if mult is not None:
+        x = x * mult
+    return x.half()
+
+
+def prefill(m: Model, kvq, synth, dev):
+    """write the first len0 - 1 tokens of every sequence, layer by layer"""
+    torch, w = m.torch, m.w
+    for l in range(w.num_layers):
+        mult = torch.from_numpy(synth.outlier_mask(w, l)).to(dev)
+        for s in range(w.batch):
+            n = int(m.lens0[s]) - 1
+            if n <= 0:
+                continue
+            seed = (w.config_id * 1000 + l) * 100000 + s
+            k = gen_normal_f16(torch, (1, n, w.num_kv_heads, w.head_dim), 2 * seed, dev, mult)
+            v = gen_normal_f16(torch, (1, n, w.num_kv_heads, w.head_dim), 2 * seed + 1, dev)
+            pos = torch.zeros(1, dtype=torch.int32, device=dev)
+            kvq.kv_quant_write(m.g, m.pools[l], m.bt[l][s:s + 1], pos, 1, n, k, v, m.ring[l][s:s + 1])
+    torch.cuda.synchronize()
+
+
+def run(args):
+    import torch
+
+    import mixed_precision_quantized_kv_amd as kvq
+    from mixed_precision_quantized_kv_amd import synth
+
+    dev = "cuda:0"
+    w = synth.WORKLOADS[args.workload]
+    L, B, nn = w.num_layers, w.batch, w.new_tokens
+    steps_total = args.warmup + args.steps
+    t0 = time.time()
+    m = Model(w, steps_total, torch, kvq, synth, dev)
+    prefill(m, kvq, synth, dev)
+    t_setup = time.time() - t0
+
+    # per-step inputs, resident before timing
+    gen_seed = w.config_id * 7919 + 1
+    q_all = gen_normal_f16(torch, (steps_total, L, B, w.num_q_heads, w.head_dim), gen_seed, dev)
+    k_all = gen_normal_f16(torch, (steps_total, L, B, nn, w.num_kv_heads, w.head_dim), gen_seed + 1, dev)
+    v_all = gen_normal_f16(torch, (steps_total, L, B, nn, w.num_kv_heads, w.head_dim), gen_seed + 2, dev)
+    lens0 = torch.from_numpy(m.lens0.astype(np.int32)).to(dev)
+    pos_all = torch.stack([lens0 - 1 + i * nn for i in range(steps_total)]).contiguous()
+    ctx_all = (pos_all + nn).contiguous()
+    scale = 1.0 / math.sqrt(w.head_dim)
+    pps = args.pages_per_split or kvq.kv_decode_pages_per_split(m.g, B, m.max_ctx)
+    wsb = kvq.kv_decode_workspace_bytes(m.g, B, m.max_ctx, pps)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    cwsb = kvq.kv_canary_workspace_bytes(m.g, B)
+    cws = torch.zeros(cwsb, dtype=torch.uint8, device=dev)
+    kl = torch.zeros((L, 3), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step(i, canary: bool, ev=None):
+        for l in range(L):
+            kvq.kv_quant_write(m.g, m.pools[l], m.bt[l], pos_all[i], B, nn, k_all[i, l], v_all[i, l],
+                               m.ring[l], stream=sp)
+            if ev is not None:
+                ev[l][0].record(stream)
+            kvq.kv_decode_attn(m.g, m.pools[l], m.bt[l], ctx_all[i], B, m.max_ctx, q_all[i, l], scale,
+                               out, ws, wsb, pps, stream=sp)
+            if ev is not None:
+                ev[l][1].record(stream)
+            if canary:
+                kvq.kv_canary_kl(m.g, m.ring[l], ctx_all[i], B, q_all[i, l], scale, kl[l], None,
+                                 cws, cwsb, stream=sp)
+
+    for i in range(args.warmup):
+        step(i, i % CANARY_EVERY == 0)
+    torch.cuda.synchronize()
+
+    # timed window: K steps, the canary firing on every 64th
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for j in range(args.steps):
+        i = args.warmup + j
+        step(i, j % CANARY_EVERY == 0)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+
+    # attention launch durations: HIP events on the launch stream around every attention
+    # launch of a second window of the same K steps (same inputs, same launches)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(L)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for j in range(args.steps):
+        i = args.warmup + j
+        step(i, j % CANARY_EVERY == 0, ev=evs[j])
+    torch.cuda.synchronize()
+    attn_ms = np.array([[a.elapsed_time(b) for (a, b) in row] for row in evs])   # [K][L]
+
+    # step without the canary (for its overhead)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for j in range(args.steps):
+        step(args.warmup + j, False)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step_nocanary = t_start.elapsed_time(t_end) / args.steps
+
+    # algorithmic bytes
+    lens = m.lens0.astype(np.int64)
+    step_bytes = []
+    per_launch_bytes = np.zeros((args.steps, L))
+    for j in range(args.steps):
+        ctx = lens + (args.warmup + j) * nn
+        for l, b in enumerate(m.bits):
+            per_launch_bytes[j, l] = sum(attn_bytes(w, int(c), b) for c in ctx)
+        step_bytes.append(per_launch_bytes[j].sum())
+    step_bytes = float(np.mean(step_bytes))
+    avg_launch_bytes = float(per_launch_bytes.mean())
+    avg_attn_ms = float(attn_ms.mean())
+    achieved = avg_launch_bytes / (avg_attn_ms * 1e-3) / 1e9
+
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    tiers = {b: m.bits.count(b) for b in (2, 4, 8)}
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "steps_per_s": round(1000.0 / ms_step, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "layers": L, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "batch": B, "context": int(m.lens0.max()),
+            "page": 16, "ring": w.ring_size, "layer_bits": {f"int{b}": n for b, n in tiers.items()},
+            "pages_per_split": pps, "canary_every": CANARY_EVERY,
+        },
+        "storage": "packed int2/int4/int8 codes + fp16 scales; f16 MFMA, f32 accumulate",
+        "attn_bytes_per_step": int(step_bytes),
+        "attn_kernel_us": round(avg_attn_ms * 1e3, 3),
+        "canary_overhead": round(ms_step / ms_step_nocanary - 1.0, 5),
+        "ms_per_step_no_canary": round(ms_step_nocanary, 5),
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "decode_attn_kernel<128>", "bytes_per_launch": int(avg_launch_bytes),
+        },
+        "setup_s": round(t_setup, 1),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, m.bits, args.cpu_layers, step_bytes)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(w, bits, n_layers: int, step_bytes: float) -> dict:
+    """The oracle (plain C, fp64) on a sample of the same step: quantize-on-write of the new
+    token plus decode attention for `n_layers` layers at full context, scaled to all layers."""
+    import oracle
+    from mixed_precision_quantized_kv_amd import synth
+
+    oracle.lib()
+    g = oracle.geom(w.num_q_heads, w.num_kv_heads, w.head_dim, 16, w.ring_size)
+    N = int(synth.seq_lengths(w).max())
+    layers = list(range(n_layers))
+    B = w.batch
+    t_total = 0.0
+    # one seeded draw of the layer's keys and values serves every sampled layer (the oracle's
+    # time does not depend on the values); each layer keeps its own bit-width
+    K, V = synth.keys_values(w, 0, N, synth.S_PREFILL_K, synth.S_PREFILL_V)
+    for l in layers:
+        b = bits[l]
+        tier = synth.TIER_OF_BITS[b]
+        pages = (N + 15) // 16
+        cap = [pages * B if t == tier else 1 for t in range(3)]
+        bt = synth.block_table([[tier] * pages] * B, pages, cap, synth.rng(w, l, synth.S_SHUFFLE))
+        pools = oracle.Pools(g, cap)
+        ring = np.zeros((B, w.ring_size, w.num_kv_heads, w.head_dim), dtype=np.uint16)
+        oracle.quant_write(g, pools, bt, np.zeros(B, np.int32), K[:, :N - 1], V[:, :N - 1], ring)
+        q = synth.queries(w, l)
+        scale = np.float32(1.0 / math.sqrt(w.head_dim))
+        t0 = time.perf_counter()
+        oracle.quant_write(g, pools, bt, np.full(B, N - 1, np.int32), K[:, N - 1:], V[:, N - 1:], ring)
+        oracle.decode_attn(g, pools, bt, np.full(B, N, np.int32), q, scale)
+        t_total += time.perf_counter() - t0
+    t_step = t_total / len(layers) * w.num_layers
+    # the oracle's parallel loop runs over (sequence, KV head) items
+    cores = min(oracle.num_threads(), B * w.num_kv_heads)
+    return {"value": round(step_bytes / t_step / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle", "steps_per_s": round(1.0 / t_step, 5),
+            "sample": f"{len(layers)} of {w.num_layers} layers (bits {[bits[l] for l in layers]}), one "
+                      f"decode step (write + attention) at context {N}, batch {B}; per-step time "
+                      f"scaled by {w.num_layers}/{len(layers)}",
+            "seconds_measured": round(t_total, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported "
+                                   "(multi-GPU sharding is a design note only)", "n_gpus": args.gpus}))
+        sys.exit(2)
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -144,7 +144,7 @@ kv_status kv_quant_write(const kv_geometry* g, const kv_layer_pools* pools, cons
  *   ctx_len  dev int32 [batch], each in [0, max_ctx_len]; a zero length gives a zero row
  *   q        dev fp16 [batch][H_q][D];  out  dev fp32 [batch][H_q][D]
  *   max_ctx_len    host upper bound on ctx_len, sizes the launch (<= max_pages_per_seq * P)
- *   pages_per_split  pages one workgroup reads (a multiple of 16); 0 = chosen by the library
+ *   pages_per_split  pages one workgroup reads (even, >= 2); 0 = chosen by the library
  *   workspace  dev, >= kv_decode_workspace_bytes(...) bytes, zero-filled before its first use;
  *              the call leaves it ready for the next call. One workspace per in-flight call.
  * The split-K partials are merged in a fixed order, so results are bitwise reproducible. */

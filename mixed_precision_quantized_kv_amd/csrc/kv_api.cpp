@@ -85,14 +85,15 @@ uint64_t splitmix64(uint64_t& x) {
 }
 
 int auto_pages_per_split(const kv_geometry& g, int batch, int max_pages) {
-    // enough workgroups to give each of the 256 CUs one, pairs of pages per wave, and at
-    // most 256 splits per (sequence, KV head)
+    // one workgroup per CU (the kernel holds one 8-wave workgroup per CU): split each
+    // (sequence, KV head) so that the grid has about 256 workgroups, pages in pairs, at most
+    // 256 splits
     const int64_t groups = (int64_t)batch * g.num_kv_heads;
-    int64_t want_wg = 256;
-    int64_t pps = (groups * max_pages + want_wg - 1) / want_wg;
-    pps = std::max<int64_t>(pps, 16);
+    int64_t splits = std::max<int64_t>(1, (256 + groups - 1) / groups);
+    int64_t pps = (max_pages + splits - 1) / splits;
+    pps = std::max<int64_t>(pps, 2);
     pps = std::max<int64_t>(pps, (max_pages + 255) / 256);
-    pps = (pps + 15) / 16 * 16;
+    pps += pps & 1;
     return (int)pps;
 }
 
@@ -322,7 +323,7 @@ static kv_status decode_plan(const kv_geometry* g, int batch, int max_ctx_len, i
         return fail(KV_EINVAL, "max_ctx_len %d", max_ctx_len);
     const int max_pages = std::max(1, (max_ctx_len + g->page_size - 1) / g->page_size);
     int p = pps_in ? pps_in : auto_pages_per_split(*g, batch, max_pages);
-    if (p < 16 || p % 16 != 0) return fail(KV_EINVAL, "pages_per_split %d: a multiple of 16", p);
+    if (p < 2 || p % 2 != 0) return fail(KV_EINVAL, "pages_per_split %d: an even number >= 2", p);
     const int s = (max_pages + p - 1) / p;
     if (s > 256) return fail(KV_EINVAL, "pages_per_split %d gives %d splits (max 256)", p, s);
     *pps = p;

@@ -33,6 +33,11 @@ constexpr int kWaves = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxSplits = 256;
 
+// read-only tables indexed by wave-uniform values: the constant address space lets the compiler
+// use scalar loads, so block-table lookups never wait on the vector-memory counter
+typedef const __attribute__((address_space(4))) uint32_t* const_u32_ptr;
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+
 struct AttnArgs {
     PoolPtrs pools;
     const uint32_t* bt;
@@ -40,7 +45,7 @@ struct AttnArgs {
     const uint16_t* q;
     float* out;
     uint32_t* counters;   // [groups]
-    float2* ws_ml;        // [groups][splits][group] (max, sum) in log2 units
+    float* ws_ml;         // [groups][splits][group][2] (max, sum) in log2 units
     float* ws_o;          // [groups][splits][group][D]
     int max_pages;
     int H;                // KV heads
@@ -62,57 +67,57 @@ struct PageRaw {
     int ntok;        // valid tokens in the page
 };
 
-template <int NBYTES>
-__device__ inline void load_chunk(const uint8_t* p, uint32_t* dst) {
-    if constexpr (NBYTES == 4) {
-        dst[0] = *reinterpret_cast<const uint32_t*>(p);
-    } else if constexpr (NBYTES == 8) {
-        uint2 a = *reinterpret_cast<const uint2*>(p);
-        dst[0] = a.x; dst[1] = a.y;
-    } else if constexpr (NBYTES == 16) {
-        uint4 a = *reinterpret_cast<const uint4*>(p);
-        dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
-    } else {
-        static_assert(NBYTES == 32, "chunk size");
-        uint4 a = *reinterpret_cast<const uint4*>(p);
-        uint4 b = *reinterpret_cast<const uint4*>(p + 16);
-        dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
-        dst[4] = b.x; dst[5] = b.y; dst[6] = b.z; dst[7] = b.w;
-    }
-}
-
-template <int D, int BITS>
-__device__ inline void load_page_bits(const uint8_t* sec, int lane, PageRaw& r) {
-    constexpr Section L = {(uint32_t)(kPage * D * BITS / 8), (uint32_t)(kPage * D * BITS / 8),
-                           (uint32_t)(kPage * D * BITS / 8 + 2 * D),
-                           (uint32_t)(2 * kPage * D * BITS / 8 + 2 * D),
-                           (uint32_t)(2 * kPage * D * BITS / 8 + 2 * D + 2 * kPage)};
-    constexpr int CH = D * BITS / 32;               // bytes of one lane chunk
+// Loads of one page for this lane. The instruction sequence is the same for every tier (two
+// 16-byte K loads, two 16-byte V loads, one scale dword, one scale pair): the second 16 bytes are
+// only needed by INT8, so INT2/INT4 re-read their first 16 bytes (same cache lines, all inside
+// the section). A fixed count lets the compiler wait for exactly one page's loads while the next
+// pair's loads stay in flight. `page` must be a valid page index even when `present` is false.
+template <int D>
+__device__ __forceinline__ void load_page(const AttnArgs& a, int s, int kv, int page, bool present,
+                                          int ctx, int lane, PageRaw& r) {
+    const uint32_t handle = ((const_u32_ptr)a.bt)[(size_t)s * a.max_pages + page];
+    const int tier = (int)(handle >> 30);
+    const uint32_t idx = handle & 0x3fffffffu;
+    const int bits = bits_of_tier(tier);
+    r.bits = present ? bits : 0;
+    r.ntok = present ? min(kPage, ctx - page * kPage) : 0;
+    const uint32_t code_bytes = kPage * D * bits / 8;
+    const uint32_t sec_bytes = 2 * code_bytes + 2 * D + 2 * kPage;
+    const uint8_t* base = tier == 0 ? a.pools.base[0] : tier == 1 ? a.pools.base[1] : a.pools.base[2];
+    const uint8_t* sec = base + ((size_t)idx * a.H + kv) * sec_bytes;
     const int t = lane & 15, G = lane >> 4;
-    load_chunk<CH>(sec + t * (D * BITS / 8) + G * CH, r.k);
-    load_chunk<CH>(sec + L.vcode_off + (G * D + t * (D / 16)) * BITS / 2, r.v);
-    r.ks = lane < D / 2 ? *reinterpret_cast<const uint32_t*>(sec + L.kscale_off + 4 * lane) : 0u;
-    uint2 vs = *reinterpret_cast<const uint2*>(sec + L.vscale_off + 8 * G);
+    const int ch = D * bits / 32;                   // bytes of one lane chunk
+    const uint8_t* kp = sec + t * (D * bits / 8) + G * ch;
+    const uint8_t* vp = sec + code_bytes + 2 * D + (G * D + t * (D / 16)) * bits / 2;
+    const int second = bits == 8 ? 16 : 0;
+    const uint4 k0 = *reinterpret_cast<const uint4*>(kp);
+    const uint4 k1 = *reinterpret_cast<const uint4*>(kp + second);
+    const uint4 v0 = *reinterpret_cast<const uint4*>(vp);
+    const uint4 v1 = *reinterpret_cast<const uint4*>(vp + second);
+    r.ks = *reinterpret_cast<const uint32_t*>(sec + code_bytes + 4 * (lane & (D / 2 - 1)));
+    const uint2 vs = *reinterpret_cast<const uint2*>(sec + 2 * code_bytes + 2 * D + 8 * G);
+    r.k[0] = k0.x; r.k[1] = k0.y; r.k[2] = k0.z; r.k[3] = k0.w;
+    r.k[4] = k1.x; r.k[5] = k1.y; r.k[6] = k1.z; r.k[7] = k1.w;
+    r.v[0] = v0.x; r.v[1] = v0.y; r.v[2] = v0.z; r.v[3] = v0.w;
+    r.v[4] = v1.x; r.v[5] = v1.y; r.v[6] = v1.z; r.v[7] = v1.w;
     r.vs[0] = vs.x; r.vs[1] = vs.y;
 }
 
+// page pair `pair` of the split [pbeg, pend); pairs past the end reload the last pair (their
+// data is never used) so that every iteration issues the same loads
 template <int D>
-__device__ inline void load_page(const AttnArgs& a, int s, int kv, int page, int ctx, int lane,
-                                 PageRaw& r) {
-    const uint32_t handle = a.bt[(size_t)s * a.max_pages + page];
-    const int tier = (int)(handle >> 30);
-    const uint32_t idx = handle & 0x3fffffffu;
-    r.bits = bits_of_tier(tier);
-    r.ntok = min(kPage, ctx - page * kPage);
-    const uint32_t sb = section_layout(D, r.bits).bytes;
-    const uint8_t* sec = a.pools.base[tier] + ((size_t)idx * a.H + kv) * sb;
-    if (tier == 0) load_page_bits<D, 2>(sec, lane, r);
-    else if (tier == 1) load_page_bits<D, 4>(sec, lane, r);
-    else load_page_bits<D, 8>(sec, lane, r);
+__device__ __forceinline__ void load_pair(const AttnArgs& a, int s, int kv, int pbeg, int pend,
+                                          int pair, int npairs, int ctx, int lane, PageRaw& x,
+                                          PageRaw& y) {
+    const int pc = min(pair, npairs - 1);
+    const int pa = pbeg + 2 * pc;
+    const bool has_b = pa + 1 < pend;
+    load_page<D>(a, s, kv, pa, true, ctx, lane, x);
+    load_page<D>(a, s, kv, has_b ? pa + 1 : pa, has_b, ctx, lane, y);
 }
 
 // one packed word of codes -> consecutive fp16 pairs holding the signed codes
-__device__ inline uint32_t hadd_bias(uint32_t u, float bias) {
+__device__ __forceinline__ uint32_t hadd_bias(uint32_t u, float bias) {
     half2v x = __builtin_bit_cast(half2v, u);
     half2v b = {(_Float16)bias, (_Float16)bias};
     return __builtin_bit_cast(uint32_t, x + b);
@@ -120,7 +125,7 @@ __device__ inline uint32_t hadd_bias(uint32_t u, float bias) {
 
 // unpack a lane chunk (D*BITS/32 bytes) into D/8 dwords of fp16 pairs, in code order
 template <int D>
-__device__ inline void unpack_chunk(const uint32_t* w, int bits, uint32_t* out) {
+__device__ __forceinline__ void unpack_chunk(const uint32_t* w, int bits, uint32_t* out) {
     if (bits == 2) {
 #pragma unroll
         for (int i = 0; i < D / 64; ++i)
@@ -142,7 +147,7 @@ __device__ inline void unpack_chunk(const uint32_t* w, int bits, uint32_t* out) 
     }
 }
 
-__device__ inline half8 make_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+__device__ __forceinline__ half8 make_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
     uint4 u = {a, b, c, d};
     return __builtin_bit_cast(half8, u);
 }
@@ -156,14 +161,14 @@ struct WaveState {
 
 // QK for one page: returns S^T for tokens 4G..4G+3 of head lane%16 (log2 units, masked)
 template <int D>
-__device__ inline float4v page_logits(const PageRaw& r, const uint32_t* qf, uint32_t* lds_ks,
+__device__ __forceinline__ float4v page_logits(const PageRaw& r, const uint32_t* qf, uint32_t* lds_ks,
                                       int lane, float scale_log2) {
     const int G = lane >> 4;
     // stage the page's K scales through LDS: each lane needs the D/4 scales of its lane group
+    // (one wave writes and reads its own slot; LDS serves a wave's requests in order, and the
+    // wave barrier keeps the compiler from hoisting the reads above the write)
     lds_ks[lane] = r.ks;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     uint32_t ks[D / 8];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) {
@@ -214,7 +219,7 @@ __device__ inline float4v page_logits(const PageRaw& r, const uint32_t* qf, uint
 }
 
 template <int D>
-__device__ inline void process_pair(const PageRaw& A, const PageRaw& B, const uint32_t* qf,
+__device__ __forceinline__ void process_pair(const PageRaw& A, const PageRaw& B, const uint32_t* qf,
                                     uint32_t* lds_ks, int lane, float scale_log2, WaveState<D>& st) {
     const int G = lane >> 4;
     float4v la = page_logits<D>(A, qf, lds_ks, lane, scale_log2);
@@ -227,13 +232,13 @@ __device__ inline void process_pair(const PageRaw& A, const PageRaw& B, const ui
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(st.m, mx);            // finite: page A holds >= 1 valid token
-    const float alpha = exp2f(st.m - m_new);        // 0 on the first pair (m = -inf)
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);   // 0 on the first pair (m = -inf)
     st.m = m_new;
     float pa[4], pb[4], sum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        pa[i] = exp2f(la[i] - m_new);
-        pb[i] = exp2f(lb[i] - m_new);
+        pa[i] = __builtin_amdgcn_exp2f(la[i] - m_new);
+        pb[i] = __builtin_amdgcn_exp2f(lb[i] - m_new);
         sum += pa[i] + pb[i];
     }
     st.l = st.l * alpha + sum;
@@ -241,15 +246,15 @@ __device__ inline void process_pair(const PageRaw& A, const PageRaw& B, const ui
     for (int k = 0; k < D / 16; ++k) st.o[k] *= alpha;
 
     // p' = p * V scale of the token; masked tokens get exactly 0 (their scale may be anything)
-    auto vscale = [](const PageRaw& r, int i) {
-        const uint32_t w = r.vs[i >> 1];
-        return f16_val((uint16_t)((i & 1) ? (w >> 16) : (w & 0xffffu)));
-    };
+    const float sa[4] = {f16_val((uint16_t)(A.vs[0] & 0xffffu)), f16_val((uint16_t)(A.vs[0] >> 16)),
+                         f16_val((uint16_t)(A.vs[1] & 0xffffu)), f16_val((uint16_t)(A.vs[1] >> 16))};
+    const float sb[4] = {f16_val((uint16_t)(B.vs[0] & 0xffffu)), f16_val((uint16_t)(B.vs[0] >> 16)),
+                         f16_val((uint16_t)(B.vs[1] & 0xffffu)), f16_val((uint16_t)(B.vs[1] >> 16))};
     float wa[4], wb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        wa[i] = (4 * G + i < A.ntok) ? pa[i] * vscale(A, i) : 0.f;
-        wb[i] = (B.bits && 4 * G + i < B.ntok) ? pb[i] * vscale(B, i) : 0.f;
+        wa[i] = (4 * G + i < A.ntok) ? pa[i] * sa[i] : 0.f;
+        wb[i] = (B.bits && 4 * G + i < B.ntok) ? pb[i] * sb[i] : 0.f;
     }
     const half8 pf = {(_Float16)wa[0], (_Float16)wa[1], (_Float16)wa[2], (_Float16)wa[3],
                       (_Float16)wb[0], (_Float16)wb[1], (_Float16)wb[2], (_Float16)wb[3]};
@@ -280,9 +285,10 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
 
     const int split = blockIdx.x / a.groups, group = blockIdx.x % a.groups;
     const int s = group / a.H, kv = group % a.H;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps page math scalar
     const int grp = a.grp;
-    const int ctx = a.ctx_len[s];
+    const int ctx = ((const_i32_ptr)a.ctx_len)[s];
     const int npages = (ctx + kPage - 1) / kPage;
     const int nsplit = (npages + a.pps - 1) / a.pps;
 
@@ -313,25 +319,26 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
     for (int k = 0; k < D / 16; ++k) st.o[k] = float4v{0.f, 0.f, 0.f, 0.f};
 
     uint32_t* ks_slot = &lds_ks[wave][0][0];
-    PageRaw bufA0, bufA1, bufB0, bufB1;
-    auto load_pair = [&](int pair, PageRaw& x, PageRaw& y) {
-        const int pa = pbeg + 2 * pair;
-        load_page<D>(a, s, kv, pa, ctx, lane, x);
-        if (pa + 1 < pend) load_page<D>(a, s, kv, pa + 1, ctx, lane, y);
-        else y.bits = 0, y.ntok = 0;
-    };
+    // three page pairs in flight per wave: while one pair is processed, the next two load
+    PageRaw a0, a1, b0, b1, c0, c1;
     int pair = wave;
-    if (pair < npairs) load_pair(pair, bufA0, bufA1);
-    while (pair < npairs) {
-        int next = pair + kWaves;
-        if (next < npairs) load_pair(next, bufB0, bufB1);
-        process_pair<D>(bufA0, bufA1, qf, ks_slot, lane, a.scale_log2, st);
-        pair = next;
-        if (pair >= npairs) break;
-        next = pair + kWaves;
-        if (next < npairs) load_pair(next, bufA0, bufA1);
-        process_pair<D>(bufB0, bufB1, qf, ks_slot, lane, a.scale_log2, st);
-        pair = next;
+    if (pair < npairs) {
+        load_pair<D>(a, s, kv, pbeg, pend, pair, npairs, ctx, lane, a0, a1);
+        load_pair<D>(a, s, kv, pbeg, pend, pair + kWaves, npairs, ctx, lane, b0, b1);
+        while (true) {
+            load_pair<D>(a, s, kv, pbeg, pend, pair + 2 * kWaves, npairs, ctx, lane, c0, c1);
+            process_pair<D>(a0, a1, qf, ks_slot, lane, a.scale_log2, st);
+            pair += kWaves;
+            if (pair >= npairs) break;
+            load_pair<D>(a, s, kv, pbeg, pend, pair + 2 * kWaves, npairs, ctx, lane, a0, a1);
+            process_pair<D>(b0, b1, qf, ks_slot, lane, a.scale_log2, st);
+            pair += kWaves;
+            if (pair >= npairs) break;
+            load_pair<D>(a, s, kv, pbeg, pend, pair + 2 * kWaves, npairs, ctx, lane, b0, b1);
+            process_pair<D>(c0, c1, qf, ks_slot, lane, a.scale_log2, st);
+            pair += kWaves;
+            if (pair >= npairs) break;
+        }
     }
 
     // ---- this wave's partial -> LDS
@@ -360,49 +367,74 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
         float acc = 0.f, L = 0.f;
         for (int w = 0; w < kWaves; ++w) {
             const float mw = lds_m[w][hh];
-            const float e = mw == -INFINITY ? 0.f : exp2f(mw - M);
+            const float e = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
             acc += e * lds_o[w][hh][c];
             L += e * lds_l[w][hh];
         }
         if (single) {
             a.out[((size_t)s * a.Hq + kv * grp + hh) * D + c] = L > 0.f ? acc / L : 0.f;
         } else {
-            a.ws_o[part * grp * D + i] = acc;
-            if (c == 0) a.ws_ml[part * grp + hh] = make_float2(M, L);
+            // partials travel through device-coherent (agent-scope) stores and loads, which
+            // bypass the per-XCD L2s, so no cache write-back or invalidate is needed
+            __hip_atomic_store(a.ws_o + part * grp * D + i, acc, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            if (c == 0) {
+                __hip_atomic_store(a.ws_ml + (part * grp + hh) * 2, M, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(a.ws_ml + (part * grp + hh) * 2 + 1, L, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     }
     if (single) return;
 
-    // ---- the last split of this (sequence, KV head) to finish merges all partials in order
-    __threadfence();
+    // ---- the last split of this (sequence, KV head) to finish merges all partials in order.
+    // Every thread waits until its partial stores have completed before the workgroup takes
+    // its ticket; the winner reads the partials with coherent loads issued after the ticket.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) lds_last = atomicAdd(&a.counters[group], 1u) == (unsigned)(nsplit - 1);
+    if (tid == 0)
+        lds_last = __hip_atomic_fetch_add(&a.counters[group], 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(nsplit - 1);
     __syncthreads();
     if (!lds_last) return;
-    __threadfence();
-    const float2* ml = a.ws_ml + (size_t)group * a.splits * grp;
+    // coherent (sc1) reads of the partials as plain buffer loads, so that many are in flight
+    constexpr int kSc1 = 16;                              // cache-policy bit: device coherent
+    const __amdgpu_buffer_rsrc_t ml_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        a.ws_ml + (size_t)group * a.splits * grp * 2, (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t o_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        a.ws_o + (size_t)group * a.splits * grp * D, (short)0, 0x7fffffff, 0x00020000);
     if (tid < grp) {
         float M = -INFINITY;
-        for (int k = 0; k < nsplit; ++k) M = fmaxf(M, ml[k * grp + tid].x);
-        float L = 0.f;
+#pragma unroll 8
         for (int k = 0; k < nsplit; ++k) {
-            const float2 v = ml[k * grp + tid];
-            const float e = v.x == -INFINITY ? 0.f : exp2f(v.x - M);
+            const float mk = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ml_rsrc, ((k * grp + tid) * 2) * 4, 0, kSc1));
+            lds_w[k][tid] = mk;
+            M = fmaxf(M, mk);
+        }
+        float L = 0.f;
+#pragma unroll 8
+        for (int k = 0; k < nsplit; ++k) {
+            const float mk = lds_w[k][tid];
+            const float lk = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ml_rsrc, ((k * grp + tid) * 2 + 1) * 4, 0, kSc1));
+            const float e = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk - M);
             lds_w[k][tid] = e;
-            L += e * v.y;
+            L += e * lk;
         }
         lds_L[tid] = L;
     }
     __syncthreads();
-    const float* po = a.ws_o + (size_t)group * a.splits * grp * D;
     for (int i = tid; i < grp * D; i += kWaves * 64) {
         const int hh = i / D;
         float acc = 0.f;
-        for (int k = 0; k < nsplit; ++k) acc += lds_w[k][hh] * po[(size_t)k * grp * D + i];
+#pragma unroll 8
+        for (int k = 0; k < nsplit; ++k)
+            acc += lds_w[k][hh] * __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(o_rsrc, (k * grp * D + i) * 4, 0, kSc1));
         const float L = lds_L[hh];
         a.out[((size_t)s * a.Hq + kv * grp) * D + i] = L > 0.f ? acc / L : 0.f;
     }
-    if (tid == 0) a.counters[group] = 0u;   // ready for the next call
+    if (tid == 0)
+        __hip_atomic_store(&a.counters[group], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -412,7 +444,7 @@ size_t decode_workspace_bytes(const kv_geometry& g, int batch, int splits) {
     const size_t grp = (size_t)(g.num_q_heads / g.num_kv_heads);
     size_t bytes = 256;                                           // counters, padded
     bytes += ((groups * 4 + 255) / 256) * 256;
-    bytes += ((groups * splits * grp * sizeof(float2) + 255) / 256) * 256;
+    bytes += ((groups * splits * grp * 2 * sizeof(float) + 255) / 256) * 256;
     bytes += groups * splits * grp * g.head_dim * sizeof(float);
     return bytes;
 }
@@ -439,8 +471,8 @@ hipError_t launch_decode_attn(const kv_geometry& g, PoolPtrs pools, const uint32
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     a.counters = reinterpret_cast<uint32_t*>(ws);
     size_t off = ((groups * 4 + 255) / 256) * 256 + 256;
-    a.ws_ml = reinterpret_cast<float2*>(ws + off);
-    off += ((groups * splits * a.grp * sizeof(float2) + 255) / 256) * 256;
+    a.ws_ml = reinterpret_cast<float*>(ws + off);
+    off += ((groups * splits * a.grp * 2 * sizeof(float) + 255) / 256) * 256;
     a.ws_o = reinterpret_cast<float*>(ws + off);
     dim3 grid((unsigned)(splits * a.groups));
     if (g.head_dim == 128)

@@ -96,8 +96,8 @@ def test_kernel_calls_reject_bad_arguments_without_launching():
     with pytest.raises(kvq.KVError) as e:           # workspace too small
         kvq.kv_decode_attn(g, pools, 256, 256, 1, 100, 256, 0.1, 256, 256, need - 1, 0, stream=0)
     assert "workspace" in str(e.value)
-    with pytest.raises(kvq.KVError):                # pages_per_split not a multiple of 16
-        kvq.kv_decode_attn(g, pools, 256, 256, 1, 100, 256, 0.1, 256, 256, 1 << 20, 24, stream=0)
+    with pytest.raises(kvq.KVError):                # pages_per_split odd
+        kvq.kv_decode_attn(g, pools, 256, 256, 1, 100, 256, 0.1, 256, 256, 1 << 20, 25, stream=0)
     with pytest.raises(kvq.KVError):                # context beyond the table
         kvq.kv_decode_attn(g, pools, 256, 256, 1, 8 * 16 + 1, 256, 0.1, 256, 256, 1 << 20, 0, stream=0)
     with pytest.raises(kvq.KVError):
@@ -108,8 +108,8 @@ def test_kernel_calls_reject_bad_arguments_without_launching():
 def test_split_plan():
     g = geom(head_dim=128, num_q_heads=40, num_kv_heads=8, max_seqs=1, max_pages_per_seq=2100)
     pps = kvq.kv_decode_pages_per_split(g, 1, 32768)
-    assert pps % 16 == 0 and pps >= 16
-    assert -(-2048 // pps) * 8 >= 128            # enough workgroups to spread over the chip
+    assert pps % 2 == 0 and pps >= 2
+    assert -(-2048 // pps) * 8 >= 248            # about one workgroup per CU
     g4 = geom(max_seqs=1, max_pages_per_seq=9000)
     assert kvq.kv_decode_pages_per_split(g4, 1, 131072) * 256 >= 8192
 
