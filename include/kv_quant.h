@@ -142,7 +142,7 @@ kv_status kv_quant_write(const kv_geometry* g, const kv_layer_pools* pools, cons
  *   l_t = softmax_scale * sum_c q[s][h][c] K^_t[c],  t in [0, ctx_len[s]),
  *   K^_t[c] = code * K scale of (page of t, c),  V^_t[c] = code * V scale of t.
  *   ctx_len  dev int32 [batch], each in [0, max_ctx_len]; a zero length gives a zero row
- *   q        dev fp16 [batch][H_q][D];  out  dev fp32 [batch][H_q][D]
+ *   q        dev fp16 [batch][H_q][D] (4-byte aligned);  out  dev fp32 [batch][H_q][D] (16-byte aligned)
  *   max_ctx_len    host upper bound on ctx_len, sizes the launch (<= max_pages_per_seq * P)
  *   pages_per_split  pages one workgroup reads (even, >= 2); 0 = chosen by the library
  *   workspace  dev, >= kv_decode_workspace_bytes(...) bytes, zero-filled before its first use;

@@ -350,8 +350,9 @@ kv_status kv_decode_attn(const kv_geometry* g, const kv_layer_pools* pools, cons
     if ((st = decode_plan(g, batch, max_ctx_len, pages_per_split, &pps, &splits)) != KV_OK)
         return st;
     if (!bt || !ctx_len || !q || !out || !workspace) return fail(KV_EINVAL, "NULL device pointer");
-    if (reinterpret_cast<uintptr_t>(q) % 4 || reinterpret_cast<uintptr_t>(workspace) % 256)
-        return fail(KV_EINVAL, "q must be 4-byte and workspace 256-byte aligned");
+    if (reinterpret_cast<uintptr_t>(q) % 4 || reinterpret_cast<uintptr_t>(out) % 16 ||
+        reinterpret_cast<uintptr_t>(workspace) % 256)
+        return fail(KV_EINVAL, "q must be 4-byte, out 16-byte and workspace 256-byte aligned");
     const size_t need = kvq::decode_workspace_bytes(*g, batch, splits);
     if (workspace_bytes < need)
         return fail(KV_EINVAL, "workspace %zu bytes, %zu needed", workspace_bytes, need);

@@ -6,19 +6,23 @@
 // h / group). KV-Kaizen summary, "Background": decoding reads the entire cache per token, so
 // the kernel is built to stream the packed pages at HBM rate.
 //
-// Work decomposition. A workgroup of NW waves owns one (sequence, KV head, split) -- a run of
-// `pps` pages; its waves take page pairs round-robin. Per page pair a wave computes, on MFMA:
-//   S^T[t][h] = sum_c Kcode[t][c] * q'[h][c],   q' = q * Kscale(page)   (16x16x32 f16, 16 tokens)
-//   o^T[c][h] += sum_t Vcode[t][c] * p'[h][t],   p' = p * Vscale(t)     (16x16x32 f16, 32 tokens)
-// Codes are exact small integers in fp16 (built with a shift, a mask and one packed add), the
-// per-channel K scales are folded into q once per page, the per-token V scales into the softmax
-// weights. Computing S and o transposed puts head h in lane h%16 of both products, so the
-// softmax output is the PV operand in place and the rescale by exp(m_old - m_new) is lane-local.
-// Query heads beyond the group (MFMA rows >= group) are zero padding.
-// Waves merge in LDS; splits merge through a workspace: the last workgroup of a (sequence, KV
-// head) to finish -- found with an atomic ticket -- combines the partials in split order, so
-// results do not depend on scheduling. Split index s and group index g map to blockIdx
-// s * groups + g, which keeps all splits of a group on one XCD when groups % 8 == 0.
+// Work decomposition. A workgroup of 8 waves owns one (sequence, KV head, split) -- a run of
+// `pps` pages; its waves take page pairs round-robin, two pairs in flight per wave. Per page
+// pair a wave computes, on MFMA (v_mfma_f32_16x16x32_f16):
+//   S^T[t][h] = sum_c Kcode[t][c] * q'[h][c],  q' = q * Kscale(page, c)     (16 tokens a page)
+//   o^T[c][h] += sum_t Vcode[t][c] * p'[h][t], p' = p * Vscale(t)          (32 tokens a pair)
+// K codes become exact fp16 integers (byte masks + v_perm_b32 + one packed add). The K scales
+// fold into q: exactly for INT2 (code * scale is exact when |code| <= 1), otherwise as two fp16
+// parts hi + lo of q * scale so the products stay exact to ~2^-22. V codes enter the MFMA as
+// fp16 subnormals u * 2^-24 of their unsigned field u = code + 2^(b-1), taken straight from the
+// packed word with a shift and a mask; the offset 2^(b-1) * sum_t p'_t is removed once at the
+// end, from fp32 sums of the same rounded weights. Computing S and o transposed puts head h
+// in lane h%16 of both products, so the softmax output is the PV operand in place and the rescale
+// by exp(m_old - m_new) is lane-local. Query heads beyond the group are zero MFMA rows.
+// Waves merge in LDS; splits merge through the workspace: the last workgroup of a (sequence,
+// KV head) to finish -- found with an atomic ticket -- combines the partials in split order, so
+// results do not depend on scheduling. Split s and group g map to blockIdx s * groups + g, which
+// keeps all splits of a group on one XCD when groups % 8 == 0.
 #include "kvq_device.hpp"
 #include "kvq_launch.hpp"
 
@@ -29,14 +33,15 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 8;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kMaxSplits = 256;
-
 // read-only tables indexed by wave-uniform values: the constant address space lets the compiler
 // use scalar loads, so block-table lookups never wait on the vector-memory counter
 typedef const __attribute__((address_space(4))) uint32_t* const_u32_ptr;
 typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+
+constexpr int kWaves = 8;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kTwo24 = 16777216.0f;
+constexpr int kMaxSplits = 256;
 
 struct AttnArgs {
     PoolPtrs pools;
@@ -71,7 +76,7 @@ struct PageRaw {
 // 16-byte K loads, two 16-byte V loads, one scale dword, one scale pair): the second 16 bytes are
 // only needed by INT8, so INT2/INT4 re-read their first 16 bytes (same cache lines, all inside
 // the section). A fixed count lets the compiler wait for exactly one page's loads while the next
-// pair's loads stay in flight. `page` must be a valid page index even when `present` is false.
+// pairs' loads stay in flight. `page` must be a valid page index even when `present` is false.
 template <int D>
 __device__ __forceinline__ void load_page(const AttnArgs& a, int s, int kv, int page, bool present,
                                           int ctx, int lane, PageRaw& r) {
@@ -116,33 +121,62 @@ __device__ __forceinline__ void load_pair(const AttnArgs& a, int s, int kv, int 
     load_page<D>(a, s, kv, has_b ? pa + 1 : pa, has_b, ctx, lane, y);
 }
 
-// one packed word of codes -> consecutive fp16 pairs holding the signed codes
-__device__ __forceinline__ uint32_t hadd_bias(uint32_t u, float bias) {
-    half2v x = __builtin_bit_cast(half2v, u);
-    half2v b = {(_Float16)bias, (_Float16)bias};
-    return __builtin_bit_cast(uint32_t, x + b);
+__device__ __forceinline__ uint32_t hsub(uint32_t u, float bias) {
+    const half2v b = {(_Float16)bias, (_Float16)bias};
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, u) - b);
 }
 
-// unpack a lane chunk (D*BITS/32 bytes) into D/8 dwords of fp16 pairs, in code order
+// K chunk (D*b/32 bytes) -> D/8 dwords of fp16 pairs holding the signed codes, in code order.
+// Bytes of a masked word are spread into fp16 pairs 0x64uu (= 1024 + u) by v_perm_b32, then the
+// offset 1024 + 2^(b-1) is subtracted exactly.
 template <int D>
-__device__ __forceinline__ void unpack_chunk(const uint32_t* w, int bits, uint32_t* out) {
+__device__ __forceinline__ void unpack_k(const uint32_t* w, int bits, uint32_t* out) {
+    const uint32_t hi = 0x64646464u;
     if (bits == 2) {
 #pragma unroll
         for (int i = 0; i < D / 64; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                out[i * 8 + j] = hadd_bias(((w[i] >> (2 * j)) & 0x00030003u) | 0x64006400u, -1026.0f);
+            for (int j = 0; j < 4; ++j) {   // codes 2j, 2j+1 (bytes 0, 2) and 2j+8, 2j+9 (1, 3)
+                const uint32_t m = (w[i] >> (2 * j)) & 0x03030303u;
+                out[i * 8 + j] = hsub(__builtin_amdgcn_perm(hi, m, 0x04020400u), 1026.0f);
+                out[i * 8 + 4 + j] = hsub(__builtin_amdgcn_perm(hi, m, 0x04030401u), 1026.0f);
+            }
     } else if (bits == 4) {
 #pragma unroll
         for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                out[i * 4 + j] = hadd_bias(((w[i] >> (4 * j)) & 0x000F000Fu) | 0x64006400u, -1032.0f);
+            for (int j = 0; j < 2; ++j) {   // codes 2j, 2j+1 (bytes 0, 2) and 2j+4, 2j+5 (1, 3)
+                const uint32_t m = (w[i] >> (4 * j)) & 0x0F0F0F0Fu;
+                out[i * 4 + j] = hsub(__builtin_amdgcn_perm(hi, m, 0x04020400u), 1032.0f);
+                out[i * 4 + 2 + j] = hsub(__builtin_amdgcn_perm(hi, m, 0x04030401u), 1032.0f);
+            }
     } else {
 #pragma unroll
         for (int i = 0; i < D / 16; ++i) {
-            out[2 * i] = hadd_bias(__builtin_amdgcn_perm(0x64646464u, w[i], 0x04020400u), -1152.0f);
-            out[2 * i + 1] = hadd_bias(__builtin_amdgcn_perm(0x64646464u, w[i], 0x04030401u), -1152.0f);
+            out[2 * i] = hsub(__builtin_amdgcn_perm(hi, w[i], 0x04020400u), 1152.0f);
+            out[2 * i + 1] = hsub(__builtin_amdgcn_perm(hi, w[i], 0x04030401u), 1152.0f);
+        }
+    }
+}
+
+// V chunk -> D/8 dwords of fp16 subnormal pairs (u_a * 2^-24, u_b * 2^-24), in code order
+template <int D>
+__device__ __forceinline__ void unpack_v(const uint32_t* w, int bits, uint32_t* out) {
+    if (bits == 2) {
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) out[i * 8 + j] = (w[i] >> (2 * j)) & 0x00030003u;
+    } else if (bits == 4) {
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) out[i * 4 + j] = (w[i] >> (4 * j)) & 0x000F000Fu;
+    } else {
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) {
+            out[2 * i] = __builtin_amdgcn_perm(0u, w[i], 0x0C020C00u);
+            out[2 * i + 1] = __builtin_amdgcn_perm(0u, w[i], 0x0C030C01u);
         }
     }
 }
@@ -152,17 +186,28 @@ __device__ __forceinline__ half8 make_half8(uint32_t a, uint32_t b, uint32_t c, 
     return __builtin_bit_cast(half8, u);
 }
 
+// max / sum over the four lanes of a head (lanes h, h+16, h+32, h+48)
+__device__ __forceinline__ float rows_max(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16, 64));
+    return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+    x += __shfl_xor(x, 16, 64);
+    return x + __shfl_xor(x, 32, 64);
+}
+
 template <int D>
 struct WaveState {
     float4v o[D / 16];   // o^T tile per channel chunk: lane (h, G) element r -> channel G*D/4 + r*D/16 + k
     float m;             // running max (log2 units) of head lane%16
-    float l;             // this lane's share of the running sum
+    float l;             // this lane's share of the running sum of p
+    float off;           // this lane's share of sum_t 2^(b-1) * p'_t (the V code offset)
 };
 
-// QK for one page: returns S^T for tokens 4G..4G+3 of head lane%16 (log2 units, masked)
+// QK for one page: S^T for tokens 4G..4G+3 of head lane%16, in log2 units, masked
 template <int D>
 __device__ __forceinline__ float4v page_logits(const PageRaw& r, const uint32_t* qf, uint32_t* lds_ks,
-                                      int lane, float scale_log2) {
+                                               int lane, float scale_log2) {
     const int G = lane >> 4;
     // stage the page's K scales through LDS: each lane needs the D/4 scales of its lane group
     // (one wave writes and reads its own slot; LDS serves a wave's requests in order, and the
@@ -172,11 +217,11 @@ __device__ __forceinline__ float4v page_logits(const PageRaw& r, const uint32_t*
     uint32_t ks[D / 8];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) {
-        uint4 v = *reinterpret_cast<const uint4*>(lds_ks + G * (D / 8) + 4 * i);
+        const uint4 v = *reinterpret_cast<const uint4*>(lds_ks + G * (D / 8) + 4 * i);
         ks[4 * i] = v.x; ks[4 * i + 1] = v.y; ks[4 * i + 2] = v.z; ks[4 * i + 3] = v.w;
     }
     uint32_t kf[D / 8];
-    unpack_chunk<D>(r.k, r.bits, kf);
+    unpack_k<D>(r.k, r.bits, kf);
     float4v acc = {0.f, 0.f, 0.f, 0.f};
     if (r.bits == 2) {
         // INT2 codes are -1, 0, 1: code * scale is exact in fp16, so the scales fold into the
@@ -212,57 +257,84 @@ __device__ __forceinline__ float4v page_logits(const PageRaw& r, const uint32_t*
                 kk, make_half8(ql[4 * i], ql[4 * i + 1], ql[4 * i + 2], ql[4 * i + 3]), acc, 0, 0, 0);
         }
     }
-    float4v lg;
+    float4v lg = acc * scale_log2;
+    if (r.ntok < kPage) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lg[i] = (4 * G + i < r.ntok) ? acc[i] * scale_log2 : -INFINITY;
+        for (int i = 0; i < 4; ++i)
+            if (4 * G + i >= r.ntok) lg[i] = -INFINITY;
+    }
     return lg;
+}
+
+// softmax weights of one page times the V scales, as fp16 pairs; masked tokens get exactly 0
+// (their scale slot may hold anything)
+__device__ __forceinline__ void page_weights(const PageRaw& r, const float* p, int G, uint32_t* w) {
+    const half2v p01 = {(_Float16)p[0], (_Float16)p[1]};
+    const half2v p23 = {(_Float16)p[2], (_Float16)p[3]};
+    half2v w01 = p01 * __builtin_bit_cast(half2v, r.vs[0]);
+    half2v w23 = p23 * __builtin_bit_cast(half2v, r.vs[1]);
+    if (r.ntok < kPage) {
+        const int t = 4 * G;
+        if (t >= r.ntok) w01[0] = 0;
+        if (t + 1 >= r.ntok) w01[1] = 0;
+        if (t + 2 >= r.ntok) w23[0] = 0;
+        if (t + 3 >= r.ntok) w23[1] = 0;
+    }
+    w[0] = __builtin_bit_cast(uint32_t, w01);
+    w[1] = __builtin_bit_cast(uint32_t, w23);
 }
 
 template <int D>
 __device__ __forceinline__ void process_pair(const PageRaw& A, const PageRaw& B, const uint32_t* qf,
-                                    uint32_t* lds_ks, int lane, float scale_log2, WaveState<D>& st) {
+                                             uint32_t* lds_ks, int lane, float scale_log2,
+                                             WaveState<D>& st) {
     const int G = lane >> 4;
-    float4v la = page_logits<D>(A, qf, lds_ks, lane, scale_log2);
+    const float4v la = page_logits<D>(A, qf, lds_ks, lane, scale_log2);
     float4v lb = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     if (B.bits) lb = page_logits<D>(B, qf, lds_ks + 64, lane, scale_log2);
 
     // online softmax over the pair's 32 tokens, per head (lanes h, h+16, h+32, h+48)
     float mx = fmaxf(fmaxf(fmaxf(la[0], la[1]), fmaxf(la[2], la[3])),
                      fmaxf(fmaxf(lb[0], lb[1]), fmaxf(lb[2], lb[3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = rows_max(mx);
     const float m_new = fmaxf(st.m, mx);            // finite: page A holds >= 1 valid token
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);   // 0 on the first pair (m = -inf)
-    st.m = m_new;
-    float pa[4], pb[4], sum = 0.f;
+    if (__builtin_amdgcn_ballot_w64(m_new != st.m)) {
+        const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);   // 0 on the first pair
+        st.l *= alpha;
+        st.off *= alpha;
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k) st.o[k] *= alpha;
+        st.m = m_new;
+    }
+    float pa[4], pb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         pa[i] = __builtin_amdgcn_exp2f(la[i] - m_new);
         pb[i] = __builtin_amdgcn_exp2f(lb[i] - m_new);
-        sum += pa[i] + pb[i];
     }
-    st.l = st.l * alpha + sum;
-#pragma unroll
-    for (int k = 0; k < D / 16; ++k) st.o[k] *= alpha;
+    st.l += ((pa[0] + pa[1]) + (pa[2] + pa[3])) + ((pb[0] + pb[1]) + (pb[2] + pb[3]));
 
-    // p' = p * V scale of the token; masked tokens get exactly 0 (their scale may be anything)
-    const float sa[4] = {f16_val((uint16_t)(A.vs[0] & 0xffffu)), f16_val((uint16_t)(A.vs[0] >> 16)),
-                         f16_val((uint16_t)(A.vs[1] & 0xffffu)), f16_val((uint16_t)(A.vs[1] >> 16))};
-    const float sb[4] = {f16_val((uint16_t)(B.vs[0] & 0xffffu)), f16_val((uint16_t)(B.vs[0] >> 16)),
-                         f16_val((uint16_t)(B.vs[1] & 0xffffu)), f16_val((uint16_t)(B.vs[1] >> 16))};
-    float wa[4], wb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        wa[i] = (4 * G + i < A.ntok) ? pa[i] * sa[i] : 0.f;
-        wb[i] = (B.bits && 4 * G + i < B.ntok) ? pb[i] * sb[i] : 0.f;
+    uint32_t wgt[4];
+    page_weights(A, pa, G, wgt);
+    if (B.bits) {
+        page_weights(B, pb, G, wgt + 2);
+    } else {
+        wgt[2] = 0u;
+        wgt[3] = 0u;
     }
-    const half8 pf = {(_Float16)wa[0], (_Float16)wa[1], (_Float16)wa[2], (_Float16)wa[3],
-                      (_Float16)wb[0], (_Float16)wb[1], (_Float16)wb[2], (_Float16)wb[3]};
+    // fp32 sums of the same rounded weights, times each page's code offset 2^(b-1)
+    const half2v one = {(_Float16)1.0f, (_Float16)1.0f};
+    const float sa = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, wgt[0]), one,
+                     __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, wgt[1]), one, 0.f, false), false);
+    const float sb = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, wgt[2]), one,
+                     __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, wgt[3]), one, 0.f, false), false);
+    st.off += (float)(1 << (A.bits - 1)) * sa + (B.bits ? (float)(1 << (B.bits - 1)) * sb : 0.f);
+    const half8 pf = make_half8(wgt[0], wgt[1], wgt[2], wgt[3]);
 
     uint32_t va[D / 8], vb[D / 8];
-    unpack_chunk<D>(A.v, A.bits, va);
+    unpack_v<D>(A.v, A.bits, va);
     if (B.bits) {
-        unpack_chunk<D>(B.v, B.bits, vb);
+        unpack_v<D>(B.v, B.bits, vb);
     } else {
 #pragma unroll
         for (int i = 0; i < D / 8; ++i) vb[i] = 0u;
@@ -275,11 +347,12 @@ __device__ __forceinline__ void process_pair(const PageRaw& A, const PageRaw& B,
 
 template <int D>
 __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
-    __shared__ uint32_t lds_ks[kWaves][2][64];
-    __shared__ float lds_o[kWaves][kMaxGroup][D];
+    __shared__ __attribute__((aligned(16))) uint32_t lds_ks[kWaves][2][64];
+    __shared__ __attribute__((aligned(16))) float lds_o[kWaves][kMaxGroup][D];
     __shared__ float lds_m[kWaves][kMaxGroup];
     __shared__ float lds_l[kWaves][kMaxGroup];
     __shared__ float lds_w[kMaxSplits][kMaxGroup];   // split weights in the final merge
+    __shared__ float lds_lk[kMaxSplits][kMaxGroup];  // split sums in the final merge
     __shared__ float lds_L[kMaxGroup];
     __shared__ int lds_last;
 
@@ -315,36 +388,33 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
     WaveState<D> st;
     st.m = -INFINITY;
     st.l = 0.f;
+    st.off = 0.f;
 #pragma unroll
     for (int k = 0; k < D / 16; ++k) st.o[k] = float4v{0.f, 0.f, 0.f, 0.f};
 
     uint32_t* ks_slot = &lds_ks[wave][0][0];
-    // three page pairs in flight per wave: while one pair is processed, the next two load
-    PageRaw a0, a1, b0, b1, c0, c1;
+    // two page pairs in flight per wave: while one pair is processed, the next one loads (a
+    // deeper rotation made the compiler drain the loads in flight before each new issue)
+    PageRaw a0, a1, b0, b1;
     int pair = wave;
     if (pair < npairs) {
         load_pair<D>(a, s, kv, pbeg, pend, pair, npairs, ctx, lane, a0, a1);
-        load_pair<D>(a, s, kv, pbeg, pend, pair + kWaves, npairs, ctx, lane, b0, b1);
         while (true) {
-            load_pair<D>(a, s, kv, pbeg, pend, pair + 2 * kWaves, npairs, ctx, lane, c0, c1);
+            load_pair<D>(a, s, kv, pbeg, pend, pair + kWaves, npairs, ctx, lane, b0, b1);
             process_pair<D>(a0, a1, qf, ks_slot, lane, a.scale_log2, st);
             pair += kWaves;
             if (pair >= npairs) break;
-            load_pair<D>(a, s, kv, pbeg, pend, pair + 2 * kWaves, npairs, ctx, lane, a0, a1);
+            load_pair<D>(a, s, kv, pbeg, pend, pair + kWaves, npairs, ctx, lane, a0, a1);
             process_pair<D>(b0, b1, qf, ks_slot, lane, a.scale_log2, st);
-            pair += kWaves;
-            if (pair >= npairs) break;
-            load_pair<D>(a, s, kv, pbeg, pend, pair + 2 * kWaves, npairs, ctx, lane, b0, b1);
-            process_pair<D>(c0, c1, qf, ks_slot, lane, a.scale_log2, st);
             pair += kWaves;
             if (pair >= npairs) break;
         }
     }
 
-    // ---- this wave's partial -> LDS
-    float lsum = st.l;
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
+    // ---- this wave's partial -> LDS; V codes carried their offset 2^(b-1) and the 2^-24 of
+    // the subnormal representation: o = 2^24 * acc - sum_t 2^(b-1) p'_t
+    const float lsum = rows_sum(st.l);
+    const float off = rows_sum(st.off);
     if (h < grp) {
         if (G == 0) {
             lds_m[wave][h] = st.m;
@@ -353,7 +423,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int k = 0; k < D / 16; ++k)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) lds_o[wave][h][G * (D / 4) + r * (D / 16) + k] = st.o[k][r];
+            for (int r = 0; r < 4; ++r)
+                lds_o[wave][h][G * (D / 4) + r * (D / 16) + k] = st.o[k][r] * kTwo24 - off;
     }
     __syncthreads();
 
@@ -398,40 +469,61 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
                                           __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(nsplit - 1);
     __syncthreads();
     if (!lds_last) return;
-    // coherent (sc1) reads of the partials as plain buffer loads, so that many are in flight
+
+    // Coherent (sc1) reads of the partials as plain buffer loads, all issued before any is
+    // used: one memory round trip for the (max, sum) pairs, one for the outputs.
     constexpr int kSc1 = 16;                              // cache-policy bit: device coherent
     const __amdgpu_buffer_rsrc_t ml_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         a.ws_ml + (size_t)group * a.splits * grp * 2, (short)0, 0x7fffffff, 0x00020000);
     const __amdgpu_buffer_rsrc_t o_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         a.ws_o + (size_t)group * a.splits * grp * D, (short)0, 0x7fffffff, 0x00020000);
+    for (int i = tid; i < nsplit * grp; i += kWaves * 64) {
+        const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(ml_rsrc, i * 8, 0, kSc1));
+        lds_w[i / grp][i % grp] = __builtin_bit_cast(float, v.x);        // max, then weight
+        lds_lk[i / grp][i % grp] = __builtin_bit_cast(float, v.y);       // sum
+    }
+    __syncthreads();
     if (tid < grp) {
         float M = -INFINITY;
-#pragma unroll 8
-        for (int k = 0; k < nsplit; ++k) {
-            const float mk = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ml_rsrc, ((k * grp + tid) * 2) * 4, 0, kSc1));
-            lds_w[k][tid] = mk;
-            M = fmaxf(M, mk);
-        }
+        for (int k = 0; k < nsplit; ++k) M = fmaxf(M, lds_w[k][tid]);
         float L = 0.f;
-#pragma unroll 8
         for (int k = 0; k < nsplit; ++k) {
             const float mk = lds_w[k][tid];
-            const float lk = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ml_rsrc, ((k * grp + tid) * 2 + 1) * 4, 0, kSc1));
             const float e = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk - M);
             lds_w[k][tid] = e;
-            L += e * lk;
+            L += e * lds_lk[k][tid];
         }
         lds_L[tid] = L;
     }
     __syncthreads();
-    for (int i = tid; i < grp * D; i += kWaves * 64) {
-        const int hh = i / D;
-        float acc = 0.f;
-#pragma unroll 8
-        for (int k = 0; k < nsplit; ++k)
-            acc += lds_w[k][hh] * __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(o_rsrc, (k * grp * D + i) * 4, 0, kSc1));
-        const float L = lds_L[hh];
-        a.out[((size_t)s * a.Hq + kv * grp) * D + i] = L > 0.f ? acc / L : 0.f;
+    // outputs in float4 slots; the splits of a slot are shared by kParts threads, each summing
+    // a contiguous run of splits, and the runs are added in order
+    constexpr int kParts = 4;
+    const int slots = grp * D / 4;
+    const int per_part = (nsplit + kParts - 1) / kParts;
+    float4v* part_acc = reinterpret_cast<float4v*>(&lds_o[0][0][0]);   // [kParts][slots]
+    for (int job = tid; job < slots * kParts; job += kWaves * 64) {
+        const int slot = job % slots, pidx = job / slots;
+        const int hh = slot * 4 / D;
+        const int k0 = pidx * per_part, k1 = min(nsplit, k0 + per_part);
+        float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 16
+        for (int k = k0; k < k1; ++k) {
+            const float4v v = __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(
+                o_rsrc, (k * grp * D + slot * 4) * 4, 0, kSc1));
+            acc += lds_w[k][hh] * v;
+        }
+        part_acc[pidx * slots + slot] = acc;
+    }
+    __syncthreads();
+    for (int slot = tid; slot < slots; slot += kWaves * 64) {
+        float4v acc = part_acc[slot];
+#pragma unroll
+        for (int pidx = 1; pidx < kParts; ++pidx) acc += part_acc[pidx * slots + slot];
+        const float L = lds_L[slot * 4 / D];
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        float* o = a.out + ((size_t)s * a.Hq + kv * grp) * D + slot * 4;
+        *reinterpret_cast<float4*>(o) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
     }
     if (tid == 0)
         __hip_atomic_store(&a.counters[group], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

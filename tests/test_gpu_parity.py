@@ -142,6 +142,32 @@ def test_ragged_batch_gqa_shapes(hq, hkv, d):
     assert np.abs(kl - okl).max() <= KL_TOL and np.abs(rows - orows).max() <= KL_TOL
 
 
+@pytest.mark.parametrize("hq,hkv,d", [(40, 8, 128), (8, 2, 64)])
+@pytest.mark.parametrize("mix", ["int8", "int4", "int2", "mixed"])
+def test_many_page_pairs_per_wave(hq, hkv, d, mix):
+    """long splits: each wave walks up to 8 page pairs (ctx 2048 and 1500, up to 128 pages per
+    split), so the loaded-ahead page buffers are refilled many times inside the loop"""
+    case_banner(f"many pairs hq={hq} hkv={hkv} d={d} {mix}")
+    g = np.random.default_rng(d * 10 + len(mix))
+    lens = [2048, 1500]
+    if mix == "mixed":
+        tiers = [list(g.integers(0, 3, size=130)) for _ in lens]
+    else:
+        tiers = [[{"int2": 0, "int4": 1, "int8": 2}[mix]] * 130 for _ in lens]
+    L = LayerPair(hq, hkv, d, len(lens), 130, tiers, seed=d)
+    for s, n in enumerate(lens):
+        K = synth.normal_f16(g, (1, n, hkv, d))
+        V = synth.normal_f16(g, (1, n, hkv, d))
+        L.write(K, V, rows=[s])
+    q = synth.normal_f16(g, (len(lens), hq, d))
+    ref = L.oracle_attn(q)
+    for pps in (0, 32, 64, 128):
+        got, _ = L.attn(q, pages_per_split=pps)
+        err = rowwise_rel_err(got, ref)
+        print(f"  attn pps={pps} max rel err {err.max():.3e}")
+        assert err.max() <= ATTN_TOL, (pps, err.max())
+
+
 def test_deterministic_and_workspace_reuse():
     case_banner("determinism")
     L = tiny_layer(2)
