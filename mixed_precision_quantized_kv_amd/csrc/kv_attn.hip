@@ -14,11 +14,12 @@
 // K codes become exact fp16 integers (byte masks + v_perm_b32 + one packed add). The K scales
 // fold into q: exactly for INT2 (code * scale is exact when |code| <= 1), otherwise as two fp16
 // parts hi + lo of q * scale so the products stay exact to ~2^-22. V codes enter the MFMA as
-// fp16 subnormals u * 2^-24 of their unsigned field u = code + 2^(b-1), taken straight from the
-// packed word with a shift and a mask; the offset 2^(b-1) * sum_t p'_t is removed once at the
-// end, from fp32 sums of the same rounded weights. Computing S and o transposed puts head h
-// in lane h%16 of both products, so the softmax output is the PV operand in place and the rescale
-// by exp(m_old - m_new) is lane-local. Query heads beyond the group are zero MFMA rows.
+// signed fp16 subnormals code * 2^-24, taken from the packed word with a shift and a mask and one
+// exact packed subtract of the field offset 2^(b-1) * 2^-24; the weights p * Vscale enter as two
+// fp16 parts hi + lo of their fp32 product (two MFMAs), so no term carries more than ~2^-22 of
+// rounding and nothing cancels. Computing S and o transposed puts head h in lane h%16 of both
+// products, so the softmax output is the PV operand in place and the rescale by
+// exp(m_old - m_new) is lane-local. Query heads beyond the group are zero MFMA rows.
 // Waves merge in LDS; splits merge through the workspace: the last workgroup of a (sequence,
 // KV head) to finish -- found with an atomic ticket -- combines the partials in split order, so
 // results do not depend on scheduling. Split s and group g map to blockIdx s * groups + g, which
@@ -159,24 +160,32 @@ __device__ __forceinline__ void unpack_k(const uint32_t* w, int bits, uint32_t* 
     }
 }
 
-// V chunk -> D/8 dwords of fp16 subnormal pairs (u_a * 2^-24, u_b * 2^-24), in code order
+// V chunk -> D/8 dwords of signed fp16 subnormal pairs (code_a * 2^-24, code_b * 2^-24), in code
+// order: the field u = code + 2^(b-1) as a subnormal, minus 2^(b-1) * 2^-24 (exact: both operands
+// are subnormals of the same exponent)
+__device__ __forceinline__ uint32_t sub_subnormal(uint32_t u, uint32_t offset) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, u) - __builtin_bit_cast(half2v, offset));
+}
+
 template <int D>
 __device__ __forceinline__ void unpack_v(const uint32_t* w, int bits, uint32_t* out) {
     if (bits == 2) {
 #pragma unroll
         for (int i = 0; i < D / 64; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) out[i * 8 + j] = (w[i] >> (2 * j)) & 0x00030003u;
+            for (int j = 0; j < 8; ++j)
+                out[i * 8 + j] = sub_subnormal((w[i] >> (2 * j)) & 0x00030003u, 0x00020002u);
     } else if (bits == 4) {
 #pragma unroll
         for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) out[i * 4 + j] = (w[i] >> (4 * j)) & 0x000F000Fu;
+            for (int j = 0; j < 4; ++j)
+                out[i * 4 + j] = sub_subnormal((w[i] >> (4 * j)) & 0x000F000Fu, 0x00080008u);
     } else {
 #pragma unroll
         for (int i = 0; i < D / 16; ++i) {
-            out[2 * i] = __builtin_amdgcn_perm(0u, w[i], 0x0C020C00u);
-            out[2 * i + 1] = __builtin_amdgcn_perm(0u, w[i], 0x0C030C01u);
+            out[2 * i] = sub_subnormal(__builtin_amdgcn_perm(0u, w[i], 0x0C020C00u), 0x00800080u);
+            out[2 * i + 1] = sub_subnormal(__builtin_amdgcn_perm(0u, w[i], 0x0C030C01u), 0x00800080u);
         }
     }
 }
@@ -201,7 +210,6 @@ struct WaveState {
     float4v o[D / 16];   // o^T tile per channel chunk: lane (h, G) element r -> channel G*D/4 + r*D/16 + k
     float m;             // running max (log2 units) of head lane%16
     float l;             // this lane's share of the running sum of p
-    float off;           // this lane's share of sum_t 2^(b-1) * p'_t (the V code offset)
 };
 
 // QK for one page: S^T for tokens 4G..4G+3 of head lane%16, in log2 units, masked
@@ -266,22 +274,27 @@ __device__ __forceinline__ float4v page_logits(const PageRaw& r, const uint32_t*
     return lg;
 }
 
-// softmax weights of one page times the V scales, as fp16 pairs; masked tokens get exactly 0
-// (their scale slot may hold anything)
-__device__ __forceinline__ void page_weights(const PageRaw& r, const float* p, int G, uint32_t* w) {
-    const half2v p01 = {(_Float16)p[0], (_Float16)p[1]};
-    const half2v p23 = {(_Float16)p[2], (_Float16)p[3]};
-    half2v w01 = p01 * __builtin_bit_cast(half2v, r.vs[0]);
-    half2v w23 = p23 * __builtin_bit_cast(half2v, r.vs[1]);
+// softmax weights of one page times the V scales: the fp32 product p * s split into fp16 parts
+// hi = round(p * s) and lo = round(p * s - hi), as pairs for this lane's four tokens; masked
+// tokens get exactly 0 (their scale slot may hold anything)
+__device__ __forceinline__ void page_weights(const PageRaw& r, const float* p, int G, uint32_t* wh,
+                                             uint32_t* wl) {
+    const half2v s01 = __builtin_bit_cast(half2v, r.vs[0]);
+    const half2v s23 = __builtin_bit_cast(half2v, r.vs[1]);
+    float ps[4] = {p[0] * (float)s01[0], p[1] * (float)s01[1], p[2] * (float)s23[0], p[3] * (float)s23[1]};
     if (r.ntok < kPage) {
-        const int t = 4 * G;
-        if (t >= r.ntok) w01[0] = 0;
-        if (t + 1 >= r.ntok) w01[1] = 0;
-        if (t + 2 >= r.ntok) w23[0] = 0;
-        if (t + 3 >= r.ntok) w23[1] = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (4 * G + i >= r.ntok) ps[i] = 0.f;
     }
-    w[0] = __builtin_bit_cast(uint32_t, w01);
-    w[1] = __builtin_bit_cast(uint32_t, w23);
+    const half2v h01 = {(_Float16)ps[0], (_Float16)ps[1]};
+    const half2v h23 = {(_Float16)ps[2], (_Float16)ps[3]};
+    const half2v l01 = {(_Float16)(ps[0] - (float)h01[0]), (_Float16)(ps[1] - (float)h01[1])};
+    const half2v l23 = {(_Float16)(ps[2] - (float)h23[0]), (_Float16)(ps[3] - (float)h23[1])};
+    wh[0] = __builtin_bit_cast(uint32_t, h01);
+    wh[1] = __builtin_bit_cast(uint32_t, h23);
+    wl[0] = __builtin_bit_cast(uint32_t, l01);
+    wl[1] = __builtin_bit_cast(uint32_t, l23);
 }
 
 template <int D>
@@ -301,7 +314,6 @@ __device__ __forceinline__ void process_pair(const PageRaw& A, const PageRaw& B,
     if (__builtin_amdgcn_ballot_w64(m_new != st.m)) {
         const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);   // 0 on the first pair
         st.l *= alpha;
-        st.off *= alpha;
 #pragma unroll
         for (int k = 0; k < D / 16; ++k) st.o[k] *= alpha;
         st.m = m_new;
@@ -314,22 +326,15 @@ __device__ __forceinline__ void process_pair(const PageRaw& A, const PageRaw& B,
     }
     st.l += ((pa[0] + pa[1]) + (pa[2] + pa[3])) + ((pb[0] + pb[1]) + (pb[2] + pb[3]));
 
-    uint32_t wgt[4];
-    page_weights(A, pa, G, wgt);
+    uint32_t wh[4], wl[4];
+    page_weights(A, pa, G, wh, wl);
     if (B.bits) {
-        page_weights(B, pb, G, wgt + 2);
+        page_weights(B, pb, G, wh + 2, wl + 2);
     } else {
-        wgt[2] = 0u;
-        wgt[3] = 0u;
+        wh[2] = wh[3] = wl[2] = wl[3] = 0u;
     }
-    // fp32 sums of the same rounded weights, times each page's code offset 2^(b-1)
-    const half2v one = {(_Float16)1.0f, (_Float16)1.0f};
-    const float sa = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, wgt[0]), one,
-                     __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, wgt[1]), one, 0.f, false), false);
-    const float sb = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, wgt[2]), one,
-                     __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, wgt[3]), one, 0.f, false), false);
-    st.off += (float)(1 << (A.bits - 1)) * sa + (B.bits ? (float)(1 << (B.bits - 1)) * sb : 0.f);
-    const half8 pf = make_half8(wgt[0], wgt[1], wgt[2], wgt[3]);
+    const half8 ph = make_half8(wh[0], wh[1], wh[2], wh[3]);
+    const half8 pl = make_half8(wl[0], wl[1], wl[2], wl[3]);
 
     uint32_t va[D / 8], vb[D / 8];
     unpack_v<D>(A.v, A.bits, va);
@@ -340,9 +345,11 @@ __device__ __forceinline__ void process_pair(const PageRaw& A, const PageRaw& B,
         for (int i = 0; i < D / 8; ++i) vb[i] = 0u;
     }
 #pragma unroll
-    for (int k = 0; k < D / 16; ++k)
-        st.o[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-            make_half8(va[2 * k], va[2 * k + 1], vb[2 * k], vb[2 * k + 1]), pf, st.o[k], 0, 0, 0);
+    for (int k = 0; k < D / 16; ++k) {
+        const half8 vv = make_half8(va[2 * k], va[2 * k + 1], vb[2 * k], vb[2 * k + 1]);
+        st.o[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vv, ph, st.o[k], 0, 0, 0);
+        st.o[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vv, pl, st.o[k], 0, 0, 0);
+    }
 }
 
 template <int D>
@@ -388,7 +395,6 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
     WaveState<D> st;
     st.m = -INFINITY;
     st.l = 0.f;
-    st.off = 0.f;
 #pragma unroll
     for (int k = 0; k < D / 16; ++k) st.o[k] = float4v{0.f, 0.f, 0.f, 0.f};
 
@@ -411,10 +417,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
         }
     }
 
-    // ---- this wave's partial -> LDS; V codes carried their offset 2^(b-1) and the 2^-24 of
-    // the subnormal representation: o = 2^24 * acc - sum_t 2^(b-1) p'_t
+    // ---- this wave's partial -> LDS; the V codes carried the 2^-24 of their subnormal form
     const float lsum = rows_sum(st.l);
-    const float off = rows_sum(st.off);
     if (h < grp) {
         if (G == 0) {
             lds_m[wave][h] = st.m;
@@ -424,7 +428,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
         for (int k = 0; k < D / 16; ++k)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                lds_o[wave][h][G * (D / 4) + r * (D / 16) + k] = st.o[k][r] * kTwo24 - off;
+                lds_o[wave][h][G * (D / 4) + r * (D / 16) + k] = st.o[k][r] * kTwo24;
     }
     __syncthreads();
 

@@ -135,6 +135,17 @@ def keys_values(w: Workload, layer: int, n_tokens: int, stream_k: int, stream_v:
     return k, v
 
 
+def sequence_keys_values(w: Workload, layer: int, seq: int, n_tokens: int):
+    """K and V of one sequence, [1][n][H_kv][D] uint16 fp16 bits, from a stream of its own (ragged
+    batches draw each sequence separately, so no array spans the longest length times the batch)."""
+    shape = (1, n_tokens, w.num_kv_heads, w.head_dim)
+    gk = np.random.Generator(np.random.PCG64(np.random.SeedSequence(
+        [MASTER_SEED, w.config_id, layer, S_PREFILL_K, 0, seq])))
+    gv = np.random.Generator(np.random.PCG64(np.random.SeedSequence(
+        [MASTER_SEED, w.config_id, layer, S_PREFILL_V, 0, seq])))
+    return normal_f16(gk, shape, outlier_mask(w, layer)), normal_f16(gv, shape)
+
+
 def queries(w: Workload, layer: int, step: int = 0, batch: Optional[int] = None) -> np.ndarray:
     B = w.batch if batch is None else batch
     return normal_f16(rng(w, layer, S_Q, step), (B, w.num_q_heads, w.head_dim))
