@@ -124,8 +124,8 @@ kv_status kv_check_block_table(const kv_alloc* a, const uint32_t* bt_host);
  * One layer, `batch` sequences (rows 0..batch-1 of bt, pos, ring), n_new tokens each:
  *   bt     dev uint32 [max_seqs][max_pages_per_seq]  handles; every page touched must be allocated
  *   pos    dev int32  [batch]      tokens already cached in each sequence
- *   k_new, v_new  dev fp16 [batch][n_new][H_kv][D]
- *   ring   dev fp16 [max_seqs][R][H_kv][D], in/out: position p lives in slot p % R
+ *   k_new, v_new  dev fp16 [batch][n_new][H_kv][D] (16-byte aligned)
+ *   ring   dev fp16 [max_seqs][R][H_kv][D] (16-byte aligned), in/out: position p lives in slot p % R
  * For every page touched, the K scales and codes of all its present tokens are recomputed from
  * their FP16 originals (ring for positions < pos, k_new after), so writing token by token gives
  * the same bytes as writing at once. Each new value vector gets its own scale; codes of earlier

@@ -302,9 +302,9 @@ kv_status kv_quant_write(const kv_geometry* g, const kv_layer_pools* pools, cons
         return fail(KV_EINVAL, "n_new %d", n_new);
     if (batch == 0 || n_new == 0) return ok();
     if (!bt || !pos || !k_new || !v_new || !ring) return fail(KV_EINVAL, "NULL device pointer");
-    if (reinterpret_cast<uintptr_t>(k_new) % 4 || reinterpret_cast<uintptr_t>(v_new) % 4 ||
-        reinterpret_cast<uintptr_t>(ring) % 4)
-        return fail(KV_EINVAL, "fp16 buffers must be 4-byte aligned");
+    if (reinterpret_cast<uintptr_t>(k_new) % 16 || reinterpret_cast<uintptr_t>(v_new) % 16 ||
+        reinterpret_cast<uintptr_t>(ring) % 16)
+        return fail(KV_EINVAL, "k_new, v_new and ring must be 16-byte aligned");
     return hip_status(kvq::launch_quant_write(*g, pool_ptrs(pools), bt, pos, batch, n_new, k_new,
                                               v_new, ring, static_cast<hipStream_t>(stream)),
                       "kv_quant_write");

@@ -78,10 +78,20 @@ struct PageRaw {
 // only needed by INT8, so INT2/INT4 re-read their first 16 bytes (same cache lines, all inside
 // the section). A fixed count lets the compiler wait for exactly one page's loads while the next
 // pairs' loads stay in flight. `page` must be a valid page index even when `present` is false.
+// what the width-independent page loads need, as plain values (the kernel argument block is
+// never addressed, so it stays in scalar registers)
+struct PageSrc {
+    const uint8_t* base0;
+    const uint8_t* base1;
+    const uint8_t* base2;
+    const uint32_t* bt_row;   // this sequence's block-table row
+    int H;
+};
+
 template <int D>
-__device__ __forceinline__ void load_page(const AttnArgs& a, int s, int kv, int page, bool present,
+__device__ __forceinline__ void load_page(const PageSrc& a, int kv, int page, bool present,
                                           int ctx, int lane, PageRaw& r) {
-    const uint32_t handle = ((const_u32_ptr)a.bt)[(size_t)s * a.max_pages + page];
+    const uint32_t handle = ((const_u32_ptr)a.bt_row)[page];
     const int tier = (int)(handle >> 30);
     const uint32_t idx = handle & 0x3fffffffu;
     const int bits = bits_of_tier(tier);
@@ -89,7 +99,12 @@ __device__ __forceinline__ void load_page(const AttnArgs& a, int s, int kv, int 
     r.ntok = present ? min(kPage, ctx - page * kPage) : 0;
     const uint32_t code_bytes = kPage * D * bits / 8;
     const uint32_t sec_bytes = 2 * code_bytes + 2 * D + 2 * kPage;
-    const uint8_t* base = tier == 0 ? a.pools.base[0] : tier == 1 ? a.pools.base[1] : a.pools.base[2];
+    // pool base by arithmetic rather than a select chain, which the compiler would otherwise
+    // turn into a lookup table in scratch memory
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(a.base0);
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(
+        b0 + (uintptr_t)(tier == 1) * (reinterpret_cast<uintptr_t>(a.base1) - b0) +
+        (uintptr_t)(tier == 2) * (reinterpret_cast<uintptr_t>(a.base2) - b0));
     const uint8_t* sec = base + ((size_t)idx * a.H + kv) * sec_bytes;
     const int t = lane & 15, G = lane >> 4;
     const int ch = D * bits / 32;                   // bytes of one lane chunk
@@ -112,14 +127,50 @@ __device__ __forceinline__ void load_page(const AttnArgs& a, int s, int kv, int 
 // page pair `pair` of the split [pbeg, pend); pairs past the end reload the last pair (their
 // data is never used) so that every iteration issues the same loads
 template <int D>
-__device__ __forceinline__ void load_pair(const AttnArgs& a, int s, int kv, int pbeg, int pend,
+__device__ __forceinline__ void load_pair(const PageSrc& a, int kv, int pbeg, int pend,
                                           int pair, int npairs, int ctx, int lane, PageRaw& x,
                                           PageRaw& y) {
     const int pc = min(pair, npairs - 1);
     const int pa = pbeg + 2 * pc;
     const bool has_b = pa + 1 < pend;
-    load_page<D>(a, s, kv, pa, true, ctx, lane, x);
-    load_page<D>(a, s, kv, has_b ? pa + 1 : pa, has_b, ctx, lane, y);
+    load_page<D>(a, kv, pa, true, ctx, lane, x);
+    load_page<D>(a, kv, has_b ? pa + 1 : pa, has_b, ctx, lane, y);
+}
+
+// Loads of one page whose width is known at compile time: exactly the bytes this lane needs
+// (K and V chunks of D*b/32 bytes each, one K-scale dword, one V-scale pair).
+template <int D, int BITS>
+__device__ __forceinline__ void load_page_t(const uint8_t* base, uint32_t idx, int H, int kv,
+                                            bool present, int ntok, int lane, PageRaw& r) {
+    constexpr uint32_t code_bytes = kPage * D * BITS / 8;
+    constexpr uint32_t sec_bytes = 2 * code_bytes + 2 * D + 2 * kPage;
+    constexpr int ch = D * BITS / 32;              // bytes of one lane chunk: 4, 8, 16 or 32
+    const uint8_t* sec = base + ((size_t)idx * H + kv) * sec_bytes;
+    const int t = lane & 15, G = lane >> 4;
+    const uint8_t* kp = sec + t * (D * BITS / 8) + G * ch;
+    const uint8_t* vp = sec + code_bytes + 2 * D + (G * D + t * (D / 16)) * BITS / 2;
+    if constexpr (ch == 4) {
+        r.k[0] = *reinterpret_cast<const uint32_t*>(kp);
+        r.v[0] = *reinterpret_cast<const uint32_t*>(vp);
+    } else if constexpr (ch == 8) {
+        const uint2 k0 = *reinterpret_cast<const uint2*>(kp);
+        const uint2 v0 = *reinterpret_cast<const uint2*>(vp);
+        r.k[0] = k0.x; r.k[1] = k0.y;
+        r.v[0] = v0.x; r.v[1] = v0.y;
+    } else {
+#pragma unroll
+        for (int h = 0; h < ch / 16; ++h) {
+            const uint4 k0 = *reinterpret_cast<const uint4*>(kp + 16 * h);
+            const uint4 v0 = *reinterpret_cast<const uint4*>(vp + 16 * h);
+            r.k[4 * h] = k0.x; r.k[4 * h + 1] = k0.y; r.k[4 * h + 2] = k0.z; r.k[4 * h + 3] = k0.w;
+            r.v[4 * h] = v0.x; r.v[4 * h + 1] = v0.y; r.v[4 * h + 2] = v0.z; r.v[4 * h + 3] = v0.w;
+        }
+    }
+    r.ks = *reinterpret_cast<const uint32_t*>(sec + code_bytes + 4 * (lane & (D / 2 - 1)));
+    const uint2 vs = *reinterpret_cast<const uint2*>(sec + 2 * code_bytes + 2 * D + 8 * G);
+    r.vs[0] = vs.x; r.vs[1] = vs.y;
+    r.bits = present ? BITS : 0;
+    r.ntok = ntok;
 }
 
 __device__ __forceinline__ uint32_t hsub(uint32_t u, float bias) {
@@ -214,8 +265,8 @@ struct WaveState {
 
 // QK for one page: S^T for tokens 4G..4G+3 of head lane%16, in log2 units, masked
 template <int D>
-__device__ __forceinline__ float4v page_logits(const PageRaw& r, const uint32_t* qf, uint32_t* lds_ks,
-                                               int lane, float scale_log2) {
+__device__ __forceinline__ float4v page_logits(const PageRaw& r, int bits, const uint32_t* qf,
+                                               uint32_t* lds_ks, int lane, float scale_log2) {
     const int G = lane >> 4;
     // stage the page's K scales through LDS: each lane needs the D/4 scales of its lane group
     // (one wave writes and reads its own slot; LDS serves a wave's requests in order, and the
@@ -229,9 +280,9 @@ __device__ __forceinline__ float4v page_logits(const PageRaw& r, const uint32_t*
         ks[4 * i] = v.x; ks[4 * i + 1] = v.y; ks[4 * i + 2] = v.z; ks[4 * i + 3] = v.w;
     }
     uint32_t kf[D / 8];
-    unpack_k<D>(r.k, r.bits, kf);
+    unpack_k<D>(r.k, bits, kf);
     float4v acc = {0.f, 0.f, 0.f, 0.f};
-    if (r.bits == 2) {
+    if (bits == 2) {
         // INT2 codes are -1, 0, 1: code * scale is exact in fp16, so the scales fold into the
         // keys and every MFMA product is exact
 #pragma unroll
@@ -297,14 +348,18 @@ __device__ __forceinline__ void page_weights(const PageRaw& r, const float* p, i
     wl[1] = __builtin_bit_cast(uint32_t, l23);
 }
 
-template <int D>
+// One page pair: QK, online softmax and PV. BITS is the width of both pages when the caller
+// knows it at compile time, 0 when each page carries its own; page B may be absent (bits 0).
+template <int D, int BITS>
 __device__ __forceinline__ void process_pair(const PageRaw& A, const PageRaw& B, const uint32_t* qf,
                                              uint32_t* lds_ks, int lane, float scale_log2,
                                              WaveState<D>& st) {
     const int G = lane >> 4;
-    const float4v la = page_logits<D>(A, qf, lds_ks, lane, scale_log2);
+    const int bits_a = BITS ? BITS : A.bits;
+    const int bits_b = BITS ? BITS : B.bits;
+    const float4v la = page_logits<D>(A, bits_a, qf, lds_ks, lane, scale_log2);
     float4v lb = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    if (B.bits) lb = page_logits<D>(B, qf, lds_ks + 64, lane, scale_log2);
+    if (B.bits) lb = page_logits<D>(B, bits_b, qf, lds_ks + 64, lane, scale_log2);
 
     // online softmax over the pair's 32 tokens, per head (lanes h, h+16, h+32, h+48)
     float mx = fmaxf(fmaxf(fmaxf(la[0], la[1]), fmaxf(la[2], la[3])),
@@ -337,9 +392,9 @@ __device__ __forceinline__ void process_pair(const PageRaw& A, const PageRaw& B,
     const half8 pl = make_half8(wl[0], wl[1], wl[2], wl[3]);
 
     uint32_t va[D / 8], vb[D / 8];
-    unpack_v<D>(A.v, A.bits, va);
+    unpack_v<D>(A.v, bits_a, va);
     if (B.bits) {
-        unpack_v<D>(B.v, B.bits, vb);
+        unpack_v<D>(B.v, bits_b, vb);
     } else {
 #pragma unroll
         for (int i = 0; i < D / 8; ++i) vb[i] = 0u;
@@ -349,6 +404,64 @@ __device__ __forceinline__ void process_pair(const PageRaw& A, const PageRaw& B,
         const half8 vv = make_half8(va[2 * k], va[2 * k + 1], vb[2 * k], vb[2 * k + 1]);
         st.o[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vv, ph, st.o[k], 0, 0, 0);
         st.o[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vv, pl, st.o[k], 0, 0, 0);
+    }
+}
+
+// Page pair q of a wave's chunk [cb, cb + npg) whose handles sit in `hv` (lane i: page cb + i),
+// all of width BITS. Pairs past the end reload the last pair (their data is never used).
+template <int D, int BITS>
+__device__ __forceinline__ void load_pair_t(const uint8_t* base, uint32_t hv, int H, int kv, int cb,
+                                            int npg, int q, int nq, int ctx, int lane, PageRaw& x,
+                                            PageRaw& y) {
+    const int pa = 2 * min(q, nq - 1);
+    const bool has_b = pa + 1 < npg;
+    const uint32_t ia = (uint32_t)__builtin_amdgcn_readlane((int)hv, pa) & 0x3fffffffu;
+    const uint32_t ib = (uint32_t)__builtin_amdgcn_readlane((int)hv, has_b ? pa + 1 : pa) & 0x3fffffffu;
+    const int page = cb + pa;
+    load_page_t<D, BITS>(base, ia, H, kv, true, min(kPage, ctx - page * kPage), lane, x);
+    load_page_t<D, BITS>(base, ib, H, kv, has_b, has_b ? min(kPage, ctx - (page + 1) * kPage) : 0,
+                         lane, y);
+}
+
+// A wave's chunk of pages, all of one width: two pairs in flight (while one pair is processed
+// the next one loads), no per-page branching and no block-table reads in the loop.
+template <int D, int BITS>
+__device__ __forceinline__ void wave_chunk_uniform(const uint8_t* base, uint32_t hv, int H, int kv,
+                                                   int cb, int npg, int ctx, int lane,
+                                                   const uint32_t* qf, uint32_t* ks_slot,
+                                                   float scale_log2, WaveState<D>& st) {
+    const int nq = (npg + 1) / 2;
+    PageRaw a0, a1, b0, b1;
+    int q = 0;
+    load_pair_t<D, BITS>(base, hv, H, kv, cb, npg, 0, nq, ctx, lane, a0, a1);
+    while (true) {
+        load_pair_t<D, BITS>(base, hv, H, kv, cb, npg, q + 1, nq, ctx, lane, b0, b1);
+        process_pair<D, BITS>(a0, a1, qf, ks_slot, lane, scale_log2, st);
+        if (++q >= nq) break;
+        load_pair_t<D, BITS>(base, hv, H, kv, cb, npg, q + 1, nq, ctx, lane, a0, a1);
+        process_pair<D, BITS>(b0, b1, qf, ks_slot, lane, scale_log2, st);
+        if (++q >= nq) break;
+    }
+}
+
+// The same for a chunk whose pages may differ in width: handles from the block table, the
+// width-independent loads of load_page and per-page width branches.
+template <int D>
+__device__ __forceinline__ void wave_chunk_mixed(const PageSrc& src, int kv, int cb, int npg,
+                                                 int ctx, int lane, const uint32_t* qf,
+                                                 uint32_t* ks_slot, float scale_log2,
+                                                 WaveState<D>& st) {
+    const int nq = (npg + 1) / 2;
+    PageRaw a0, a1, b0, b1;
+    int q = 0;
+    load_pair<D>(src, kv, cb, cb + npg, 0, nq, ctx, lane, a0, a1);
+    while (true) {
+        load_pair<D>(src, kv, cb, cb + npg, q + 1, nq, ctx, lane, b0, b1);
+        process_pair<D, 0>(a0, a1, qf, ks_slot, lane, scale_log2, st);
+        if (++q >= nq) break;
+        load_pair<D>(src, kv, cb, cb + npg, q + 1, nq, ctx, lane, a0, a1);
+        process_pair<D, 0>(b0, b1, qf, ks_slot, lane, scale_log2, st);
+        if (++q >= nq) break;
     }
 }
 
@@ -380,7 +493,6 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
     }
     const int pbeg = split * a.pps;
     const int pend = min(pbeg + a.pps, npages);
-    const int npairs = (pend - pbeg + 1) / 2;
 
     // q fragment: lane (h, G) holds q[h][G*D/4 .. +D/4) as fp16 pairs (zero for h >= grp)
     const int h = lane & 15, G = lane >> 4;
@@ -399,21 +511,36 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
     for (int k = 0; k < D / 16; ++k) st.o[k] = float4v{0.f, 0.f, 0.f, 0.f};
 
     uint32_t* ks_slot = &lds_ks[wave][0][0];
-    // two page pairs in flight per wave: while one pair is processed, the next one loads (a
-    // deeper rotation made the compiler drain the loads in flight before each new issue)
-    PageRaw a0, a1, b0, b1;
-    int pair = wave;
-    if (pair < npairs) {
-        load_pair<D>(a, s, kv, pbeg, pend, pair, npairs, ctx, lane, a0, a1);
-        while (true) {
-            load_pair<D>(a, s, kv, pbeg, pend, pair + kWaves, npairs, ctx, lane, b0, b1);
-            process_pair<D>(a0, a1, qf, ks_slot, lane, a.scale_log2, st);
-            pair += kWaves;
-            if (pair >= npairs) break;
-            load_pair<D>(a, s, kv, pbeg, pend, pair + kWaves, npairs, ctx, lane, a0, a1);
-            process_pair<D>(b0, b1, qf, ks_slot, lane, a.scale_log2, st);
-            pair += kWaves;
-            if (pair >= npairs) break;
+    // Each wave takes a contiguous chunk of the split (sizes differ by at most one page) and
+    // walks it in page pairs. A chunk of at most 64 pages has its handles read once into
+    // registers (lane i: page cb + i); when they all share one width -- the common case, since
+    // a layer changes width at most at a tier switch -- the chunk runs a loop specialized for
+    // that width.
+    const int n = pend - pbeg;
+    const int cb = pbeg + (wave * n) / kWaves;
+    const int npg = pbeg + ((wave + 1) * n) / kWaves - cb;
+    if (npg > 0) {
+        bool uniform = false;
+        uint32_t hv = 0;
+        int tier0 = 0;
+        if (npg <= 64) {
+            hv = a.bt[(size_t)s * a.max_pages + cb + min(lane, npg - 1)];
+            tier0 = (int)((uint32_t)__builtin_amdgcn_readfirstlane((int)hv) >> 30);
+            uniform = __builtin_amdgcn_ballot_w64((int)(hv >> 30) != tier0) == 0;
+        }
+        if (uniform && tier0 == 0)
+            wave_chunk_uniform<D, 2>(a.pools.base[0], hv, a.H, kv, cb, npg, ctx, lane, qf, ks_slot,
+                                     a.scale_log2, st);
+        else if (uniform && tier0 == 1)
+            wave_chunk_uniform<D, 4>(a.pools.base[1], hv, a.H, kv, cb, npg, ctx, lane, qf, ks_slot,
+                                     a.scale_log2, st);
+        else if (uniform && tier0 == 2)
+            wave_chunk_uniform<D, 8>(a.pools.base[2], hv, a.H, kv, cb, npg, ctx, lane, qf, ks_slot,
+                                     a.scale_log2, st);
+        else {
+            const PageSrc src = {a.pools.base[0], a.pools.base[1], a.pools.base[2],
+                                 a.bt + (size_t)s * a.max_pages, a.H};
+            wave_chunk_mixed<D>(src, kv, cb, npg, ctx, lane, qf, ks_slot, a.scale_log2, st);
         }
     }
 
@@ -474,60 +601,83 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
     __syncthreads();
     if (!lds_last) return;
 
-    // Coherent (sc1) reads of the partials as plain buffer loads, all issued before any is
-    // used: one memory round trip for the (max, sum) pairs, one for the outputs.
+    // Coherent (sc1) reads of the partials as plain buffer loads. Output slot `slot` (four
+    // channels of one head) is summed over the splits by `parts` threads, each over a contiguous
+    // run of at most kBatch splits per round; every thread issues its (max, sum) pair and its first
+    // round of partial outputs before it waits on the pair, so the merge costs one memory round
+    // trip in the common case. Loads past a thread's range re-read a valid entry and are ignored.
     constexpr int kSc1 = 16;                              // cache-policy bit: device coherent
+    constexpr int kBatch = 16;
     const __amdgpu_buffer_rsrc_t ml_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         a.ws_ml + (size_t)group * a.splits * grp * 2, (short)0, 0x7fffffff, 0x00020000);
     const __amdgpu_buffer_rsrc_t o_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         a.ws_o + (size_t)group * a.splits * grp * D, (short)0, 0x7fffffff, 0x00020000);
-    for (int i = tid; i < nsplit * grp; i += kWaves * 64) {
-        const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(ml_rsrc, i * 8, 0, kSc1));
-        lds_w[i / grp][i % grp] = __builtin_bit_cast(float, v.x);        // max, then weight
-        lds_lk[i / grp][i % grp] = __builtin_bit_cast(float, v.y);       // sum
-    }
-    __syncthreads();
-    if (tid < grp) {
-        float M = -INFINITY;
-        for (int k = 0; k < nsplit; ++k) M = fmaxf(M, lds_w[k][tid]);
-        float L = 0.f;
-        for (int k = 0; k < nsplit; ++k) {
-            const float mk = lds_w[k][tid];
-            const float e = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk - M);
-            lds_w[k][tid] = e;
-            L += e * lds_lk[k][tid];
-        }
-        lds_L[tid] = L;
-    }
-    __syncthreads();
-    // outputs in float4 slots; the splits of a slot are shared by kParts threads, each summing
-    // a contiguous run of splits, and the runs are added in order
-    constexpr int kParts = 4;
+    const int npair_ml = nsplit * grp;
+    const uint2 ml_first = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+        ml_rsrc, min(tid, npair_ml - 1) * 8, 0, kSc1));
     const int slots = grp * D / 4;
-    const int per_part = (nsplit + kParts - 1) / kParts;
-    float4v* part_acc = reinterpret_cast<float4v*>(&lds_o[0][0][0]);   // [kParts][slots]
-    for (int job = tid; job < slots * kParts; job += kWaves * 64) {
-        const int slot = job % slots, pidx = job / slots;
-        const int hh = slot * 4 / D;
-        const int k0 = pidx * per_part, k1 = min(nsplit, k0 + per_part);
-        float4v acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 16
-        for (int k = k0; k < k1; ++k) {
-            const float4v v = __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(
-                o_rsrc, (k * grp * D + slot * 4) * 4, 0, kSc1));
-            acc += lds_w[k][hh] * v;
-        }
-        part_acc[pidx * slots + slot] = acc;
+    const int parts = max(1, min(nsplit, (kWaves * 64) / slots));
+    const int per_part = (nsplit + parts - 1) / parts;
+    const bool has_job = tid < slots * parts;
+    const int job = has_job ? tid : 0;
+    const int slot = job % slots, pidx = job / slots;
+    const int hh = slot * 4 / D;
+    const int k0 = pidx * per_part;                      // this job's splits: [k0, k1)
+    const int k1 = min(nsplit, k0 + per_part);
+    float4v buf[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+        buf[i] = __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(
+            o_rsrc, (min(k0 + i, nsplit - 1) * grp * D + slot * 4) * 4, 0, kSc1));
+    if (tid < npair_ml) {
+        lds_w[tid / grp][tid % grp] = __builtin_bit_cast(float, ml_first.x);   // max, then weight
+        lds_lk[tid / grp][tid % grp] = __builtin_bit_cast(float, ml_first.y);  // sum
+    }
+    for (int i = tid + kWaves * 64; i < npair_ml; i += kWaves * 64) {
+        const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(ml_rsrc, i * 8, 0, kSc1));
+        lds_w[i / grp][i % grp] = __builtin_bit_cast(float, v.x);
+        lds_lk[i / grp][i % grp] = __builtin_bit_cast(float, v.y);
     }
     __syncthreads();
-    for (int slot = tid; slot < slots; slot += kWaves * 64) {
-        float4v acc = part_acc[slot];
+    // split weights, one wave per head: global max, e_k = 2^(m_k - M), L = sum_k e_k * l_k
+    for (int h2 = wave; h2 < grp; h2 += kWaves) {
+        float M = -INFINITY;
+        for (int k = lane; k < nsplit; k += 64) M = fmaxf(M, lds_w[k][h2]);
+        M = wave_max(M);
+        float L = 0.f;
+        for (int k = lane; k < nsplit; k += 64) {
+            const float mk = lds_w[k][h2];
+            const float e = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk - M);
+            lds_w[k][h2] = e;
+            L += e * lds_lk[k][h2];
+        }
+        L = wave_sum(L);
+        if (lane == 0) lds_L[h2] = L;
+    }
+    __syncthreads();
+    float4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int pidx = 1; pidx < kParts; ++pidx) acc += part_acc[pidx * slots + slot];
-        const float L = lds_L[slot * 4 / D];
+    for (int i = 0; i < kBatch; ++i)
+        if (k0 + i < k1) acc += lds_w[k0 + i][hh] * buf[i];
+    for (int kb = k0 + kBatch; kb < k1; kb += kBatch) {         // long split lists only
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+            buf[i] = __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(
+                o_rsrc, (min(kb + i, nsplit - 1) * grp * D + slot * 4) * 4, 0, kSc1));
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+            if (kb + i < k1) acc += lds_w[kb + i][hh] * buf[i];
+    }
+    float4v* part_acc = reinterpret_cast<float4v*>(&lds_o[0][0][0]);   // [parts][slots]
+    if (has_job) part_acc[pidx * slots + slot] = acc;
+    __syncthreads();
+    for (int sl = tid; sl < slots; sl += kWaves * 64) {
+        float4v sum = part_acc[sl];
+        for (int pi = 1; pi < parts; ++pi) sum += part_acc[pi * slots + sl];
+        const float L = lds_L[sl * 4 / D];
         const float inv = L > 0.f ? 1.f / L : 0.f;
-        float* o = a.out + ((size_t)s * a.Hq + kv * grp) * D + slot * 4;
-        *reinterpret_cast<float4*>(o) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+        float* o = a.out + ((size_t)s * a.Hq + kv * grp) * D + sl * 4;
+        *reinterpret_cast<float4*>(o) = make_float4(sum[0] * inv, sum[1] * inv, sum[2] * inv, sum[3] * inv);
     }
     if (tid == 0)
         __hip_atomic_store(&a.counters[group], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
