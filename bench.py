@@ -4,7 +4,8 @@
 A step is one pass of the whole hot path over one synthetic decode token: for every layer,
 quantize-on-write of the new key/value (kv_quant_write) followed by decode attention over the
 paged mixed-precision cache (kv_decode_attn); on every 64th step the KL canary runs for every
-layer (kv_canary_kl). Inputs are resident in HBM before timing starts.
+layer (kv_canary_kl). Inputs are resident in HBM before timing starts; each timed step is
+replayed from a HIP graph holding exactly the eager step's launches.
 
     python bench.py [--gpus 1] [--steps 256] [--warmup 10] [--workload qwen14b_32k]
 
@@ -191,18 +192,43 @@ def run(args):
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
-    def step(i, canary: bool):
+    def writes_and_attention(i, sp_):
         for l in range(L):
             kvq.kv_quant_write(m.g, m.pools[l], m.bt[l], pos_all[i], B, nn, k_all[i, l], v_all[i, l],
-                               m.ring[l], stream=sp)
+                               m.ring[l], stream=sp_)
             kvq.kv_decode_attn(m.g, m.pools[l], m.bt[l], ctx_all[i], B, m.max_ctx, q_all[i, l], scale,
-                               out, ws, wsb, pps, stream=sp)
-            if canary:
-                kvq.kv_canary_kl(m.g, m.ring[l], ctx_all[i], B, q_all[i, l], scale, kl[l], None,
-                                 cws, cwsb, stream=sp)
+                               out, ws, wsb, pps, stream=sp_)
 
-    for i in range(args.warmup):
-        step(i, i % CANARY_EVERY == 0)
+    def attention_only(i, sp_):
+        for l in range(L):
+            kvq.kv_decode_attn(m.g, m.pools[l], m.bt[l], ctx_all[i], B, m.max_ctx, q_all[i, l], scale,
+                               out, ws, wsb, pps, stream=sp_)
+
+    def canary_all(i, sp_):
+        for l in range(L):
+            kvq.kv_canary_kl(m.g, m.ring[l], ctx_all[i], B, q_all[i, l], scale, kl[l], None,
+                             cws, cwsb, stream=sp_)
+
+    for i in range(args.warmup):                         # eager warm-up steps
+        writes_and_attention(i, sp)
+        if i % CANARY_EVERY == 0:
+            canary_all(i, sp)
+    torch.cuda.synchronize()
+
+    # Each timed step is replayed from a HIP graph captured once (one launch per step from the
+    # host instead of ~2L+1): a decode step is a chain of short kernels, and launching them one
+    # by one from Python would time the interpreter, not the GPU. A step's graph holds the same
+    # launches, with the same arguments, as the eager step.
+    def capture(fn, i):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(i, torch.cuda.current_stream().cuda_stream)
+        return g
+
+    steps_idx = [args.warmup + j for j in range(args.steps)]
+    g_step = [capture(writes_and_attention, i) for i in steps_idx]
+    g_attn = [capture(attention_only, i) for i in steps_idx]
+    g_canary = {j: capture(canary_all, steps_idx[j]) for j in range(0, args.steps, CANARY_EVERY)}
     torch.cuda.synchronize()
 
     # timed window: K steps, the canary firing on every 64th
@@ -210,45 +236,36 @@ def run(args):
     torch.cuda.synchronize()
     t_start.record(stream)
     for j in range(args.steps):
-        i = args.warmup + j
-        step(i, j % CANARY_EVERY == 0)
+        g_step[j].replay()
+        if j in g_canary:
+            g_canary[j].replay()
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
 
-    # attention launch durations: a second window of the same K steps in which each step issues
-    # its L writes first and then its L attention launches back to back, with HIP events on the
-    # launch stream around the attention group (each layer's attention reads only its own
-    # layer's cache, so the order changes no result); the per-launch time is the group's time / L
+    # attention launch durations: events on the launch stream around each step's L attention
+    # launches, replayed back to back (the caches already hold the step's tokens, and each
+    # layer's attention reads only its own layer's cache); the per-launch time is the group's / L
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     torch.cuda.synchronize()
     for j in range(args.steps):
-        i = args.warmup + j
-        for l in range(L):
-            kvq.kv_quant_write(m.g, m.pools[l], m.bt[l], pos_all[i], B, nn, k_all[i, l], v_all[i, l],
-                               m.ring[l], stream=sp)
         evs[j][0].record(stream)
-        for l in range(L):
-            kvq.kv_decode_attn(m.g, m.pools[l], m.bt[l], ctx_all[i], B, m.max_ctx, q_all[i, l], scale,
-                               out, ws, wsb, pps, stream=sp)
+        g_attn[j].replay()
         evs[j][1].record(stream)
-        if j % CANARY_EVERY == 0:
-            for l in range(L):
-                kvq.kv_canary_kl(m.g, m.ring[l], ctx_all[i], B, q_all[i, l], scale, kl[l], None,
-                                 cws, cwsb, stream=sp)
     torch.cuda.synchronize()
     attn_group_ms = np.array([a.elapsed_time(b) for (a, b) in evs])          # [K], L launches each
 
-    # step without the canary (for its overhead)
+    # steps without the canary (for its overhead)
     torch.cuda.synchronize()
     t_start.record(stream)
     for j in range(args.steps):
-        step(args.warmup + j, False)
+        g_step[j].replay()
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_step_nocanary = t_start.elapsed_time(t_end) / args.steps
+    del g_step, g_attn, g_canary
 
     # algorithmic bytes
     lens = m.lens0.astype(np.int64)

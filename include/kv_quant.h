@@ -162,8 +162,8 @@ kv_status kv_decode_attn(const kv_geometry* g, const kv_layer_pools* pools, cons
  * for each sequence the n = min(seq_len[s], R) newest keys (positions seq_len-n .. seq_len-1).
  * quant_b is the cache's own quantizer, grouped by each key's page (one scale per page and
  * channel); the copies are temporary. Rows use the softmax_scale of attention.
- *   ring     dev fp16 [max_seqs][R][H_kv][D];  seq_len dev int32 [batch], >= 0
- *   q        dev fp16 [batch][H_q][D]
+ *   ring     dev fp16 [max_seqs][R][H_kv][D] (16-byte aligned);  seq_len dev int32 [batch], >= 0
+ *   q        dev fp16 [batch][H_q][D] (16-byte aligned)
  *   kl_out   dev fp32 [3]: mean over batch*H_q rows for b = 2, 4, 8
  *   kl_rows  dev fp32 [batch][H_q][3] or NULL
  *   workspace dev, >= kv_canary_workspace_bytes(g, batch), zero-filled before its first use */

@@ -376,6 +376,8 @@ kv_status kv_canary_kl(const kv_geometry* g, const uint16_t* ring, const int32_t
     if (batch < 1 || batch > g->max_seqs) return fail(KV_EINVAL, "batch %d", batch);
     if (!ring || !seq_len || !q || !kl_out || !workspace)
         return fail(KV_EINVAL, "NULL device pointer");
+    if (reinterpret_cast<uintptr_t>(ring) % 16 || reinterpret_cast<uintptr_t>(q) % 16)
+        return fail(KV_EINVAL, "ring and q must be 16-byte aligned");
     if (reinterpret_cast<uintptr_t>(workspace) % 256)
         return fail(KV_EINVAL, "workspace must be 256-byte aligned");
     const size_t need = kvq::canary_workspace_bytes(*g, batch);

@@ -328,15 +328,15 @@ __device__ __forceinline__ float4v page_logits(const PageRaw& r, int bits, const
 // softmax weights of one page times the V scales: the fp32 product p * s split into fp16 parts
 // hi = round(p * s) and lo = round(p * s - hi), as pairs for this lane's four tokens; masked
 // tokens get exactly 0 (their scale slot may hold anything)
-__device__ __forceinline__ void page_weights(const PageRaw& r, const float* p, int G, uint32_t* wh,
-                                             uint32_t* wl) {
-    const half2v s01 = __builtin_bit_cast(half2v, r.vs[0]);
-    const half2v s23 = __builtin_bit_cast(half2v, r.vs[1]);
+__device__ __forceinline__ void page_weights(uint32_t vs0, uint32_t vs1, int ntok, const float* p,
+                                             int G, uint32_t* wh, uint32_t* wl) {
+    const half2v s01 = __builtin_bit_cast(half2v, vs0);
+    const half2v s23 = __builtin_bit_cast(half2v, vs1);
     float ps[4] = {p[0] * (float)s01[0], p[1] * (float)s01[1], p[2] * (float)s23[0], p[3] * (float)s23[1]};
-    if (r.ntok < kPage) {
+    if (ntok < kPage) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            if (4 * G + i >= r.ntok) ps[i] = 0.f;
+            if (4 * G + i >= ntok) ps[i] = 0.f;
     }
     const half2v h01 = {(_Float16)ps[0], (_Float16)ps[1]};
     const half2v h23 = {(_Float16)ps[2], (_Float16)ps[3]};
@@ -382,9 +382,9 @@ __device__ __forceinline__ void process_pair(const PageRaw& A, const PageRaw& B,
     st.l += ((pa[0] + pa[1]) + (pa[2] + pa[3])) + ((pb[0] + pb[1]) + (pb[2] + pb[3]));
 
     uint32_t wh[4], wl[4];
-    page_weights(A, pa, G, wh, wl);
+    page_weights(A.vs[0], A.vs[1], A.ntok, pa, G, wh, wl);
     if (B.bits) {
-        page_weights(B, pb, G, wh + 2, wl + 2);
+        page_weights(B.vs[0], B.vs[1], B.ntok, pb, G, wh + 2, wl + 2);
     } else {
         wh[2] = wh[3] = wl[2] = wl[3] = 0u;
     }
@@ -409,6 +409,150 @@ __device__ __forceinline__ void process_pair(const PageRaw& A, const PageRaw& B,
 
 // Page pair q of a wave's chunk [cb, cb + npg) whose handles sit in `hv` (lane i: page cb + i),
 // all of width BITS. Pairs past the end reload the last pair (their data is never used).
+// The same pair for groups of at most 8 query heads. The 16 head columns of the MFMA tiles hold
+// both pages: lanes with h = lane % 16 < 8 carry page A for head h, lanes h >= 8 page B for head
+// h - 8. The scaled query q * Kscale is then computed once for both pages (each lane with its
+// own page's scales), each lane keeps four logits and four weights instead of eight, and the PV
+// product accumulates page B's share in columns 8..15, folded into 0..7 at the end.
+template <int D, int BITS>
+__device__ __forceinline__ void process_pair_half(const PageRaw& A, const PageRaw& B,
+                                                  const uint32_t* qf, uint32_t* lds_ks, int lane,
+                                                  float scale_log2, WaveState<D>& st) {
+    const int G = lane >> 4;
+    const bool side = (lane & 8) != 0;
+    const int bits_a = BITS ? BITS : A.bits;
+    const int bits_b = BITS ? BITS : B.bits;
+    const bool has_b = B.bits != 0;
+    const int ntok = side ? B.ntok : A.ntok;
+    lds_ks[lane] = A.ks;
+    lds_ks[64 + lane] = B.ks;
+    __builtin_amdgcn_wave_barrier();
+    float4v acc;
+    if (bits_a == 2 && bits_b == 2) {
+        // INT2: the scales fold exactly into each page's keys, q is used as is
+        uint32_t ksa[D / 8], ksb[D / 8];
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) {
+            const uint4 va = *reinterpret_cast<const uint4*>(lds_ks + G * (D / 8) + 4 * i);
+            const uint4 vb = *reinterpret_cast<const uint4*>(lds_ks + 64 + G * (D / 8) + 4 * i);
+            ksa[4 * i] = va.x; ksa[4 * i + 1] = va.y; ksa[4 * i + 2] = va.z; ksa[4 * i + 3] = va.w;
+            ksb[4 * i] = vb.x; ksb[4 * i + 1] = vb.y; ksb[4 * i + 2] = vb.z; ksb[4 * i + 3] = vb.w;
+        }
+        uint32_t kfa[D / 8], kfb[D / 8];
+        unpack_k<D>(A.k, 2, kfa);
+        unpack_k<D>(B.k, 2, kfb);
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) {
+            kfa[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, kfa[i]) *
+                                                      __builtin_bit_cast(half2v, ksa[i]));
+            kfb[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, kfb[i]) *
+                                                      __builtin_bit_cast(half2v, ksb[i]));
+        }
+        float4v acca = {0.f, 0.f, 0.f, 0.f}, accb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) {
+            const half8 qq = make_half8(qf[4 * i], qf[4 * i + 1], qf[4 * i + 2], qf[4 * i + 3]);
+            acca = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                make_half8(kfa[4 * i], kfa[4 * i + 1], kfa[4 * i + 2], kfa[4 * i + 3]), qq, acca, 0, 0, 0);
+            if (has_b)
+                accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    make_half8(kfb[4 * i], kfb[4 * i + 1], kfb[4 * i + 2], kfb[4 * i + 3]), qq, accb, 0, 0, 0);
+        }
+        acc = side ? accb : acca;
+    } else {
+        // q * Kscale of this lane's page as fp16 hi + lo; the two pages' keys against it
+        uint32_t ks[D / 8];
+        const uint32_t* src = lds_ks + (side ? 64 : 0) + G * (D / 8);
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) {
+            const uint4 v = *reinterpret_cast<const uint4*>(src + 4 * i);
+            ks[4 * i] = v.x; ks[4 * i + 1] = v.y; ks[4 * i + 2] = v.z; ks[4 * i + 3] = v.w;
+        }
+        uint32_t qh[D / 8], ql[D / 8];
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) {
+            const half2v q2 = __builtin_bit_cast(half2v, qf[i]);
+            const half2v s2 = __builtin_bit_cast(half2v, ks[i]);
+            const half2v hi = q2 * s2;
+            qh[i] = __builtin_bit_cast(uint32_t, hi);
+            ql[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q2, s2, -hi));
+        }
+        uint32_t kfa[D / 8], kfb[D / 8];
+        unpack_k<D>(A.k, bits_a, kfa);
+        if (has_b) unpack_k<D>(B.k, bits_b, kfb);
+        float4v acca = {0.f, 0.f, 0.f, 0.f}, accb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) {
+            const half8 hq = make_half8(qh[4 * i], qh[4 * i + 1], qh[4 * i + 2], qh[4 * i + 3]);
+            const half8 lq = make_half8(ql[4 * i], ql[4 * i + 1], ql[4 * i + 2], ql[4 * i + 3]);
+            const half8 ka = make_half8(kfa[4 * i], kfa[4 * i + 1], kfa[4 * i + 2], kfa[4 * i + 3]);
+            acca = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, hq, acca, 0, 0, 0);
+            acca = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, lq, acca, 0, 0, 0);
+            if (has_b) {
+                const half8 kb = make_half8(kfb[4 * i], kfb[4 * i + 1], kfb[4 * i + 2], kfb[4 * i + 3]);
+                accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, hq, accb, 0, 0, 0);
+                accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, lq, accb, 0, 0, 0);
+            }
+        }
+        acc = side ? accb : acca;
+    }
+    float4v lg = acc * scale_log2;
+    if (ntok < kPage) {                                  // includes an absent page B (ntok 0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (4 * G + i >= ntok) lg[i] = -INFINITY;
+    }
+
+    // online softmax over the pair's 32 tokens: a head's lanes are h, h+8 and the four rows
+    float mx = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 8, 64));
+    mx = rows_max(mx);
+    const float m_new = fmaxf(st.m, mx);            // finite: page A holds >= 1 valid token
+    if (__builtin_amdgcn_ballot_w64(m_new != st.m)) {
+        const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);   // 0 on the first pair
+        st.l *= alpha;
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k) st.o[k] *= alpha;
+        st.m = m_new;
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(lg[i] - m_new);
+    st.l += (p[0] + p[1]) + (p[2] + p[3]);
+
+    uint32_t wh[2], wl[2];
+    page_weights(side ? B.vs[0] : A.vs[0], side ? B.vs[1] : A.vs[1], ntok, p, G, wh, wl);
+    const uint32_t z = 0u;
+    const half8 ph = make_half8(side ? z : wh[0], side ? z : wh[1], side ? wh[0] : z, side ? wh[1] : z);
+    const half8 pl = make_half8(side ? z : wl[0], side ? z : wl[1], side ? wl[0] : z, side ? wl[1] : z);
+
+    uint32_t va[D / 8], vb[D / 8];
+    unpack_v<D>(A.v, bits_a, va);
+    if (has_b) {
+        unpack_v<D>(B.v, bits_b, vb);
+    } else {
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) vb[i] = 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) {
+        const half8 vv = make_half8(va[2 * k], va[2 * k + 1], vb[2 * k], vb[2 * k + 1]);
+        st.o[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vv, ph, st.o[k], 0, 0, 0);
+        st.o[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vv, pl, st.o[k], 0, 0, 0);
+    }
+}
+
+// one pair through the layout the kernel was instantiated for
+template <int D, int BITS, bool HALF>
+__device__ __forceinline__ void run_pair(const PageRaw& A, const PageRaw& B, const uint32_t* qf,
+                                         uint32_t* lds_ks, int lane, float scale_log2,
+                                         WaveState<D>& st) {
+    if constexpr (HALF)
+        process_pair_half<D, BITS>(A, B, qf, lds_ks, lane, scale_log2, st);
+    else
+        process_pair<D, BITS>(A, B, qf, lds_ks, lane, scale_log2, st);
+}
+
 template <int D, int BITS>
 __device__ __forceinline__ void load_pair_t(const uint8_t* base, uint32_t hv, int H, int kv, int cb,
                                             int npg, int q, int nq, int ctx, int lane, PageRaw& x,
@@ -423,30 +567,38 @@ __device__ __forceinline__ void load_pair_t(const uint8_t* base, uint32_t hv, in
                          lane, y);
 }
 
-// A wave's chunk of pages, all of one width: two pairs in flight (while one pair is processed
-// the next one loads), no per-page branching and no block-table reads in the loop.
-template <int D, int BITS>
+// A wave's chunk of pages, all of one width, with DEPTH page pairs in flight: while pair q is
+// processed, pairs q+1 .. q+DEPTH-1 are loading. The rotation over the DEPTH buffers is unrolled,
+// so every buffer index is a constant. No per-page branching and no block-table reads in the loop.
+template <int D, int BITS, int DEPTH, bool HALF>
 __device__ __forceinline__ void wave_chunk_uniform(const uint8_t* base, uint32_t hv, int H, int kv,
                                                    int cb, int npg, int ctx, int lane,
                                                    const uint32_t* qf, uint32_t* ks_slot,
                                                    float scale_log2, WaveState<D>& st) {
     const int nq = (npg + 1) / 2;
-    PageRaw a0, a1, b0, b1;
+    PageRaw buf[DEPTH][2];
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d)
+        load_pair_t<D, BITS>(base, hv, H, kv, cb, npg, d, nq, ctx, lane, buf[d][0], buf[d][1]);
     int q = 0;
-    load_pair_t<D, BITS>(base, hv, H, kv, cb, npg, 0, nq, ctx, lane, a0, a1);
-    while (true) {
-        load_pair_t<D, BITS>(base, hv, H, kv, cb, npg, q + 1, nq, ctx, lane, b0, b1);
-        process_pair<D, BITS>(a0, a1, qf, ks_slot, lane, scale_log2, st);
-        if (++q >= nq) break;
-        load_pair_t<D, BITS>(base, hv, H, kv, cb, npg, q + 1, nq, ctx, lane, a0, a1);
-        process_pair<D, BITS>(b0, b1, qf, ks_slot, lane, scale_log2, st);
-        if (++q >= nq) break;
+    bool done = false;
+    while (!done) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            if (!done) {
+                const int nxt = (d + DEPTH - 1) % DEPTH;
+                load_pair_t<D, BITS>(base, hv, H, kv, cb, npg, q + DEPTH - 1, nq, ctx, lane,
+                                     buf[nxt][0], buf[nxt][1]);
+                run_pair<D, BITS, HALF>(buf[d][0], buf[d][1], qf, ks_slot, lane, scale_log2, st);
+                done = ++q >= nq;
+            }
+        }
     }
 }
 
 // The same for a chunk whose pages may differ in width: handles from the block table, the
 // width-independent loads of load_page and per-page width branches.
-template <int D>
+template <int D, bool HALF>
 __device__ __forceinline__ void wave_chunk_mixed(const PageSrc& src, int kv, int cb, int npg,
                                                  int ctx, int lane, const uint32_t* qf,
                                                  uint32_t* ks_slot, float scale_log2,
@@ -457,15 +609,16 @@ __device__ __forceinline__ void wave_chunk_mixed(const PageSrc& src, int kv, int
     load_pair<D>(src, kv, cb, cb + npg, 0, nq, ctx, lane, a0, a1);
     while (true) {
         load_pair<D>(src, kv, cb, cb + npg, q + 1, nq, ctx, lane, b0, b1);
-        process_pair<D, 0>(a0, a1, qf, ks_slot, lane, scale_log2, st);
+        run_pair<D, 0, HALF>(a0, a1, qf, ks_slot, lane, scale_log2, st);
         if (++q >= nq) break;
         load_pair<D>(src, kv, cb, cb + npg, q + 1, nq, ctx, lane, a0, a1);
-        process_pair<D, 0>(b0, b1, qf, ks_slot, lane, scale_log2, st);
+        run_pair<D, 0, HALF>(b0, b1, qf, ks_slot, lane, scale_log2, st);
         if (++q >= nq) break;
     }
 }
 
-template <int D>
+// HALF: the group has at most 8 query heads (see process_pair_half)
+template <int D, bool HALF>
 __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t lds_ks[kWaves][2][64];
     __shared__ __attribute__((aligned(16))) float lds_o[kWaves][kMaxGroup][D];
@@ -481,6 +634,27 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps page math scalar
     const int grp = a.grp;
+    // The handles of this wave's chunk are requested before the context length arrives, on the
+    // guess that the split is full (every split but a sequence's last); the guess is checked
+    // once the length is known and the last split re-reads its own.
+    const int pbeg = split * a.pps;
+    const int cb_full = pbeg + (wave * a.pps) / kWaves;
+    const int npg_full = pbeg + ((wave + 1) * a.pps) / kWaves - cb_full;
+    const uint32_t* bt_row = a.bt + (size_t)s * a.max_pages;
+    uint32_t hv_full = 0;
+    if (npg_full > 0 && npg_full <= 64)
+        hv_full = bt_row[min(cb_full + min(lane, npg_full - 1), a.max_pages - 1)];
+    // q fragment: lane (h, G) holds q[h][G*D/4 .. +D/4) as fp16 pairs (zero for h >= grp)
+    const int h = lane & 15, G = lane >> 4;
+    const int hq = HALF ? (h & 7) : h;                 // the query head of this lane's column
+    uint32_t qf[D / 8];
+    {
+        const uint32_t* qp = reinterpret_cast<const uint32_t*>(
+            a.q + ((size_t)s * a.Hq + kv * grp + min(hq, grp - 1)) * D + G * (D / 4));
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) qf[i] = hq < grp ? qp[i] : 0u;
+    }
+
     const int ctx = ((const_i32_ptr)a.ctx_len)[s];
     const int npages = (ctx + kPage - 1) / kPage;
     const int nsplit = (npages + a.pps - 1) / a.pps;
@@ -491,18 +665,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
                 a.out[((size_t)s * a.Hq + kv * grp) * D + i] = 0.f;
         return;
     }
-    const int pbeg = split * a.pps;
     const int pend = min(pbeg + a.pps, npages);
-
-    // q fragment: lane (h, G) holds q[h][G*D/4 .. +D/4) as fp16 pairs (zero for h >= grp)
-    const int h = lane & 15, G = lane >> 4;
-    uint32_t qf[D / 8];
-    {
-        const uint32_t* qp = reinterpret_cast<const uint32_t*>(
-            a.q + ((size_t)s * a.Hq + kv * grp + min(h, grp - 1)) * D + G * (D / 4));
-#pragma unroll
-        for (int i = 0; i < D / 8; ++i) qf[i] = h < grp ? qp[i] : 0u;
-    }
 
     WaveState<D> st;
     st.m = -INFINITY;
@@ -524,28 +687,35 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
         uint32_t hv = 0;
         int tier0 = 0;
         if (npg <= 64) {
-            hv = a.bt[(size_t)s * a.max_pages + cb + min(lane, npg - 1)];
+            hv = pend - pbeg == a.pps ? hv_full : bt_row[cb + min(lane, npg - 1)];
             tier0 = (int)((uint32_t)__builtin_amdgcn_readfirstlane((int)hv) >> 30);
             uniform = __builtin_amdgcn_ballot_w64((int)(hv >> 30) != tier0) == 0;
         }
         if (uniform && tier0 == 0)
-            wave_chunk_uniform<D, 2>(a.pools.base[0], hv, a.H, kv, cb, npg, ctx, lane, qf, ks_slot,
+            wave_chunk_uniform<D, 2, 2, HALF>(a.pools.base[0], hv, a.H, kv, cb, npg, ctx, lane, qf, ks_slot,
                                      a.scale_log2, st);
         else if (uniform && tier0 == 1)
-            wave_chunk_uniform<D, 4>(a.pools.base[1], hv, a.H, kv, cb, npg, ctx, lane, qf, ks_slot,
+            wave_chunk_uniform<D, 4, 2, HALF>(a.pools.base[1], hv, a.H, kv, cb, npg, ctx, lane, qf, ks_slot,
                                      a.scale_log2, st);
         else if (uniform && tier0 == 2)
-            wave_chunk_uniform<D, 8>(a.pools.base[2], hv, a.H, kv, cb, npg, ctx, lane, qf, ks_slot,
+            wave_chunk_uniform<D, 8, 2, HALF>(a.pools.base[2], hv, a.H, kv, cb, npg, ctx, lane, qf, ks_slot,
                                      a.scale_log2, st);
         else {
             const PageSrc src = {a.pools.base[0], a.pools.base[1], a.pools.base[2],
-                                 a.bt + (size_t)s * a.max_pages, a.H};
-            wave_chunk_mixed<D>(src, kv, cb, npg, ctx, lane, qf, ks_slot, a.scale_log2, st);
+                                 bt_row, a.H};
+            wave_chunk_mixed<D, HALF>(src, kv, cb, npg, ctx, lane, qf, ks_slot, a.scale_log2, st);
         }
     }
 
     // ---- this wave's partial -> LDS; the V codes carried the 2^-24 of their subnormal form
-    const float lsum = rows_sum(st.l);
+    float lsum = rows_sum(st.l);
+    if constexpr (HALF) {                              // fold page-B columns 8..15 into 0..7
+        lsum += __shfl_xor(lsum, 8, 64);
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st.o[k][r] += __shfl_xor(st.o[k][r], 8, 64);
+    }
     if (h < grp) {
         if (G == 0) {
             lds_m[wave][h] = st.m;
@@ -721,10 +891,14 @@ hipError_t launch_decode_attn(const kv_geometry& g, PoolPtrs pools, const uint32
     off += ((groups * splits * a.grp * 2 * sizeof(float) + 255) / 256) * 256;
     a.ws_o = reinterpret_cast<float*>(ws + off);
     dim3 grid((unsigned)(splits * a.groups));
-    if (g.head_dim == 128)
-        hipLaunchKernelGGL(decode_attn_kernel<128>, grid, dim3(kWaves * 64), 0, stream, a);
-    else
-        hipLaunchKernelGGL(decode_attn_kernel<64>, grid, dim3(kWaves * 64), 0, stream, a);
+    const bool half = a.grp <= 8;
+    if (g.head_dim == 128) {
+        if (half) hipLaunchKernelGGL((decode_attn_kernel<128, true>), grid, dim3(kWaves * 64), 0, stream, a);
+        else hipLaunchKernelGGL((decode_attn_kernel<128, false>), grid, dim3(kWaves * 64), 0, stream, a);
+    } else {
+        if (half) hipLaunchKernelGGL((decode_attn_kernel<64, true>), grid, dim3(kWaves * 64), 0, stream, a);
+        else hipLaunchKernelGGL((decode_attn_kernel<64, false>), grid, dim3(kWaves * 64), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -8,16 +8,26 @@
 // quant_b is the cache's own quantizer (one scale per page and channel), so complete pages in
 // the ring get exactly the codes the cache stores.
 //
-// One workgroup per (sequence, KV head): ring keys -> LDS, temporary copies built in LDS, one
-// thread per (head, key) dot product, one wave per head for the log-sum-exp reductions. The
-// mean over all rows is taken by the last workgroup to finish (atomic ticket), in row order.
+// One workgroup per (sequence, KV head, width). The ring keys and the group's queries go to
+// LDS once (16-byte loads); the workgroup takes the reference logits, then turns the keys in
+// place into its width's temporary copy (one scale per (page group, channel), then one code per
+// element) and takes the copy's logits with one wave
+// per query head and one lane per key -- the keys sit in LDS rows padded to D + 1 floats, so the
+// 64 lanes of a wave read 64 different banks while the query element is a broadcast. One wave
+// per head then takes the log-sum-exp form of the divergence. Rows are stored with
+// device-coherent stores; the last workgroup to take the ticket averages every row, in row order,
+// from device-coherent loads (no cache flushes).
 #include "kvq_device.hpp"
 #include "kvq_launch.hpp"
+
+#include <mutex>
 
 namespace kvq {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWavesC = kThreads / 64;
+constexpr int kMaxRing = 128;   // largest ring the geometry check accepts
 
 struct CanaryArgs {
     const uint16_t* ring;
@@ -31,26 +41,35 @@ struct CanaryArgs {
     float scale;
 };
 
-// dot product of a query row and a key row held in LDS (fixed order)
+// logits of every query head of the group against n keys held in LDS rows of stride D + 1
 template <int D>
-__device__ inline float row_dot(const float* qrow, const float* krow) {
-    float acc = 0.f;
-#pragma unroll 8
-    for (int c = 0; c < D; ++c) acc = fmaf(qrow[c], krow[c], acc);
-    return acc;
+__device__ __forceinline__ void group_logits(const float* qs, const float* keys, int grp, int n,
+                                             int R, float scale, int wave, int lane, float* out) {
+    for (int hh = wave; hh < grp; hh += kWavesC) {
+        const float* qrow = qs + hh * D;
+        for (int k = lane; k < n; k += 64) {
+            const float* krow = keys + k * (D + 1);
+            float acc = 0.f;
+#pragma unroll 16
+            for (int c = 0; c < D; ++c) acc = fmaf(qrow[c], krow[c], acc);
+            out[hh * R + k] = scale * acc;
+        }
+    }
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void canary_kernel(CanaryArgs a) {
     extern __shared__ float smem[];
     const int R = a.R;
-    float* kref = smem;                      // [R][D]
-    float* kb = kref + R * D;                // [R][D] temporary copy
-    float* qh = kb + R * D;                  // [grp][D]
-    float* lref = qh + kMaxGroup * D;        // [grp][R]
-    float* lb = lref + kMaxGroup * R;        // [grp][R]
+    float* kref = smem;                          // [R][D + 1]; later the copy, in place
+    float* qs = kref + R * (D + 1);              // [grp][D]
+    float* sc = qs + kMaxGroup * D;              // [R / P + 1][D] scales of the copy
+    float* lref = sc + (R / kPage + 1) * D;      // [grp][R]
+    float* lb = lref + kMaxGroup * R;            // [grp][R]
     __shared__ int last;
 
+    const int ti = blockIdx.y;                   // width 2, 4, 8
+    const int bits = 2 << ti;
     const int s = blockIdx.x / a.H, kv = blockIdx.x % a.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int grp = a.grp;
@@ -58,86 +77,108 @@ __global__ __launch_bounds__(kThreads) void canary_kernel(CanaryArgs a) {
     const int n = min(N, R);
     const int first = N - n;
 
-    for (int i = tid; i < n * D; i += kThreads) {
-        const int k = i / D, c = i - k * D;
-        kref[i] = f16_val(a.ring[(((size_t)s * R + (first + k) % R) * a.H + kv) * D + c]);
+    // ---- ring keys (positions first .. N-1, slot p % R) and the group's queries, 8 fp16 a load
+    for (int i = tid; i < n * (D / 8); i += kThreads) {
+        const int k = i / (D / 8), c8 = (i - k * (D / 8)) * 8;
+        const uint4 v = *reinterpret_cast<const uint4*>(
+            a.ring + (((size_t)s * R + (first + k) % R) * a.H + kv) * D + c8);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        float* dst = kref + k * (D + 1) + c8;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            dst[2 * j] = f16_val((uint16_t)(w[j] & 0xffffu));
+            dst[2 * j + 1] = f16_val((uint16_t)(w[j] >> 16));
+        }
     }
-    for (int i = tid; i < grp * D; i += kThreads)
-        qh[i] = f16_val(a.q[((size_t)s * a.Hq + kv * grp) * D + i]);
+    for (int i = tid; i < grp * (D / 8); i += kThreads) {
+        const uint4 v = *reinterpret_cast<const uint4*>(a.q + ((size_t)s * a.Hq + kv * grp) * D + 8 * i);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            qs[8 * i + 2 * j] = f16_val((uint16_t)(w[j] & 0xffffu));
+            qs[8 * i + 2 * j + 1] = f16_val((uint16_t)(w[j] >> 16));
+        }
+    }
     __syncthreads();
-    for (int i = tid; i < grp * n; i += kThreads) {
-        const int hh = i / n, k = i - hh * n;
-        lref[hh * R + k] = a.scale * row_dot<D>(qh + hh * D, kref + k * D);
-    }
 
+    // ---- the copy's scales: one per (page group, channel) over its ring-resident keys
     const int pfirst = first / kPage;
     const int npg = n > 0 ? (N - 1) / kPage - pfirst + 1 : 0;
-    for (int ti = 0; ti < 3; ++ti) {
-        const int bits = 2 << ti;
-        // temporary b-bit copy: one scale per (page group, channel) over its ring-resident keys
-        for (int i = tid; i < npg * D; i += kThreads) {
-            const int pg = i / D, c = i - pg * D;
-            const int k0 = max(first, (pfirst + pg) * kPage) - first;
-            const int k1 = min(N, (pfirst + pg + 1) * kPage) - first;
-            float amax = 0.f;
-            for (int k = k0; k < k1; ++k) amax = fmaxf(amax, fabsf(kref[k * D + c]));
-            const uint16_t sb = group_scale(amax, bits);
-            const float sf = f16_val(sb);
-            for (int k = k0; k < k1; ++k)
-                kb[k * D + c] = sb ? (float)quant_code(kref[k * D + c], sf, bits) * sf : 0.f;
+    for (int i = tid; i < npg * D; i += kThreads) {
+        const int pg = i / D, c = i - pg * D;
+        const int k0 = max(first, (pfirst + pg) * kPage) - first;
+        const int k1 = min(N, (pfirst + pg + 1) * kPage) - first;
+        float amax = 0.f;
+        for (int k = k0; k < k1; ++k) amax = fmaxf(amax, fabsf(kref[k * (D + 1) + c]));
+        sc[pg * D + c] = f16_val(group_scale(amax, bits));
+    }
+    // reference logits meanwhile (they only read the keys and queries)
+    group_logits<D>(qs, kref, grp, n, R, a.scale, wave, lane, lref);
+    __syncthreads();
+    // ---- the copy itself, in place of the keys: code * scale, one element a thread and step
+    for (int i = tid; i < n * D; i += kThreads) {
+        const int k = i / D, c = i - k * D;
+        const float sf = sc[((first + k) / kPage - pfirst) * D + c];
+        const float x = kref[k * (D + 1) + c];
+        kref[k * (D + 1) + c] = sf != 0.f ? (float)quant_code(x, sf, bits) * sf : 0.f;
+    }
+    __syncthreads();
+    group_logits<D>(qs, kref, grp, n, R, a.scale, wave, lane, lb);
+    __syncthreads();
+
+    // ---- KL(P_ref || P_b) = sum_k P_k (l_k - m_k) - LSE(l) + LSE(m), one wave per head
+    for (int hh = wave; hh < grp; hh += kWavesC) {
+        float ml = -INFINITY, mm = -INFINITY;
+        for (int k = lane; k < n; k += 64) {
+            ml = fmaxf(ml, lref[hh * R + k]);
+            mm = fmaxf(mm, lb[hh * R + k]);
         }
-        __syncthreads();
-        for (int i = tid; i < grp * n; i += kThreads) {
-            const int hh = i / n, k = i - hh * n;
-            lb[hh * R + k] = a.scale * row_dot<D>(qh + hh * D, kb + k * D);
+        ml = wave_max(ml);
+        mm = wave_max(mm);
+        float sl = 0.f, sm = 0.f;
+        for (int k = lane; k < n; k += 64) {
+            sl += expf(lref[hh * R + k] - ml);
+            sm += expf(lb[hh * R + k] - mm);
         }
-        __syncthreads();
-        // KL(P_ref || P_b) = sum_k P_k (l_k - m_k) - LSE(l) + LSE(m), one wave per head
-        for (int hh = wave; hh < grp; hh += kThreads / 64) {
-            float ml = -INFINITY, mm = -INFINITY;
-            for (int k = lane; k < n; k += 64) {
-                ml = fmaxf(ml, lref[hh * R + k]);
-                mm = fmaxf(mm, lb[hh * R + k]);
-            }
-            ml = wave_max(ml);
-            mm = wave_max(mm);
-            float sl = 0.f, sm = 0.f;
-            for (int k = lane; k < n; k += 64) {
-                sl += expf(lref[hh * R + k] - ml);
-                sm += expf(lb[hh * R + k] - mm);
-            }
-            sl = wave_sum(sl);
-            sm = wave_sum(sm);
-            const float lse_l = ml + logf(sl), lse_m = mm + logf(sm);
-            float acc = 0.f;
-            for (int k = lane; k < n; k += 64)
-                acc += expf(lref[hh * R + k] - lse_l) * (lref[hh * R + k] - lb[hh * R + k]);
-            acc = wave_sum(acc);
-            const float kl = n > 0 ? fmaxf(acc - lse_l + lse_m, 0.f) : 0.f;
-            if (lane == 0) {
-                const size_t row = ((size_t)s * a.Hq + kv * grp + hh) * 3 + ti;
-                a.ws_rows[row] = kl;
-                if (a.kl_rows) a.kl_rows[row] = kl;
-            }
+        sl = wave_sum(sl);
+        sm = wave_sum(sm);
+        const float lse_l = ml + logf(sl), lse_m = mm + logf(sm);
+        float acc = 0.f;
+        for (int k = lane; k < n; k += 64)
+            acc += expf(lref[hh * R + k] - lse_l) * (lref[hh * R + k] - lb[hh * R + k]);
+        acc = wave_sum(acc);
+        const float kl = n > 0 ? fmaxf(acc - lse_l + lse_m, 0.f) : 0.f;
+        if (lane == 0) {
+            const size_t row = ((size_t)s * a.Hq + kv * grp + hh) * 3 + ti;
+            __hip_atomic_store(a.ws_rows + row, kl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (a.kl_rows) a.kl_rows[row] = kl;
         }
-        __syncthreads();
     }
 
-    // the last workgroup averages all rows, in row order
-    __threadfence();
+    // ---- the last workgroup averages all rows, in row order. Its coherent stores complete
+    // before the ticket; the winner reads the rows with coherent loads issued after it.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) last = atomicAdd(a.counter, 1u) == (unsigned)(gridDim.x - 1);
+    const unsigned total = gridDim.x * gridDim.y;
+    if (tid == 0)
+        last = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               total - 1;
     __syncthreads();
     if (!last) return;
-    __threadfence();
+    constexpr int kSc1 = 16;                                    // device-coherent load
+    const __amdgpu_buffer_rsrc_t rows_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(a.ws_rows, (short)0, 0x7fffffff, 0x00020000);
     if (wave < 3) {
         const int rows = a.batch * a.Hq;
         float acc = 0.f;
-        for (int r = lane; r < rows; r += 64) acc += a.ws_rows[(size_t)r * 3 + wave];
+        for (int r = lane; r < rows; r += 64)
+            acc += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 rows_rsrc, (r * 3 + wave) * 4, 0, kSc1));
         acc = wave_sum(acc);
         if (lane == 0) a.kl_out[wave] = acc / (float)rows;
     }
-    if (tid == 0) *a.counter = 0u;
+    if (tid == 0)
+        __hip_atomic_store(a.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -164,12 +205,23 @@ hipError_t launch_canary(const kv_geometry& g, const uint16_t* ring, const int32
     a.batch = batch;
     a.scale = softmax_scale;
     const int D = g.head_dim;
-    const size_t lds = sizeof(float) * (2 * (size_t)a.R * D + kMaxGroup * D + 2 * kMaxGroup * (size_t)a.R);
-    dim3 grid((unsigned)(batch * g.num_kv_heads));
-    // the LDS footprint exceeds the 64 KiB default for rings of 64 keys at D = 128
-    const void* fn = D == 128 ? reinterpret_cast<const void*>(&canary_kernel<128>)
-                              : reinterpret_cast<const void*>(&canary_kernel<64>);
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const size_t lds = sizeof(float) * ((size_t)a.R * (D + 1) + kMaxGroup * D +
+                                        ((size_t)a.R / kPage + 1) * D + 2 * kMaxGroup * (size_t)a.R);
+    dim3 grid((unsigned)(batch * g.num_kv_heads), 3u);
+    // the LDS footprint exceeds the 64 KiB default for rings of 64 keys at D = 128: raise the
+    // limit to the largest footprint any supported ring needs, once per process and kernel (so
+    // that launches stay plain stream work, e.g. under graph capture)
+    static std::once_flag once[2];
+    hipError_t e = hipSuccess;
+    const int which = D == 128 ? 0 : 1;
+    std::call_once(once[which], [&] {
+        const void* fn = D == 128 ? reinterpret_cast<const void*>(&canary_kernel<128>)
+                                  : reinterpret_cast<const void*>(&canary_kernel<64>);
+        const size_t max_lds = sizeof(float) * ((size_t)kMaxRing * (D + 1) + kMaxGroup * D +
+                                                ((size_t)kMaxRing / kPage + 1) * D +
+                                                2 * kMaxGroup * (size_t)kMaxRing);
+        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_lds);
+    });
     if (e != hipSuccess) return e;
     if (D == 128)
         hipLaunchKernelGGL(canary_kernel<128>, grid, dim3(kThreads), lds, stream, a);
