@@ -156,7 +156,27 @@ kv_status kv_decode_attn(const kv_geometry* g, const kv_layer_pools* pools, cons
                          float softmax_scale, float* out, void* workspace,
                          size_t workspace_bytes, int pages_per_split, void* stream);
 
-/* ---------------------------------------------------------------- canary
+/* ---------------------------------------------------------------- fused decode step
+ * The write of kv_quant_write and the attention of kv_decode_attn in one launch (one per layer
+ * and step): for each sequence s, n_new tokens are written at positions pos[s] .. pos[s]+n_new-1
+ * exactly as kv_quant_write writes them (same bytes, same ring), and the attention then runs
+ * over ctx_len = pos[s] + n_new tokens exactly as kv_decode_attn runs it (same outputs). The
+ * workgroup whose split holds a touched page writes it before it reads it; no other workgroup
+ * reads that page.
+ *   n_new            0 .. page_size (at most two pages per sequence); 0 = attention over pos
+ *   pos, k_new, v_new, ring   as for kv_quant_write (k_new, v_new, ring 16-byte aligned)
+ *   max_ctx_len      host upper bound on pos[s] + n_new
+ *   q, softmax_scale, out, workspace, workspace_bytes, pages_per_split   as for kv_decode_attn
+ *                    (the workspace is sized by kv_decode_workspace_bytes(g, batch, max_ctx_len,
+ *                    pages_per_split))
+ * Errors: as for the two calls it joins; n_new outside 0..page_size is KV_EINVAL. */
+kv_status kv_decode_step(const kv_geometry* g, const kv_layer_pools* pools, const uint32_t* bt,
+                         const int32_t* pos, int batch, int n_new, const uint16_t* k_new,
+                         const uint16_t* v_new, uint16_t* ring, int max_ctx_len, const uint16_t* q,
+                         float softmax_scale, float* out, void* workspace,
+                         size_t workspace_bytes, int pages_per_split, void* stream);
+
+/* ---------------------------------------------------------------- canary/* ---------------------------------------------------------------- canary
  * [EchoKV] "Show the math": delta_b = KL(softmax(Q K_ref^T) || softmax(Q quant_b(K_ref)^T)),
  * summed over keys, averaged over queries; one number per b in {2, 4, 8}. K_ref is the ring:
  * for each sequence the n = min(seq_len[s], R) newest keys (positions seq_len-n .. seq_len-1).

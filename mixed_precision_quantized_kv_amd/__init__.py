@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
             "kv_decode_pages_per_split": (i32, [G, i32, i32]),
             "kv_decode_attn": (i32, [G, ctypes.POINTER(LayerPools), P, P, i32, i32, P,
                                      ctypes.c_float, P, P, sz, i32, P]),
+            "kv_decode_step": (i32, [G, ctypes.POINTER(LayerPools), P, P, i32, i32, P, P, P, i32,
+                                     P, ctypes.c_float, P, P, sz, i32, P]),
             "kv_canary_workspace_bytes": (sz, [G, i32]),
             "kv_canary_kl": (i32, [G, P, P, i32, P, ctypes.c_float, P, P, P, sz, P]),
         }
@@ -232,6 +234,17 @@ def kv_decode_attn(g: Geometry, pools: LayerPools, bt, ctx_len, batch: int, max_
                                 batch, max_ctx_len, _addr(q), softmax_scale, _addr(out),
                                 _addr(workspace), workspace_bytes, pages_per_split,
                                 _stream(stream)))
+
+
+def kv_decode_step(g: Geometry, pools: LayerPools, bt, pos, batch: int, n_new: int, k_new, v_new,
+                   ring, max_ctx_len: int, q, softmax_scale: float, out, workspace,
+                   workspace_bytes=None, pages_per_split: int = 0, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().kv_decode_step(ctypes.byref(g), ctypes.byref(pools), _addr(bt), _addr(pos), batch,
+                                n_new, _addr(k_new), _addr(v_new), _addr(ring), max_ctx_len,
+                                _addr(q), softmax_scale, _addr(out), _addr(workspace),
+                                workspace_bytes, pages_per_split, _stream(stream)))
 
 
 def kv_canary_kl(g: Geometry, ring, seq_len, batch: int, q, softmax_scale: float, kl_out,

@@ -26,6 +26,7 @@
 // keeps all splits of a group on one XCD when groups % 8 == 0.
 #include "kvq_device.hpp"
 #include "kvq_launch.hpp"
+#include "kvq_write_dev.hpp"
 
 namespace kvq {
 namespace {
@@ -61,6 +62,10 @@ struct AttnArgs {
     int splits;
     int pps;              // pages per split
     float scale_log2;     // softmax_scale * log2(e)
+    // fused decode step only: the write of n_new tokens at pos, done before the attention
+    const int32_t* pos;
+    int n_new;
+    WriteArgs wr;
 };
 
 // raw bytes of one page, as this lane needs them
@@ -617,8 +622,12 @@ __device__ __forceinline__ void wave_chunk_mixed(const PageSrc& src, int kv, int
     }
 }
 
-// HALF: the group has at most 8 query heads (see process_pair_half)
-template <int D, bool HALF>
+// HALF: the group has at most 8 query heads (see process_pair_half). FUSED: the kernel first
+// writes the step's new tokens (at most 16 per sequence, so at most two pages): the workgroup
+// whose split holds a touched page quantizes it (256 threads a page) and, for the first page,
+// updates the ring, then makes its writes visible to its own loads and attends over
+// pos + n_new tokens. No other workgroup reads those pages, so one launch does both steps.
+template <int D, bool HALF, bool FUSED>
 __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t lds_ks[kWaves][2][64];
     __shared__ __attribute__((aligned(16))) float lds_o[kWaves][kMaxGroup][D];
@@ -655,7 +664,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
         for (int i = 0; i < D / 8; ++i) qf[i] = hq < grp ? qp[i] : 0u;
     }
 
-    const int ctx = ((const_i32_ptr)a.ctx_len)[s];
+    const int ctx = FUSED ? ((const_i32_ptr)a.pos)[s] + a.n_new : ((const_i32_ptr)a.ctx_len)[s];
     const int npages = (ctx + kPage - 1) / kPage;
     const int nsplit = (npages + a.pps - 1) / a.pps;
 
@@ -666,6 +675,28 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
         return;
     }
     const int pend = min(pbeg + a.pps, npages);
+
+    if constexpr (FUSED) {
+        __shared__ float chan_max[2][4][D];
+        const int p0 = ctx - a.n_new;
+        const int first_page = p0 / kPage, last_page = (ctx - 1) / kPage;
+        const bool mine0 = first_page >= pbeg && first_page < pend;
+        const bool mine1 = last_page != first_page && last_page >= pbeg && last_page < pend;
+        if (a.n_new > 0 && (mine0 || mine1)) {          // uniform over the workgroup
+            const int half = tid >> 8;                   // threads 0..255: page 0, 256..511: page 1
+            write_page<D>(a.wr, s, kv, p0, half, tid & 255, half == 0 ? mine0 : mine1,
+                          chan_max[half]);
+            if (mine0) {
+                __syncthreads();                         // the first page's ring reads are done
+                write_ring<D>(a.wr, s, kv, p0, tid, kWaves * 64);
+            }
+            // the writes reach memory before any wave of this workgroup reads the pages, and
+            // this compute unit's vector cache forgets what the write phase loaded
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+    }
 
     WaveState<D> st;
     st.m = -INFINITY;
@@ -865,14 +896,14 @@ size_t decode_workspace_bytes(const kv_geometry& g, int batch, int splits) {
     return bytes;
 }
 
-hipError_t launch_decode_attn(const kv_geometry& g, PoolPtrs pools, const uint32_t* bt,
-                              const int32_t* ctx_len, int batch, int splits, int pages_per_split,
-                              const uint16_t* q, float softmax_scale, float* out,
-                              void* workspace, hipStream_t stream) {
-    AttnArgs a;
+namespace {
+
+AttnArgs attn_args(const kv_geometry& g, PoolPtrs pools, const uint32_t* bt, int batch, int splits,
+                   int pages_per_split, const uint16_t* q, float softmax_scale, float* out,
+                   void* workspace) {
+    AttnArgs a = {};
     a.pools = pools;
     a.bt = bt;
-    a.ctx_len = ctx_len;
     a.q = q;
     a.out = out;
     a.max_pages = g.max_pages_per_seq;
@@ -890,16 +921,55 @@ hipError_t launch_decode_attn(const kv_geometry& g, PoolPtrs pools, const uint32
     a.ws_ml = reinterpret_cast<float*>(ws + off);
     off += ((groups * splits * a.grp * 2 * sizeof(float) + 255) / 256) * 256;
     a.ws_o = reinterpret_cast<float*>(ws + off);
+    return a;
+}
+
+template <bool FUSED>
+hipError_t launch(const kv_geometry& g, const AttnArgs& a, int splits, hipStream_t stream) {
     dim3 grid((unsigned)(splits * a.groups));
     const bool half = a.grp <= 8;
     if (g.head_dim == 128) {
-        if (half) hipLaunchKernelGGL((decode_attn_kernel<128, true>), grid, dim3(kWaves * 64), 0, stream, a);
-        else hipLaunchKernelGGL((decode_attn_kernel<128, false>), grid, dim3(kWaves * 64), 0, stream, a);
+        if (half) hipLaunchKernelGGL((decode_attn_kernel<128, true, FUSED>), grid, dim3(kWaves * 64), 0, stream, a);
+        else hipLaunchKernelGGL((decode_attn_kernel<128, false, FUSED>), grid, dim3(kWaves * 64), 0, stream, a);
     } else {
-        if (half) hipLaunchKernelGGL((decode_attn_kernel<64, true>), grid, dim3(kWaves * 64), 0, stream, a);
-        else hipLaunchKernelGGL((decode_attn_kernel<64, false>), grid, dim3(kWaves * 64), 0, stream, a);
+        if (half) hipLaunchKernelGGL((decode_attn_kernel<64, true, FUSED>), grid, dim3(kWaves * 64), 0, stream, a);
+        else hipLaunchKernelGGL((decode_attn_kernel<64, false, FUSED>), grid, dim3(kWaves * 64), 0, stream, a);
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_attn(const kv_geometry& g, PoolPtrs pools, const uint32_t* bt,
+                              const int32_t* ctx_len, int batch, int splits, int pages_per_split,
+                              const uint16_t* q, float softmax_scale, float* out,
+                              void* workspace, hipStream_t stream) {
+    AttnArgs a = attn_args(g, pools, bt, batch, splits, pages_per_split, q, softmax_scale, out,
+                           workspace);
+    a.ctx_len = ctx_len;
+    return launch<false>(g, a, splits, stream);
+}
+
+hipError_t launch_decode_step(const kv_geometry& g, PoolPtrs pools, const uint32_t* bt,
+                              const int32_t* pos, int batch, int n_new, const uint16_t* k_new,
+                              const uint16_t* v_new, uint16_t* ring, int splits,
+                              int pages_per_split, const uint16_t* q, float softmax_scale,
+                              float* out, void* workspace, hipStream_t stream) {
+    AttnArgs a = attn_args(g, pools, bt, batch, splits, pages_per_split, q, softmax_scale, out,
+                           workspace);
+    a.pos = pos;
+    a.n_new = n_new;
+    a.wr.pools = pools;
+    a.wr.bt = bt;
+    a.wr.pos = pos;
+    a.wr.k_new = k_new;
+    a.wr.v_new = v_new;
+    a.wr.ring = ring;
+    a.wr.max_pages = g.max_pages_per_seq;
+    a.wr.n_new = n_new;
+    a.wr.H = g.num_kv_heads;
+    a.wr.R = g.ring_size;
+    return launch<true>(g, a, splits, stream);
 }
 
 }  // namespace kvq

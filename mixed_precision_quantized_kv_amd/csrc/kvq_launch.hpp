@@ -23,6 +23,13 @@ hipError_t launch_decode_attn(const kv_geometry& g, PoolPtrs pools, const uint32
                               const uint16_t* q, float softmax_scale, float* out,
                               void* workspace, hipStream_t stream);
 
+// write of n_new <= 16 tokens per sequence fused into the decode attention over pos + n_new
+hipError_t launch_decode_step(const kv_geometry& g, PoolPtrs pools, const uint32_t* bt,
+                              const int32_t* pos, int batch, int n_new, const uint16_t* k_new,
+                              const uint16_t* v_new, uint16_t* ring, int splits,
+                              int pages_per_split, const uint16_t* q, float softmax_scale,
+                              float* out, void* workspace, hipStream_t stream);
+
 // workspace layout of the decode attention (bytes)
 size_t decode_workspace_bytes(const kv_geometry& g, int batch, int splits);
 

@@ -1,0 +1,270 @@
+// kvq_write_dev.hpp -- quantize-on-write of one page by 256 threads, shared by the write kernel
+// and the fused decode-step kernel.
+//
+// EchoKV, "How EchoKV works": the step's key enters the per-layer FP16 ring before it is
+// quantized into the paged cache. Behavior-Guided KV-Cache Quantization, "K/V Role-Aware
+// Low-Bit Quantization": keys get one scale per channel (over the page's tokens), values one
+// scale per token (over its channels); "Online inference": pack and store.
+//
+// Thread (t, g) = (tid / 16, tid % 16) owns token slot t of the page and channels
+// [g*D/16, (g+1)*D/16): every input element is fetched by exactly one 8- or 16-byte load,
+// issued up front, so the threads wait on memory once. Channel maxima over the page's tokens
+// reduce across the four token lanes of a wave (shuffles) and the four waves (LDS); token maxima
+// over D reduce across the 16 lanes of a token (shuffles). Codes are packed in registers; words
+// shared by several threads are OR-reduced with shuffles.
+#pragma once
+
+#include "kvq_device.hpp"
+
+namespace kvq {
+
+struct WriteArgs {
+    PoolPtrs pools;
+    const uint32_t* bt;
+    const int32_t* pos;
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    uint16_t* ring;
+    int max_pages;
+    int n_new;
+    int H;
+    int R;
+};
+
+// CPT consecutive fp16 values (CPT = 4 or 8, 8- or 16-byte aligned) as floats
+template <int CPT>
+__device__ __forceinline__ void load_f16(const uint16_t* p, float* out) {
+    if constexpr (CPT == 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(p);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = f16_val((uint16_t)(w[i] & 0xffffu));
+            out[2 * i + 1] = f16_val((uint16_t)(w[i] >> 16));
+        }
+    } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        const uint32_t w[2] = {v.x, v.y};
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            out[2 * i] = f16_val((uint16_t)(w[i] & 0xffffu));
+            out[2 * i + 1] = f16_val((uint16_t)(w[i] >> 16));
+        }
+    }
+}
+
+// pool base of a tier, by arithmetic (a select chain would become a lookup table in scratch)
+__device__ __forceinline__ uint8_t* pool_base(const PoolPtrs& pools, int tier) {
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(pools.base[0]);
+    return reinterpret_cast<uint8_t*>(
+        b0 + (uintptr_t)(tier == 1) * (reinterpret_cast<uintptr_t>(pools.base[1]) - b0) +
+        (uintptr_t)(tier == 2) * (reinterpret_cast<uintptr_t>(pools.base[2]) - b0));
+}
+
+// Write page p0/P + j of sequence s, KV head kv, for the call's new tokens [p0, p0 + n_new):
+// the page's K scales and the codes of all its present tokens from their FP16 originals (ring
+// for positions < p0, k_new after), the new tokens' V codes and scales. `tid` is 0..255 within
+// the 256 threads doing this page; `active` false (or a page past the call) writes nothing.
+// Every thread of the workgroup must call this (it holds one workgroup barrier).
+template <int D>
+__device__ __forceinline__ void write_page(const WriteArgs& a, int s, int kv, int p0, int j, int tid,
+                                           bool active, float (*chan_max)[D]) {
+    constexpr int P = kPage;
+    constexpr int CPT = D / 16;                 // channels per thread
+    const int t = tid >> 4, g = tid & 15, c0 = g * CPT;
+    const int wave = tid >> 6;
+    const int end = p0 + a.n_new;
+    const int page = p0 / P + j;
+    const int lo = page * P;
+    active = active && lo < end;                // uniform over the 256 threads
+    const int nk = min(lo + P, end) - lo;       // present tokens after the write
+    const int told = max(0, p0 - lo);           // tokens cached before this call
+    const int p = lo + t;
+    const bool present = active && t < nk;
+    const bool is_new = present && t >= told;
+
+    // ---- gather first (it depends only on pos): this thread's keys (ring for positions < pos,
+    // input after) and new values; the block-table lookup and old V words follow
+    float kf[CPT], vf[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) kf[i] = vf[i] = 0.f;
+    uint16_t* ring_s = a.ring + (size_t)s * a.R * a.H * D;
+    if (present) {
+        const uint16_t* src = p < p0
+            ? ring_s + ((size_t)(p % a.R) * a.H + kv) * D + c0
+            : a.k_new + (((size_t)s * a.n_new + (p - p0)) * a.H + kv) * D + c0;
+        load_f16<CPT>(src, kf);
+    }
+    if (is_new)
+        load_f16<CPT>(a.v_new + (((size_t)s * a.n_new + (p - p0)) * a.H + kv) * D + c0, vf);
+
+    uint32_t handle = 0;
+    if (active) handle = a.bt[(size_t)s * a.max_pages + page];
+    const int tier = (int)(handle >> 30);
+    const int bits = bits_of_tier(tier);
+    const Section L = section_layout(D, bits);
+    uint8_t* sec = pool_base(a.pools, tier) + ((size_t)(handle & 0x3fffffffu) * a.H + kv) * L.bytes;
+    const uint32_t qoff = 1u << (bits - 1);
+    const uint32_t fmask = (1u << bits) - 1u;
+
+    // ---- V code words this lane will store. V codes are grouped by token quads: code index
+    // ((t/4)*D + c)*4 + t%4, 32/b codes per word, so a word holds cw = 8/b channels of one quad.
+    // The quad of token t is handled by the four lanes t%4 = 0..3 of one wave; lane r stores the
+    // words w of its channel group with w % 4 == r. A quad seen for the first time is written
+    // whole (its empty slots get the zero code); a quad that already holds tokens is read,
+    // merged with the new fields and written back (its other fields are kept).
+    const int cw = 8 / bits;                    // channels per V word
+    const int nwv = CPT / cw;                   // V words per (quad, channel group): 1..8
+    const int quad = t >> 2, r = t & 3;
+    const bool quad_old = 4 * quad < told;      // the quad holds tokens cached before the call
+    const bool quad_new = 4 * quad + 3 >= told && 4 * quad < nk;
+    const bool quad_store = active && (quad_new || !quad_old);   // entirely-old quads: untouched
+    uint32_t* vwords = reinterpret_cast<uint32_t*>(sec + L.vcode_off);
+    const int wbase = ((quad * D + c0) * 4) / (32 / bits);  // first V word of this (quad, group)
+    uint32_t vold[2] = {0u, 0u};                // at most 8 words / 4 lanes
+    if (quad_store && quad_old) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int w = r + 4 * i;
+            if (w < nwv) vold[i] = vwords[wbase + w];
+        }
+    }
+
+    // ---- K: channel maxima over the present tokens (empty slots hold zeros)
+    float m[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        float x = fabsf(kf[i]);
+        x = fmaxf(x, __shfl_xor(x, 16, 64));
+        m[i] = fmaxf(x, __shfl_xor(x, 32, 64));
+    }
+    if ((tid & 63) < 16) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) chan_max[wave][c0 + i] = m[i];
+    }
+    __syncthreads();
+    if (!active) return;
+    uint16_t ks[CPT];
+    uint32_t ku[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const float amax = fmaxf(fmaxf(chan_max[0][c0 + i], chan_max[1][c0 + i]),
+                                 fmaxf(chan_max[2][c0 + i], chan_max[3][c0 + i]));
+        ks[i] = group_scale(amax, bits);
+        ku[i] = (present && ks[i]) ? (uint32_t)(quant_code(kf[i], f16_val(ks[i]), bits) + (int)qoff)
+                                   : qoff;
+    }
+
+    // ---- K codes: row t holds D codes, 32/b per word; this thread's CPT codes fill CPT*b bits
+    {
+        uint32_t* row = reinterpret_cast<uint32_t*>(sec + (size_t)t * (D * bits / 8));
+        const int per_word = 32 / bits;
+        if (CPT * bits >= 32) {                 // whole words: INT4/INT8 (D=128), INT8 (D=64)
+            const int nw = CPT * bits / 32;
+            for (int w = 0; w < nw; ++w) {
+                uint32_t word = 0;
+#pragma unroll
+                for (int i = 0; i < CPT; ++i)
+                    if (i / per_word == w) word |= ku[i] << field_bit(i % per_word, bits);
+                row[c0 / per_word + w] = word;
+            }
+        } else {                                // 2 or 4 neighbouring threads share a word
+            const int share = 32 / (CPT * bits);
+            const int k0 = (g % share) * CPT;
+            uint32_t word = 0;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) word |= ku[i] << field_bit(k0 + i, bits);
+            word |= __shfl_xor(word, 1, 64);
+            if (share == 4) word |= __shfl_xor(word, 2, 64);
+            if (g % share == 0) row[c0 / per_word] = word;
+        }
+    }
+    // K scales (one slot row writes them)
+    if (t == 0) {
+        uint16_t* dst = reinterpret_cast<uint16_t*>(sec + L.kscale_off) + c0;
+        if constexpr (CPT == 8) {
+            uint4 v;
+            v.x = ks[0] | ((uint32_t)ks[1] << 16); v.y = ks[2] | ((uint32_t)ks[3] << 16);
+            v.z = ks[4] | ((uint32_t)ks[5] << 16); v.w = ks[6] | ((uint32_t)ks[7] << 16);
+            *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+            uint2 v;
+            v.x = ks[0] | ((uint32_t)ks[1] << 16); v.y = ks[2] | ((uint32_t)ks[3] << 16);
+            *reinterpret_cast<uint2*>(dst) = v;
+        }
+    }
+
+    // ---- V: one scale per new token over its D channels (the token's 16 lanes)
+    float vm = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) vm = fmaxf(vm, fabsf(vf[i]));
+#pragma unroll
+    for (int msk = 1; msk < 16; msk <<= 1) vm = fmaxf(vm, __shfl_xor(vm, msk, 64));
+    const uint16_t vs = is_new ? group_scale(vm, bits) : 0;
+    const float vsf = f16_val(vs);
+    // this token's fields (new tokens: their codes; empty slots: the zero code) and the mask of
+    // fields the call writes
+    uint32_t part[8], mask[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) part[w] = mask[w] = 0u;
+    if (t >= told) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const uint32_t u = (is_new && vs) ? (uint32_t)(quant_code(vf[i], vsf, bits) + (int)qoff)
+                                              : qoff;
+            const int w = i / cw;
+            const int fb = field_bit((i % cw) * 4 + r, bits);
+            part[w] |= u << fb;
+            mask[w] |= fmask << fb;
+        }
+    }
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        if (w < nwv) {
+            part[w] |= __shfl_xor(part[w], 16, 64);
+            part[w] |= __shfl_xor(part[w], 32, 64);
+            mask[w] |= __shfl_xor(mask[w], 16, 64);
+            mask[w] |= __shfl_xor(mask[w], 32, 64);
+        }
+    }
+    if (quad_store) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int w = r + 4 * i;
+            if (w < nwv) {
+                uint32_t pw = 0u, mw = 0u;
+#pragma unroll
+                for (int x = 0; x < 8; ++x)
+                    if (x == w) { pw = part[x]; mw = mask[x]; }
+                vwords[wbase + w] = quad_old ? ((vold[i] & ~mw) | pw) : pw;
+            }
+        }
+    }
+    // V scales: new tokens get theirs, empty slots zero; earlier tokens keep theirs
+    if (g == 0 && t >= told)
+        reinterpret_cast<uint16_t*>(sec + L.vscale_off)[t] = vs;
+}
+
+// The ring update for sequence s, KV head kv: the newest min(n_new, R) keys into their slots.
+// Called by the threads that gathered the call's first page (the only reader of the ring),
+// after a barrier that follows their gather.
+template <int D>
+__device__ __forceinline__ void write_ring(const WriteArgs& a, int s, int kv, int p0, int tid,
+                                           int nthreads) {
+    constexpr int CPT = D / 16;
+    uint16_t* ring_s = a.ring + (size_t)s * a.R * a.H * D;
+    const int end = p0 + a.n_new;
+    const int first = max(p0, end - a.R);
+    const int chunks = (end - first) * 16;
+    for (int i = tid; i < chunks; i += nthreads) {
+        const int pp = first + i / 16, cc = (i % 16) * CPT;
+        const uint16_t* src = a.k_new + (((size_t)s * a.n_new + (pp - p0)) * a.H + kv) * D + cc;
+        uint16_t* dst = ring_s + ((size_t)(pp % a.R) * a.H + kv) * D + cc;
+        if constexpr (CPT == 8)
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+        else
+            *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+    }
+}
+
+}  // namespace kvq
