@@ -4,8 +4,10 @@
 A step is one pass of the whole hot path over one synthetic decode token: for every layer,
 quantize-on-write of the new key/value (kv_quant_write) followed by decode attention over the
 paged mixed-precision cache (kv_decode_attn); on every 64th step the KL canary runs for every
-layer (kv_canary_kl). Inputs are resident in HBM before timing starts; each timed step is
-replayed from a HIP graph holding exactly the eager step's launches.
+layer (kv_canary_kl). The write and the attention of a layer run as one launch
+(kv_decode_step; --unfused times the two separate calls). Inputs are resident in HBM before
+timing starts; each timed step is replayed from a HIP graph holding exactly the eager step's
+launches.
 
     python bench.py [--gpus 1] [--steps 256] [--warmup 10] [--workload qwen14b_32k]
 
@@ -29,20 +31,24 @@ sys.path.insert(0, ROOT)
 METRIC = "quantized decode-attn achieved HBM GB/s + decode steps/s, 14B-shape @32K"
 HBM_PEAK_GBS = 8000.0
 CANARY_EVERY = 64
-ATTN_SRC = os.path.join(ROOT, "mixed_precision_quantized_kv_amd", "csrc", "kv_attn.hip")
+ATTN_SRC = [os.path.join(ROOT, "mixed_precision_quantized_kv_amd", "csrc", f)
+            for f in ("kv_attn.hip", "kvq_write_dev.hpp", "kvq_device.hpp")]
 
 # HBM bytes per attention launch on the default workload, from two rocprofv3 --pmc passes
 # (FETCH_SIZE, WRITE_SIZE) scaled by the same counters' reading for a plain copy kernel of known
-# size. It describes the kernel source with this digest only; after any change to that source
+# size. It describes the kernel sources with this digest only; after any change to them
 # the bench reports traffic as null until the counters are taken again.
 ATTN_TRAFFIC = {"source_sha256": "eda97b8727dfa921d43d364e8eb175944306dcaf43a0b8932aebc51931071aca",
                 "bytes_per_launch": 45303455}
 
 
-def source_digest(path: str) -> str:
+def source_digest(paths) -> str:
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def hbm_probes(torch, dev) -> dict:
@@ -85,6 +91,8 @@ def parse():
     ap.add_argument("--cpu-layers", type=int, default=0, help="layers in the oracle's sample (0 = all)")
     ap.add_argument("--cpu-reps", type=int, default=3, help="oracle steps timed per sampled layer")
     ap.add_argument("--pages-per-split", type=int, default=0)
+    ap.add_argument("--unfused", action="store_true",
+                    help="write and attend with two launches per layer instead of kv_decode_step")
     return ap.parse_args()
 
 
@@ -96,6 +104,20 @@ def attn_bytes(w, ctx: int, bits: int) -> int:
     pages = (ctx + 15) // 16
     per_kv = ctx * (D * bits // 4 + 2) + pages * 2 * D
     return H * per_kv + 4 * pages
+
+
+def write_bytes(w, pos: int, n: int, bits: int) -> int:
+    """bytes the write of n tokens at pos must move for one sequence: the touched pages' present
+    keys (ring or input) and the new values in, the pages' K codes and scales, the new tokens' V
+    codes and scales, and the new keys into the ring out"""
+    D, H, P = w.head_dim, w.num_kv_heads, 16
+    lo = pos // P * P
+    present = pos + n - lo                           # keys the touched pages hold afterwards
+    pages = (pos + n - 1) // P - pos // P + 1
+    per_kv = (present * D * 2 + n * D * 2 +          # keys and new values in
+              pages * (P * D * bits // 8 + 2 * D) +  # K codes and scales out
+              n * (D * bits // 8 + 2) + n * D * 2)   # V codes and scales, ring out
+    return H * per_kv
 
 
 class Model:
@@ -194,15 +216,25 @@ def run(args):
 
     def writes_and_attention(i, sp_):
         for l in range(L):
-            kvq.kv_quant_write(m.g, m.pools[l], m.bt[l], pos_all[i], B, nn, k_all[i, l], v_all[i, l],
-                               m.ring[l], stream=sp_)
-            kvq.kv_decode_attn(m.g, m.pools[l], m.bt[l], ctx_all[i], B, m.max_ctx, q_all[i, l], scale,
-                               out, ws, wsb, pps, stream=sp_)
+            if args.unfused:
+                kvq.kv_quant_write(m.g, m.pools[l], m.bt[l], pos_all[i], B, nn, k_all[i, l],
+                                   v_all[i, l], m.ring[l], stream=sp_)
+                kvq.kv_decode_attn(m.g, m.pools[l], m.bt[l], ctx_all[i], B, m.max_ctx, q_all[i, l],
+                                   scale, out, ws, wsb, pps, stream=sp_)
+            else:                                        # one launch: write, then attention
+                kvq.kv_decode_step(m.g, m.pools[l], m.bt[l], pos_all[i], B, nn, k_all[i, l],
+                                   v_all[i, l], m.ring[l], m.max_ctx, q_all[i, l], scale, out, ws,
+                                   wsb, pps, stream=sp_)
 
     def attention_only(i, sp_):
         for l in range(L):
-            kvq.kv_decode_attn(m.g, m.pools[l], m.bt[l], ctx_all[i], B, m.max_ctx, q_all[i, l], scale,
-                               out, ws, wsb, pps, stream=sp_)
+            if args.unfused:
+                kvq.kv_decode_attn(m.g, m.pools[l], m.bt[l], ctx_all[i], B, m.max_ctx, q_all[i, l],
+                                   scale, out, ws, wsb, pps, stream=sp_)
+            else:          # the step's own kernel; replaying its write stores the same bytes again
+                kvq.kv_decode_step(m.g, m.pools[l], m.bt[l], pos_all[i], B, nn, k_all[i, l],
+                                   v_all[i, l], m.ring[l], m.max_ctx, q_all[i, l], scale, out, ws,
+                                   wsb, pps, stream=sp_)
 
     def canary_all(i, sp_):
         for l in range(L):
@@ -275,7 +307,9 @@ def run(args):
         ctx = lens + (args.warmup + j) * nn
         for l, b in enumerate(m.bits):
             per_launch_bytes[j, l] = sum(attn_bytes(w, int(c), b) for c in ctx)
-        step_bytes.append(per_launch_bytes[j].sum())
+            if not args.unfused:
+                per_launch_bytes[j, l] += sum(write_bytes(w, int(c) - nn, nn, b) for c in ctx)
+        step_bytes.append(sum(attn_bytes(w, int(c), b) for c in ctx for b in m.bits))
     step_bytes = float(np.mean(step_bytes))
     avg_launch_bytes = float(per_launch_bytes.mean())
     avg_attn_ms = float(attn_group_ms.mean()) / L
@@ -315,7 +349,9 @@ def run(args):
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "decode_attn_kernel<128>", "bytes_per_launch": int(avg_launch_bytes),
+            "kernel": "decode_attn_kernel<128> (unfused)" if args.unfused else
+                      "decode_attn_kernel<128> fused with the write (kv_decode_step)",
+            "bytes_per_launch": int(avg_launch_bytes),
             "traffic_over_algorithmic": round(traffic / avg_launch_bytes, 4) if traffic else None,
         },
         "hbm_probes": probes,
