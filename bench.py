@@ -38,8 +38,10 @@ ATTN_SRC = [os.path.join(ROOT, "mixed_precision_quantized_kv_amd", "csrc", f)
 # (FETCH_SIZE, WRITE_SIZE) scaled by the same counters' reading for a plain copy kernel of known
 # size. It describes the kernel sources with this digest only; after any change to them
 # the bench reports traffic as null until the counters are taken again.
-ATTN_TRAFFIC = {"source_sha256": "eda97b8727dfa921d43d364e8eb175944306dcaf43a0b8932aebc51931071aca",
-                "bytes_per_launch": 45303455}
+ATTN_TRAFFIC = {"source_sha256": "e6d6f4ab0583804d89abfe8e96667f6d83c15905f551f4ffcf26caab77e716ef",
+                "bytes_per_launch": 45392488,
+                # the bench's algorithmic bytes per launch at the counter run's contexts
+                "algorithmic_bytes_per_launch": 41816654}
 
 
 def source_digest(paths) -> str:
@@ -352,7 +354,8 @@ def run(args):
             "kernel": "decode_attn_kernel<128> (unfused)" if args.unfused else
                       "decode_attn_kernel<128> fused with the write (kv_decode_step)",
             "bytes_per_launch": int(avg_launch_bytes),
-            "traffic_over_algorithmic": round(traffic / avg_launch_bytes, 4) if traffic else None,
+            "traffic_over_algorithmic": (round(traffic / ATTN_TRAFFIC["algorithmic_bytes_per_launch"], 4)
+                                         if traffic else None),
         },
         "hbm_probes": probes,
         "attn_source_sha256": source_digest(ATTN_SRC),
