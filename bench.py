@@ -320,8 +320,9 @@ def run(args):
     value = step_bytes / (ms_step * 1e-3) / 1e9
     probes = hbm_probes(torch, dev)
     traffic = None
-    if ATTN_TRAFFIC["source_sha256"] == source_digest(ATTN_SRC):
-        traffic = ATTN_TRAFFIC["bytes_per_launch"]
+    if (ATTN_TRAFFIC["source_sha256"] == source_digest(ATTN_SRC) and not args.unfused
+            and args.workload == "qwen14b_32k" and not args.pages_per_split):
+        traffic = ATTN_TRAFFIC["bytes_per_launch"]      # taken on the fused kernel, default workload
     tiers = {b: m.bits.count(b) for b in (2, 4, 8)}
     res = {
         "metric": METRIC,
