@@ -157,7 +157,8 @@ kv_status kv_decode_attn(const kv_geometry* g, const kv_layer_pools* pools, cons
                          size_t workspace_bytes, int pages_per_split, void* stream);
 
 /* ---------------------------------------------------------------- fused decode step
- * The write of kv_quant_write and the attention of kv_decode_attn in one launch (one per layer
+ * [EchoKV] "How EchoKV works": each step appends the new key to the ring, quantizes, then
+ * attends. The write of kv_quant_write and the attention of kv_decode_attn in one launch (one per layer
  * and step): for each sequence s, n_new tokens are written at positions pos[s] .. pos[s]+n_new-1
  * exactly as kv_quant_write writes them (same bytes, same ring), and the attention then runs
  * over ctx_len = pos[s] + n_new tokens exactly as kv_decode_attn runs it (same outputs). The
@@ -176,7 +177,7 @@ kv_status kv_decode_step(const kv_geometry* g, const kv_layer_pools* pools, cons
                          float softmax_scale, float* out, void* workspace,
                          size_t workspace_bytes, int pages_per_split, void* stream);
 
-/* ---------------------------------------------------------------- canary/* ---------------------------------------------------------------- canary
+/* ---------------------------------------------------------------- canary
  * [EchoKV] "Show the math": delta_b = KL(softmax(Q K_ref^T) || softmax(Q quant_b(K_ref)^T)),
  * summed over keys, averaged over queries; one number per b in {2, 4, 8}. K_ref is the ring:
  * for each sequence the n = min(seq_len[s], R) newest keys (positions seq_len-n .. seq_len-1).

@@ -7,8 +7,10 @@
 // the kernel is built to stream the packed pages at HBM rate.
 //
 // Work decomposition. A workgroup of 8 waves owns one (sequence, KV head, split) -- a run of
-// `pps` pages; its waves take page pairs round-robin, two pairs in flight per wave. Per page
-// pair a wave computes, on MFMA (v_mfma_f32_16x16x32_f16):
+// `pps` pages; each wave takes a contiguous chunk of the split and walks it in page pairs, two
+// pairs in flight. A chunk whose pages share one width (the common case) runs a loop compiled
+// for that width; otherwise each page carries its own. Per page pair a wave computes, on MFMA
+// (v_mfma_f32_16x16x32_f16):
 //   S^T[t][h] = sum_c Kcode[t][c] * q'[h][c],  q' = q * Kscale(page, c)     (16 tokens a page)
 //   o^T[c][h] += sum_t Vcode[t][c] * p'[h][t], p' = p * Vscale(t)          (32 tokens a pair)
 // K codes become exact fp16 integers (byte masks + v_perm_b32 + one packed add). The K scales
@@ -78,11 +80,6 @@ struct PageRaw {
     int ntok;        // valid tokens in the page
 };
 
-// Loads of one page for this lane. The instruction sequence is the same for every tier (two
-// 16-byte K loads, two 16-byte V loads, one scale dword, one scale pair): the second 16 bytes are
-// only needed by INT8, so INT2/INT4 re-read their first 16 bytes (same cache lines, all inside
-// the section). A fixed count lets the compiler wait for exactly one page's loads while the next
-// pairs' loads stay in flight. `page` must be a valid page index even when `present` is false.
 // what the width-independent page loads need, as plain values (the kernel argument block is
 // never addressed, so it stays in scalar registers)
 struct PageSrc {
@@ -93,6 +90,12 @@ struct PageSrc {
     int H;
 };
 
+// Loads of one page for this lane, width read from its handle. The instruction sequence is the
+// same for every tier (two 16-byte K loads, two 16-byte V loads, one scale dword, one scale pair):
+// the second 16 bytes are only needed by INT8, so INT2/INT4 re-read their first 16 bytes (same
+// cache lines, all inside the section). A fixed count lets the compiler wait for exactly one
+// page's loads while the next pairs' loads stay in flight. `page` must be a valid page index
+// even when `present` is false.
 template <int D>
 __device__ __forceinline__ void load_page(const PageSrc& a, int kv, int page, bool present,
                                           int ctx, int lane, PageRaw& r) {
