@@ -116,6 +116,41 @@ void      kv_alloc_destroy(kv_alloc* a);
    length holds a valid handle, no block is used twice, every other entry is KV_NO_BLOCK */
 kv_status kv_check_block_table(const kv_alloc* a, const uint32_t* bt_host);
 
+/* ---------------------------------------------------------------- controller (host)
+ * [EchoKV] "Show the math - what the canary actually computes": every canary firing gives one
+ * KL reading per (layer, width b in {2,4,8}); each goes into its own exponential moving average
+ * EMA <- (1 - alpha) EMA + alpha * reading (alpha = 0.1 on the page), and each layer's width
+ * becomes the least b whose EMA is below tau(L) = tau0 * sqrt(L / L0) (tau0 = 0.022 at
+ * L0 = 4096, "The tau(L) scaling"; L is the context length), chosen again at every firing
+ * ("Bidirectional adjustment"). "Measurement protocol - warmup, freeze, measure": a frozen
+ * controller ignores readings. Readings of the silent points: a pair's first reading starts its
+ * EMA; no width under the budget gives INT8; before its first firing a layer keeps its initial
+ * width. EMAs are binary64, each update two IEEE products and one sum (no contraction).
+ * A host object owned by the library; not thread-safe. */
+typedef struct kv_controller kv_controller;
+
+/* budget tau0 * sqrt(context_len / l0); NaN unless all three are > 0 */
+double    kv_controller_tau(double tau0, double l0, double context_len);
+/* initial_bits[num_layers] in {2,4,8,16}; alpha in (0,1]; tau0, l0 > 0 and finite */
+kv_status kv_controller_create(int num_layers, const int* initial_bits, double alpha, double tau0,
+                               double l0, kv_controller** out);
+/* one firing: kl_host[num_layers][3] = the readings of widths 2, 4, 8 (finite, >= 0; e.g. the
+   kl_out of kv_canary_kl for each layer, copied to the host); context_len > 0 sets the budget
+   (for a batch, the mean length of its sequences: the readings are means over its rows).
+   Writes the widths to bits_out[num_layers] when it is not NULL. A rejected call changes
+   nothing. */
+kv_status kv_controller_observe(kv_controller* c, const float* kl_host, double context_len,
+                                int* bits_out);
+kv_status kv_controller_set_frozen(kv_controller* c, int frozen);
+/* any output may be NULL: ema[num_layers][3] (NaN before a pair's first reading),
+   bits[num_layers], firings (readings taken while not frozen) */
+kv_status kv_controller_state(const kv_controller* c, double* ema, int* bits, int64_t* firings);
+/* route later blocks of every layer to its current width (kv_alloc_set_layer_bits for each
+   layer); all-or-nothing: KV_EINVAL if the layer counts differ, KV_EUNSUPPORTED if a width has
+   no pool */
+kv_status kv_controller_apply(const kv_controller* c, kv_alloc* a);
+void      kv_controller_destroy(kv_controller* c);
+
 /* ---------------------------------------------------------------- quantize-on-write
  * [EchoKV] "How EchoKV works": each step's key is written into the layer's FP16 ring before it
  * is quantized into the paged cache. [RoleKV] "K/V Role-Aware Low-Bit Quantization": keys per

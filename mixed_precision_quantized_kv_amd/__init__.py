@@ -67,6 +67,14 @@ def lib() -> ctypes.CDLL:
             "kv_alloc_layer_bits": (i32, [P, i32]),
             "kv_alloc_destroy": (None, [P]),
             "kv_check_block_table": (i32, [P, P]),
+            "kv_controller_tau": (ctypes.c_double, [ctypes.c_double] * 3),
+            "kv_controller_create": (i32, [i32, P, ctypes.c_double, ctypes.c_double,
+                                           ctypes.c_double, ctypes.POINTER(P)]),
+            "kv_controller_observe": (i32, [P, P, ctypes.c_double, P]),
+            "kv_controller_set_frozen": (i32, [P, i32]),
+            "kv_controller_state": (i32, [P, P, P, P]),
+            "kv_controller_apply": (i32, [P, P]),
+            "kv_controller_destroy": (None, [P]),
             "kv_quant_write": (i32, [G, ctypes.POINTER(LayerPools), P, P, i32, i32, P, P, P, P]),
             "kv_decode_workspace_bytes": (sz, [G, i32, i32, i32]),
             "kv_decode_pages_per_split": (i32, [G, i32, i32]),
@@ -214,6 +222,58 @@ class KVAlloc:
     def __del__(self):
         try:
             self.kv_alloc_destroy()
+        except Exception:
+            pass
+
+
+# ------------------------------------------------------------------ controller (host)
+def kv_controller_tau(tau0: float, l0: float, context_len: float) -> float:
+    return lib().kv_controller_tau(tau0, l0, context_len)
+
+
+class KVController:
+    """kv_controller_*: canary readings [L][3] in, one width per layer out (host only)."""
+
+    def __init__(self, initial_bits, alpha: float = 0.1, tau0: float = 0.022, l0: float = 4096.0):
+        import numpy as np
+        b = np.ascontiguousarray(initial_bits, dtype=np.int32)
+        self.layers = int(b.size)
+        h = ctypes.c_void_p()
+        _check(lib().kv_controller_create(self.layers, b.ctypes.data, alpha, tau0, l0,
+                                          ctypes.byref(h)))
+        self.handle = h.value
+
+    def kv_controller_observe(self, kl, context_len: float):
+        import numpy as np
+        k = np.ascontiguousarray(kl, dtype=np.float32).reshape(self.layers, 3)
+        out = np.zeros(self.layers, dtype=np.int32)
+        _check(lib().kv_controller_observe(self.handle, k.ctypes.data, float(context_len),
+                                           out.ctypes.data))
+        return out
+
+    def kv_controller_set_frozen(self, frozen: bool) -> None:
+        _check(lib().kv_controller_set_frozen(self.handle, int(bool(frozen))))
+
+    def kv_controller_state(self):
+        import numpy as np
+        ema = np.zeros((self.layers, 3), dtype=np.float64)
+        bits = np.zeros(self.layers, dtype=np.int32)
+        n = ctypes.c_int64()
+        _check(lib().kv_controller_state(self.handle, ema.ctypes.data, bits.ctypes.data,
+                                         ctypes.byref(n)))
+        return ema, bits, n.value
+
+    def kv_controller_apply(self, alloc: "KVAlloc") -> None:
+        _check(lib().kv_controller_apply(self.handle, alloc.handle))
+
+    def kv_controller_destroy(self) -> None:
+        if self.handle:
+            lib().kv_controller_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.kv_controller_destroy()
         except Exception:
             pass
 

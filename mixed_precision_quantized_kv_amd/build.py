@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["kv_api.cpp", "kv_write.hip", "kv_attn.hip", "kv_canary.hip"]
+SOURCES = ["kv_api.cpp", "kv_controller.cpp", "kv_write.hip", "kv_attn.hip", "kv_canary.hip"]
 FLAGS = ["-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-fno-fast-math", "-ffp-contract=fast", "-fhip-fp32-correctly-rounded-divide-sqrt",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -31,7 +31,10 @@ FLAGS = ["-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 # (bisected with -opt-bisect-limit to that pass on this kernel; the IR it emits looks sound,
 # so the fault is further down the backend). Without it the backend still forms the same
 # 16-byte global loads, and the kernel runs at the same speed.
-EXTRA = {"kv_attn.hip": ["-mllvm", "-amdgpu-load-store-vectorizer=0"]}
+# The controller keeps its averages bit-identical to a plain binary64 evaluation, so it is built
+# without floating-point contraction.
+EXTRA = {"kv_attn.hip": ["-mllvm", "-amdgpu-load-store-vectorizer=0"],
+         "kv_controller.cpp": ["-ffp-contract=off"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -11,9 +11,10 @@
 
 #include "kv_quant.h"
 #include "kvq_device.hpp"
+#include "kvq_host.hpp"
 #include "kvq_launch.hpp"
 
-namespace {
+namespace kvq {
 
 thread_local char g_last_error[512] = "";
 
@@ -29,6 +30,23 @@ kv_status ok() {
     g_last_error[0] = '\0';
     return KV_OK;
 }
+
+const char* last_error() { return g_last_error; }
+
+}  // namespace kvq
+
+namespace {
+
+int tier_of_bits(int bits);
+
+}  // namespace
+
+bool kvq::alloc_accepts_bits(int bits) { return tier_of_bits(bits) >= 0; }
+
+namespace {
+
+using kvq::fail;
+using kvq::ok;
 
 kv_status hip_status(hipError_t e, const char* what) {
     if (e == hipSuccess) return ok();
@@ -122,7 +140,7 @@ const char* kv_strerror(kv_status s) {
     return "unknown status";
 }
 
-const char* kv_last_error(void) { return g_last_error; }
+const char* kv_last_error(void) { return kvq::last_error(); }
 
 kv_status kv_validate(const kv_geometry* g) { return check_geometry(g); }
 

@@ -1,0 +1,108 @@
+"""The library's EchoKV controller (kv_controller_*, host code in libkvq) against the oracle's
+controller: identical widths and bit-identical averages on the same readings, including
+readings placed exactly around the budget; argument checks without side effects; freezing;
+and the hand-off to the block allocator (later blocks only). Runs on the CPU: the controller
+never touches the GPU."""
+import math
+
+import numpy as np
+import pytest
+
+import mixed_precision_quantized_kv_amd as kvq
+from oracle import controller as oc
+
+
+def readings(rng, L, n, budget):
+    """KL-like readings: log-uniform over six decades, a share of them within 1% of the budget"""
+    x = np.exp(rng.uniform(np.log(1e-5), np.log(1.0), size=(n, L, 3))).astype(np.float32)
+    near = rng.random((n, L, 3)) < 0.3
+    x[near] = (budget * rng.uniform(0.99, 1.01, size=near.sum())).astype(np.float32)
+    return x
+
+
+@pytest.mark.parametrize("seed,L,context", [(0, 4, 4096), (1, 80, 131072), (2, 48, 32768),
+                                            (3, 1, 1000.5)])
+def test_library_equals_oracle(seed, L, context):
+    rng = np.random.default_rng(seed)
+    init = list(rng.choice([2, 4, 8, 16], size=L))
+    lib_c = kvq.KVController(init)
+    orc_c = oc.Controller(L, init)
+    budget = oc.tau(context)
+    assert kvq.kv_controller_tau(0.022, 4096.0, context) == budget
+    for step, kl in enumerate(readings(rng, L, 60, budget)):
+        got = lib_c.kv_controller_observe(kl, context)
+        ref = orc_c.observe(kl.astype(np.float64).tolist(), context)
+        assert list(got) == ref, f"firing {step}"
+        ema, bits, n = lib_c.kv_controller_state()
+        assert np.array_equal(ema, np.array(orc_c.ema, dtype=np.float64)), f"firing {step}"
+        assert list(bits) == ref and n == step + 1
+
+
+def test_state_before_first_reading_and_freeze():
+    c = kvq.KVController([16, 8])
+    ema, bits, n = c.kv_controller_state()
+    assert np.isnan(ema).all() and list(bits) == [16, 8] and n == 0
+    c.kv_controller_observe([[0.001, 0.001, 0.0], [1.0, 1.0, 1.0]], 4096)
+    snap = c.kv_controller_state()
+    c.kv_controller_set_frozen(True)
+    for _ in range(5):
+        assert list(c.kv_controller_observe([[1.0, 1.0, 1.0], [0.0, 0.0, 0.0]], 4096)) == [2, 8]
+    after = c.kv_controller_state()
+    assert np.array_equal(snap[0], after[0]) and list(snap[1]) == list(after[1]) and snap[2] == after[2]
+    c.kv_controller_set_frozen(False)
+    c.kv_controller_observe([[1.0, 1.0, 1.0], [0.0, 0.0, 0.0]], 4096)
+    assert c.kv_controller_state()[2] == 2
+
+
+@pytest.mark.parametrize("bad", [[-1e-3, 0, 0], [math.nan, 0, 0], [math.inf, 0, 0]])
+def test_rejected_readings_change_nothing(bad):
+    c = kvq.KVController([4, 4])
+    c.kv_controller_observe([[0.01, 0.01, 0.0], [0.5, 0.01, 0.0]], 4096)
+    snap = c.kv_controller_state()
+    with pytest.raises(kvq.KVError):
+        c.kv_controller_observe([[0.0, 0.0, 0.0], bad], 4096)
+    with pytest.raises(kvq.KVError):
+        c.kv_controller_observe([[0.0, 0.0, 0.0], [0.0, 0.0, 0.0]], 0.0)
+    after = c.kv_controller_state()
+    assert np.array_equal(snap[0], after[0]) and list(snap[1]) == list(after[1]) and snap[2] == after[2]
+
+
+@pytest.mark.parametrize("args", [dict(initial_bits=[3]), dict(initial_bits=[4], alpha=0.0),
+                                  dict(initial_bits=[4], alpha=1.5), dict(initial_bits=[4], tau0=-1.0),
+                                  dict(initial_bits=[4], l0=0.0), dict(initial_bits=[])])
+def test_create_rejects(args):
+    with pytest.raises(kvq.KVError):
+        kvq.KVController(**args)
+    assert math.isnan(kvq.kv_controller_tau(0.022, 0.0, 10.0))
+
+
+def test_apply_routes_later_blocks_only():
+    L, P = 2, 16
+    g = kvq.geometry(L, 8, 2, 64, 1, 16)
+    cap = np.full((L, 3), 16, dtype=np.uint32)
+    alloc = kvq.KVAlloc(g, cap, [8, 8], shuffle_seed=7)
+    alloc.kv_alloc_extend(0, 2 * P + 3)                  # three pages per layer at INT8
+    before = alloc.bt.copy()
+    c = kvq.KVController([8, 8])
+    bits = c.kv_controller_observe([[0.001, 0.001, 0.0], [1.0, 0.001, 0.0]], 4096)
+    assert list(bits) == [2, 4]
+    c.kv_controller_apply(alloc)
+    assert [alloc.kv_alloc_layer_bits(l) for l in range(L)] == [2, 4]
+    alloc.kv_alloc_extend(0, 5 * P)                      # pages 3 and 4 are new
+    tiers = alloc.bt[:, 0, :5] >> 30
+    assert np.array_equal(alloc.bt[:, 0, :3], before[:, 0, :3])   # old blocks untouched
+    assert (tiers[:, :3] == 2).all()
+    assert list(tiers[0, 3:]) == [0, 0] and list(tiers[1, 3:]) == [1, 1]
+    alloc.kv_check_block_table()
+    # a controller over a different number of layers is refused and changes nothing
+    c3 = kvq.KVController([2, 2, 2])
+    with pytest.raises(kvq.KVError):
+        c3.kv_controller_apply(alloc)
+    assert [alloc.kv_alloc_layer_bits(l) for l in range(L)] == [2, 4]
+    # a layer still at its initial width may hold one the allocator has no pool for: refused,
+    # all-or-nothing
+    c_odd = kvq.KVController([4, 16])
+    if kvq.kv_block_bytes(g, 16) == 0:
+        with pytest.raises(kvq.KVError):
+            c_odd.kv_controller_apply(alloc)
+        assert [alloc.kv_alloc_layer_bits(l) for l in range(L)] == [2, 4]
