@@ -38,8 +38,8 @@ ATTN_SRC = [os.path.join(ROOT, "mixed_precision_quantized_kv_amd", "csrc", f)
 # (FETCH_SIZE, WRITE_SIZE) scaled by the same counters' reading for a plain copy kernel of known
 # size. It describes the kernel sources with this digest only; after any change to them
 # the bench reports traffic as null until the counters are taken again.
-ATTN_TRAFFIC = {"source_sha256": "e6d6f4ab0583804d89abfe8e96667f6d83c15905f551f4ffcf26caab77e716ef",
-                "bytes_per_launch": 45392488,
+ATTN_TRAFFIC = {"source_sha256": "d24cb1e9fb046e5155d83bec1e547ff7e732a9509a11d0426617cea1ee999c53",
+                "bytes_per_launch": 45400109,
                 # the bench's algorithmic bytes per launch at the counter run's contexts
                 "algorithmic_bytes_per_launch": 41816654}
 
