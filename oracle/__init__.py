@@ -53,6 +53,7 @@ def lib():
             "orc_f64_to_f16_rne": (ctypes.c_uint16, [d]),
             "orc_f64_to_f16_ru": (ctypes.c_uint16, [d]),
             "orc_quantize_group": (None, [P, i, ctypes.c_ssize_t, i, P, P]),
+            "orc_quantize_group_asym": (None, [P, i, ctypes.c_ssize_t, i, P, P, P]),
             "orc_pack": (None, [P, i, i, P]),
             "orc_unpack": (None, [P, i, i, P]),
             "orc_bits_of_tier": (i, [i]),
@@ -67,6 +68,7 @@ def lib():
             "orc_decode_attn": (i, [P, P, P, i, P, i, P, f, P]),
             "orc_decode_attn_row": (i, [P, P, P, i, P, i, f, P]),
             "orc_canary_kl": (None, [P, P, P, i, P, f, P, P]),
+            "orc_canary_kl_mode": (None, [P, P, P, i, P, f, i, P, P]),
             "orc_kl_logits": (d, [P, P, i]),
             "orc_cache_bytes_per_token": (d, [P, i, P]),
             "orc_ring_bytes": (d, [P, i]),
@@ -122,6 +124,16 @@ def quantize_group(x_bits: np.ndarray, bits: int):
     scale = np.zeros(1, dtype=np.uint16)
     lib().orc_quantize_group(_ptr(x), x.size, 1, bits, _ptr(scale), _ptr(codes))
     return int(scale[0]), codes
+
+
+def quantize_group_asym(x_bits: np.ndarray, bits: int):
+    """asymmetric quantizer over one group: (scale bits, zero-point bits, codes in [0, 2^b-1])"""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    codes = np.zeros(x.size, dtype=np.int32)
+    scale = np.zeros(1, dtype=np.uint16)
+    zero = np.zeros(1, dtype=np.uint16)
+    lib().orc_quantize_group_asym(_ptr(x), x.size, 1, bits, _ptr(scale), _ptr(zero), _ptr(codes))
+    return int(scale[0]), int(zero[0]), codes
 
 
 def pack(q: np.ndarray, bits: int) -> np.ndarray:
@@ -215,15 +227,15 @@ def decode_attn_row(g: Geom, pools: Pools, bt_row: np.ndarray, ctx_len: int, q_r
 
 
 def canary_kl(g: Geom, ring: np.ndarray, seq_len: np.ndarray, q: np.ndarray,
-              softmax_scale: float):
+              softmax_scale: float, asymmetric: bool = False):
     ring = np.ascontiguousarray(ring, dtype=np.uint16)
     seq_len = np.ascontiguousarray(seq_len, dtype=np.int32)
     q = np.ascontiguousarray(q, dtype=np.uint16)
     B = q.shape[0]
     kl3 = np.zeros(3, dtype=np.float64)
     rows = np.zeros((B, g.num_q_heads, 3), dtype=np.float64)
-    lib().orc_canary_kl(ctypes.byref(g), _ptr(ring), _ptr(seq_len), B, _ptr(q),
-                        float(softmax_scale), _ptr(kl3), _ptr(rows))
+    lib().orc_canary_kl_mode(ctypes.byref(g), _ptr(ring), _ptr(seq_len), B, _ptr(q),
+                             float(softmax_scale), int(bool(asymmetric)), _ptr(kl3), _ptr(rows))
     return kl3, rows
 
 

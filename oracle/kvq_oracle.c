@@ -89,6 +89,42 @@ void orc_quantize_group(const uint16_t* x, int n, ptrdiff_t stride, int bits,
 }
 
 /* ------------------------------------------------------------------------------------------ */
+/* Asymmetric (KIVI-style) quantizer over one group: zero point = the group minimum m, scale    */
+/* s = RU16((max - m) / (2^b - 1)), codes q = round-half-even((x - m) / s) in [0, 2^b - 1],     */
+/* value m + q * s.  Every step is exact in double: the difference of two fp16 values, the      */
+/* quotient's rounding up to fp16 and the code's rounding are decided on values no double       */
+/* rounding can move across a boundary (pinned against exact rational arithmetic).              */
+
+void orc_quantize_group_asym(const uint16_t* x, int n, ptrdiff_t stride, int bits,
+                             uint16_t* scale_out, uint16_t* zero_out, int* codes_out) {
+    const int top = (1 << bits) - 1;
+    double mn = 0.0, mx = 0.0;
+    uint16_t mn_bits = 0;
+    for (int i = 0; i < n; ++i) {
+        const double v = orc_f16_to_f64(x[i * stride]);
+        if (i == 0 || v < mn) { mn = v; mn_bits = x[i * stride]; }
+        if (i == 0 || v > mx) mx = v;
+    }
+    if (n > 0 && mn == 0.0) mn_bits = 0;               /* -0 and +0 are the same zero point */
+    *zero_out = mn_bits;
+    const double range = mx - mn;                      /* exact: two fp16 values */
+    if (range == 0.0) {
+        *scale_out = 0;
+        for (int i = 0; i < n; ++i) codes_out[i] = 0;
+        return;
+    }
+    const uint16_t s = orc_f64_to_f16_ru(range / (double)top);
+    const double sd = orc_f16_to_f64(s);
+    for (int i = 0; i < n; ++i) {
+        double q = rint((orc_f16_to_f64(x[i * stride]) - mn) / sd);
+        if (q > (double)top) q = (double)top;
+        if (q < 0.0) q = 0.0;
+        codes_out[i] = (int)q;
+    }
+    *scale_out = s;
+}
+
+/* ------------------------------------------------------------------------------------------ */
 /* Packing: 32/b codes per little-endian 32-bit word, code k at bit 16*(k%2) + b*(k/2).        */
 
 static int field_bit(int k, int bits) { return 16 * (k % 2) + bits * (k / 2); }
@@ -361,6 +397,12 @@ double orc_kl_logits(const double* l, const double* m, int n) {
 
 void orc_canary_kl(const orc_geom* g, const uint16_t* ring, const int32_t* seq_len, int batch,
                    const uint16_t* q, float softmax_scale, double* kl3, double* rows) {
+    orc_canary_kl_mode(g, ring, seq_len, batch, q, softmax_scale, 0, kl3, rows);
+}
+
+void orc_canary_kl_mode(const orc_geom* g, const uint16_t* ring, const int32_t* seq_len, int batch,
+                        const uint16_t* q, float softmax_scale, int asymmetric, double* kl3,
+                        double* rows) {
     const int P = g->page_size, D = g->head_dim, H = g->num_kv_heads, R = g->ring_size;
     const int Hq = g->num_q_heads, grp = Hq / H;
     const int tiers[3] = {2, 4, 8};
@@ -388,12 +430,19 @@ void orc_canary_kl(const orc_geom* g, const uint16_t* ring, const int32_t* seq_l
                     int j = i;
                     while (j < n && (first + j) / P == page) ++j;
                     for (int c = 0; c < D; ++c) {
-                        uint16_t sc;
+                        uint16_t sc, zp;
                         for (int k = i; k < j; ++k)
                             grpbuf[k - i] = rg[((size_t)((first + k) % R) * H + kv) * D + c];
-                        orc_quantize_group(grpbuf, j - i, 1, tiers[ti], &sc, codes);
-                        for (int k = i; k < j; ++k)
-                            Kb[((size_t)ti * n + k) * D + c] = codes[k - i] * orc_f16_to_f64(sc);
+                        if (asymmetric) {
+                            orc_quantize_group_asym(grpbuf, j - i, 1, tiers[ti], &sc, &zp, codes);
+                            for (int k = i; k < j; ++k)
+                                Kb[((size_t)ti * n + k) * D + c] =
+                                    orc_f16_to_f64(zp) + codes[k - i] * orc_f16_to_f64(sc);
+                        } else {
+                            orc_quantize_group(grpbuf, j - i, 1, tiers[ti], &sc, codes);
+                            for (int k = i; k < j; ++k)
+                                Kb[((size_t)ti * n + k) * D + c] = codes[k - i] * orc_f16_to_f64(sc);
+                        }
                     }
                     i = j;
                 }

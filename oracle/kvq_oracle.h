@@ -64,6 +64,12 @@ uint16_t orc_f64_to_f16_ru(double x);         /* smallest fp16 >= x (x >= 0) */
 void orc_quantize_group(const uint16_t* x, int n, ptrdiff_t stride, int bits,
                         uint16_t* scale_out, int* codes_out);
 
+/* ---- asymmetric (KIVI-style) quantizer over one group: zero point = the group minimum m (its
+ * fp16 bits, +0 for a zero minimum), scale s = RU16((max - m) / (2^b - 1)) (0 for a constant
+ * group), codes round-half-even((x - m) / s) in [0, 2^b - 1]; value m + code * s ---- */
+void orc_quantize_group_asym(const uint16_t* x, int n, ptrdiff_t stride, int bits,
+                             uint16_t* scale_out, uint16_t* zero_out, int* codes_out);
+
 /* ---- packing of a code sequence ---- */
 void orc_pack(const int* q, int n, int bits, uint8_t* out);   /* n a multiple of 32/bits */
 void orc_unpack(const uint8_t* in, int n, int bits, int* q);
@@ -102,6 +108,11 @@ int orc_decode_attn_row(const orc_geom* g, uint8_t* const pools[3], const uint32
  * rows (optional) [batch][H_q][3]. ring [batch][R][H_kv][D]; q [batch][H_q][D]. */
 void orc_canary_kl(const orc_geom* g, const uint16_t* ring, const int32_t* seq_len, int batch,
                    const uint16_t* q, float softmax_scale, double* kl3, double* rows);
+/* the same with the temporary copies built by the asymmetric quantizer when asymmetric != 0
+ * (EchoKV names its canary quantizer "KIVI-style asymmetric per-group"); same groups */
+void orc_canary_kl_mode(const orc_geom* g, const uint16_t* ring, const int32_t* seq_len, int batch,
+                        const uint16_t* q, float softmax_scale, int asymmetric, double* kl3,
+                        double* rows);
 /* KL of two logit vectors, in the log-sum-exp form used by the canary (test helper) */
 double orc_kl_logits(const double* l, const double* m, int n);
 
