@@ -227,6 +227,16 @@ size_t    kv_canary_workspace_bytes(const kv_geometry* g, int batch);
 kv_status kv_canary_kl(const kv_geometry* g, const uint16_t* ring, const int32_t* seq_len,
                        int batch, const uint16_t* q, float softmax_scale, float* kl_out,
                        float* kl_rows, void* workspace, size_t workspace_bytes, void* stream);
+/* The same divergence with the temporary copies built by the asymmetric quantizer ([EchoKV]
+ * "Show the math" describes its canary quantizer as asymmetric per group, in the manner of KIVI),
+ * over the same groups (each ring key's page, one group per channel): zero point m = the group
+ * minimum, scale s = RU16((max - m) / (2^b - 1)) (0 for a constant group), code =
+ * round-half-even((x - m) / s) in [0, 2^b - 1], value m + code * s; decided in binary64, which
+ * is exact for fp16 keys. Arguments, workspace and errors as for kv_canary_kl. */
+kv_status kv_canary_kl_asym(const kv_geometry* g, const uint16_t* ring, const int32_t* seq_len,
+                            int batch, const uint16_t* q, float softmax_scale, float* kl_out,
+                            float* kl_rows, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 #ifdef __cplusplus
 }

@@ -84,6 +84,7 @@ def lib() -> ctypes.CDLL:
                                      P, ctypes.c_float, P, P, sz, i32, P]),
             "kv_canary_workspace_bytes": (sz, [G, i32]),
             "kv_canary_kl": (i32, [G, P, P, i32, P, ctypes.c_float, P, P, P, sz, P]),
+            "kv_canary_kl_asym": (i32, [G, P, P, i32, P, ctypes.c_float, P, P, P, sz, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -314,3 +315,12 @@ def kv_canary_kl(g: Geometry, ring, seq_len, batch: int, q, softmax_scale: float
     _check(lib().kv_canary_kl(ctypes.byref(g), _addr(ring), _addr(seq_len), batch, _addr(q),
                               softmax_scale, _addr(kl_out), _addr(kl_rows), _addr(workspace),
                               workspace_bytes, _stream(stream)))
+
+
+def kv_canary_kl_asym(g: Geometry, ring, seq_len, batch: int, q, softmax_scale: float, kl_out,
+                      kl_rows, workspace, workspace_bytes=None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().kv_canary_kl_asym(ctypes.byref(g), _addr(ring), _addr(seq_len), batch, _addr(q),
+                                   softmax_scale, _addr(kl_out), _addr(kl_rows), _addr(workspace),
+                                   workspace_bytes, _stream(stream)))

@@ -417,9 +417,10 @@ size_t kv_canary_workspace_bytes(const kv_geometry* g, int batch) {
     return kvq::canary_workspace_bytes(*g, batch);
 }
 
-kv_status kv_canary_kl(const kv_geometry* g, const uint16_t* ring, const int32_t* seq_len,
-                       int batch, const uint16_t* q, float softmax_scale, float* kl_out,
-                       float* kl_rows, void* workspace, size_t workspace_bytes, void* stream) {
+static kv_status canary(const kv_geometry* g, const uint16_t* ring, const int32_t* seq_len,
+                        int batch, const uint16_t* q, float softmax_scale, bool asymmetric,
+                        float* kl_out, float* kl_rows, void* workspace, size_t workspace_bytes,
+                        void* stream, const char* name) {
     kv_status st = check_geometry(g);
     if (st != KV_OK) return st;
     if (batch < 1 || batch > g->max_seqs) return fail(KV_EINVAL, "batch %d", batch);
@@ -433,9 +434,25 @@ kv_status kv_canary_kl(const kv_geometry* g, const uint16_t* ring, const int32_t
     if (workspace_bytes < need)
         return fail(KV_EINVAL, "workspace %zu bytes, %zu needed", workspace_bytes, need);
     if (!(softmax_scale == softmax_scale)) return fail(KV_EINVAL, "softmax_scale is NaN");
-    return hip_status(kvq::launch_canary(*g, ring, seq_len, batch, q, softmax_scale, kl_out,
-                                         kl_rows, workspace, static_cast<hipStream_t>(stream)),
-                      "kv_canary_kl");
+    return hip_status(kvq::launch_canary(*g, ring, seq_len, batch, q, softmax_scale, asymmetric,
+                                         kl_out, kl_rows, workspace,
+                                         static_cast<hipStream_t>(stream)),
+                      name);
+}
+
+kv_status kv_canary_kl(const kv_geometry* g, const uint16_t* ring, const int32_t* seq_len,
+                       int batch, const uint16_t* q, float softmax_scale, float* kl_out,
+                       float* kl_rows, void* workspace, size_t workspace_bytes, void* stream) {
+    return canary(g, ring, seq_len, batch, q, softmax_scale, false, kl_out, kl_rows, workspace,
+                  workspace_bytes, stream, "kv_canary_kl");
+}
+
+kv_status kv_canary_kl_asym(const kv_geometry* g, const uint16_t* ring, const int32_t* seq_len,
+                            int batch, const uint16_t* q, float softmax_scale, float* kl_out,
+                            float* kl_rows, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    return canary(g, ring, seq_len, batch, q, softmax_scale, true, kl_out, kl_rows, workspace,
+                  workspace_bytes, stream, "kv_canary_kl_asym");
 }
 
 }  // extern "C"

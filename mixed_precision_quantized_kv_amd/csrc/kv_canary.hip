@@ -17,6 +17,11 @@
 // per head then takes the log-sum-exp form of the divergence. Rows are stored with
 // device-coherent stores; the last workgroup to take the ticket averages every row, in row order,
 // from device-coherent loads (no cache flushes).
+//
+// EchoKV describes its canary quantizer as asymmetric per group, in the manner of KIVI; the ASYM
+// instance builds the copies that way, over the same groups: zero point = the group minimum m, scale
+// s = RU16((max - m) / (2^b - 1)), code = round-half-even((x - m) / s) in [0, 2^b - 1], value
+// m + code * s. These decisions are taken in binary64, where they are exact for fp16 inputs.
 #include "kvq_device.hpp"
 #include "kvq_launch.hpp"
 
@@ -57,14 +62,26 @@ __device__ __forceinline__ void group_logits(const float* qs, const float* keys,
     }
 }
 
-template <int D>
+// smallest fp16 >= x for finite x > 0 given in binary64: a nearby fp16 value, then one step
+// toward x's side (the double-to-single-to-half rounding lands at most one step away)
+__device__ inline uint16_t f64_to_f16_up(double x) {
+    uint16_t b = f16_bits((_Float16)(float)x);
+    if ((double)f16_val(b) < x)
+        b = (uint16_t)(b + 1);
+    else if (b > 0 && (double)f16_val((uint16_t)(b - 1)) >= x)
+        b = (uint16_t)(b - 1);
+    return b;
+}
+
+template <int D, bool ASYM>
 __global__ __launch_bounds__(kThreads) void canary_kernel(CanaryArgs a) {
     extern __shared__ float smem[];
     const int R = a.R;
     float* kref = smem;                          // [R][D + 1]; later the copy, in place
     float* qs = kref + R * (D + 1);              // [grp][D]
     float* sc = qs + kMaxGroup * D;              // [R / P + 1][D] scales of the copy
-    float* lref = sc + (R / kPage + 1) * D;      // [grp][R]
+    float* zp = sc + (R / kPage + 1) * D;        // [R / P + 1][D] zero points (ASYM only)
+    float* lref = zp + (ASYM ? (R / kPage + 1) * D : 0);   // [grp][R]
     float* lb = lref + kMaxGroup * R;            // [grp][R]
     __shared__ int last;
 
@@ -108,9 +125,21 @@ __global__ __launch_bounds__(kThreads) void canary_kernel(CanaryArgs a) {
         const int pg = i / D, c = i - pg * D;
         const int k0 = max(first, (pfirst + pg) * kPage) - first;
         const int k1 = min(N, (pfirst + pg + 1) * kPage) - first;
-        float amax = 0.f;
-        for (int k = k0; k < k1; ++k) amax = fmaxf(amax, fabsf(kref[k * (D + 1) + c]));
-        sc[pg * D + c] = f16_val(group_scale(amax, bits));
+        if constexpr (ASYM) {
+            float mn = kref[k0 * (D + 1) + c], mx = mn;
+            for (int k = k0 + 1; k < k1; ++k) {
+                mn = fminf(mn, kref[k * (D + 1) + c]);
+                mx = fmaxf(mx, kref[k * (D + 1) + c]);
+            }
+            const double range = (double)mx - (double)mn;      // exact for fp16 inputs
+            sc[pg * D + c] =
+                range > 0.0 ? f16_val(f64_to_f16_up(range / (double)((1 << bits) - 1))) : 0.f;
+            zp[pg * D + c] = mn;
+        } else {
+            float amax = 0.f;
+            for (int k = k0; k < k1; ++k) amax = fmaxf(amax, fabsf(kref[k * (D + 1) + c]));
+            sc[pg * D + c] = f16_val(group_scale(amax, bits));
+        }
     }
     // reference logits meanwhile (they only read the keys and queries)
     group_logits<D>(qs, kref, grp, n, R, a.scale, wave, lane, lref);
@@ -118,9 +147,17 @@ __global__ __launch_bounds__(kThreads) void canary_kernel(CanaryArgs a) {
     // ---- the copy itself, in place of the keys: code * scale, one element a thread and step
     for (int i = tid; i < n * D; i += kThreads) {
         const int k = i / D, c = i - k * D;
-        const float sf = sc[((first + k) / kPage - pfirst) * D + c];
+        const int gi = ((first + k) / kPage - pfirst) * D + c;
+        const float sf = sc[gi];
         const float x = kref[k * (D + 1) + c];
-        kref[k * (D + 1) + c] = sf != 0.f ? (float)quant_code(x, sf, bits) * sf : 0.f;
+        if constexpr (ASYM) {
+            const double m = (double)zp[gi];
+            double q = sf != 0.f ? rint(((double)x - m) / (double)sf) : 0.0;
+            q = fmin(fmax(q, 0.0), (double)((1 << bits) - 1));
+            kref[k * (D + 1) + c] = (float)(m + q * (double)sf);
+        } else {
+            kref[k * (D + 1) + c] = sf != 0.f ? (float)quant_code(x, sf, bits) * sf : 0.f;
+        }
     }
     __syncthreads();
     group_logits<D>(qs, kref, grp, n, R, a.scale, wave, lane, lb);
@@ -187,9 +224,36 @@ size_t canary_workspace_bytes(const kv_geometry& g, int batch) {
     return 256 + (size_t)batch * g.num_q_heads * 3 * sizeof(float);
 }
 
+namespace {
+
+size_t canary_lds_bytes(int R, int D, bool asym) {
+    return sizeof(float) * ((size_t)R * (D + 1) + kMaxGroup * D +
+                            (asym ? 2 : 1) * ((size_t)R / kPage + 1) * D +
+                            2 * kMaxGroup * (size_t)R);
+}
+
+template <int D, bool ASYM>
+hipError_t launch_one(const CanaryArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
+    // the LDS footprint exceeds the 64 KiB default for rings of 64 keys at D = 128: raise the
+    // limit to the largest footprint any supported ring needs, once per process and kernel (so
+    // that launches stay plain stream work, e.g. under graph capture)
+    static std::once_flag once;
+    static hipError_t attr = hipSuccess;
+    std::call_once(once, [] {
+        attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&canary_kernel<D, ASYM>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)canary_lds_bytes(kMaxRing, D, ASYM));
+    });
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((canary_kernel<D, ASYM>), grid, dim3(kThreads), lds, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_canary(const kv_geometry& g, const uint16_t* ring, const int32_t* seq_len,
-                         int batch, const uint16_t* q, float softmax_scale, float* kl_out,
-                         float* kl_rows, void* workspace, hipStream_t stream) {
+                         int batch, const uint16_t* q, float softmax_scale, bool asymmetric,
+                         float* kl_out, float* kl_rows, void* workspace, hipStream_t stream) {
     CanaryArgs a;
     a.ring = ring;
     a.seq_len = seq_len;
@@ -205,29 +269,13 @@ hipError_t launch_canary(const kv_geometry& g, const uint16_t* ring, const int32
     a.batch = batch;
     a.scale = softmax_scale;
     const int D = g.head_dim;
-    const size_t lds = sizeof(float) * ((size_t)a.R * (D + 1) + kMaxGroup * D +
-                                        ((size_t)a.R / kPage + 1) * D + 2 * kMaxGroup * (size_t)a.R);
+    const size_t lds = canary_lds_bytes(a.R, D, asymmetric);
     dim3 grid((unsigned)(batch * g.num_kv_heads), 3u);
-    // the LDS footprint exceeds the 64 KiB default for rings of 64 keys at D = 128: raise the
-    // limit to the largest footprint any supported ring needs, once per process and kernel (so
-    // that launches stay plain stream work, e.g. under graph capture)
-    static std::once_flag once[2];
-    hipError_t e = hipSuccess;
-    const int which = D == 128 ? 0 : 1;
-    std::call_once(once[which], [&] {
-        const void* fn = D == 128 ? reinterpret_cast<const void*>(&canary_kernel<128>)
-                                  : reinterpret_cast<const void*>(&canary_kernel<64>);
-        const size_t max_lds = sizeof(float) * ((size_t)kMaxRing * (D + 1) + kMaxGroup * D +
-                                                ((size_t)kMaxRing / kPage + 1) * D +
-                                                2 * kMaxGroup * (size_t)kMaxRing);
-        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_lds);
-    });
-    if (e != hipSuccess) return e;
     if (D == 128)
-        hipLaunchKernelGGL(canary_kernel<128>, grid, dim3(kThreads), lds, stream, a);
-    else
-        hipLaunchKernelGGL(canary_kernel<64>, grid, dim3(kThreads), lds, stream, a);
-    return hipGetLastError();
+        return asymmetric ? launch_one<128, true>(a, grid, lds, stream)
+                          : launch_one<128, false>(a, grid, lds, stream);
+    return asymmetric ? launch_one<64, true>(a, grid, lds, stream)
+                      : launch_one<64, false>(a, grid, lds, stream);
 }
 
 }  // namespace kvq

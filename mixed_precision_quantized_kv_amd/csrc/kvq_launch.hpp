@@ -33,9 +33,10 @@ hipError_t launch_decode_step(const kv_geometry& g, PoolPtrs pools, const uint32
 // workspace layout of the decode attention (bytes)
 size_t decode_workspace_bytes(const kv_geometry& g, int batch, int splits);
 
+// asymmetric: build the temporary copies with the min / max (zero point) quantizer
 hipError_t launch_canary(const kv_geometry& g, const uint16_t* ring, const int32_t* seq_len,
-                         int batch, const uint16_t* q, float softmax_scale, float* kl_out,
-                         float* kl_rows, void* workspace, hipStream_t stream);
+                         int batch, const uint16_t* q, float softmax_scale, bool asymmetric,
+                         float* kl_out, float* kl_rows, void* workspace, hipStream_t stream);
 size_t canary_workspace_bytes(const kv_geometry& g, int batch);
 
 }  // namespace kvq
