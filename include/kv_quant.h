@@ -1,6 +1,7 @@
 /*
  * kv_quant.h -- C ABI of libkvq: single-token decode over a paged KV cache stored as packed
- * symmetric INT2 / INT4 / INT8 codes with a bit-width chosen per layer, for AMD MI355X (gfx950).
+ * symmetric INT2 / INT4 / INT8 codes (or plain FP16) with a bit-width chosen per layer, for AMD
+ * MI355X (gfx950).
  *
  * The operations follow three web pages on mixed-precision KV-cache quantization:
  *   [EchoKV]  "EchoKV: watching a language model decide its own precision"
@@ -33,6 +34,9 @@
  *   A code sequence is stored as little-endian 32-bit words of 32/b codes; code k of a word is
  *   the unsigned field q + 2^(b-1) at bit 16*(k%2) + b*(k/2). Token slots of a page that hold
  *   no token carry the zero code and a zero scale.
+ *   tier 3 <-> b = 16, plain FP16 ([EchoKV] "How EchoKV works": a layer starts at FP16 before
+ *   the canary first fires): S_16 = 4*P*D bytes, K values [P][D] (index t*D + c) then V values
+ *   at index ((t/4)*D + c)*4 + t%4, no scales; token slots that hold no token are +0.
  *   Quantizer over a group with absolute maximum a: scale s = smallest fp16 >= a/qmax_b
  *   (0 if a == 0), code = round-half-even(x/s); both decided in IEEE binary32, which equals the
  *   exact rational result for fp16 inputs ([Kaizen] "symmetric uniform quantization").
@@ -47,7 +51,8 @@
 extern "C" {
 #endif
 
-#define KV_ABI_VERSION 1
+#define KV_ABI_VERSION 2
+#define KV_NUM_TIERS 4          /* INT2, INT4, INT8, FP16 */
 #define KV_NO_BLOCK 0xFFFFFFFFu
 
 typedef enum {
@@ -69,11 +74,12 @@ typedef struct {
     int32_t max_pages_per_seq;  /* columns of a block table */
 } kv_geometry;
 
-/* the three tier pools of one layer: base[t] holds capacity[t] blocks of kv_block_bytes(g, b_t);
-   each base is 16-byte aligned device memory (or NULL with capacity 0) */
+/* the tier pools of one layer: base[t] holds capacity[t] blocks of kv_block_bytes(g, b_t),
+   b = 2, 4, 8, 16 for t = 0..3; each base is 16-byte aligned device memory (or NULL with
+   capacity 0) */
 typedef struct {
-    void* base[3];
-    uint32_t capacity[3];
+    void* base[KV_NUM_TIERS];
+    uint32_t capacity[KV_NUM_TIERS];
 } kv_layer_pools;
 
 /* ---------------------------------------------------------------- version, errors, sizes */
@@ -81,7 +87,7 @@ int         kv_abi_version(void);
 const char* kv_strerror(kv_status status);
 const char* kv_last_error(void);                    /* thread-local; "" when none */
 kv_status   kv_validate(const kv_geometry* g);
-uint32_t    kv_handle(int bits, uint32_t index);     /* KV_NO_BLOCK for bad bits or index */
+uint32_t    kv_handle(int bits, uint32_t index);     /* bits 2,4,8,16; KV_NO_BLOCK if invalid */
 size_t      kv_block_bytes(const kv_geometry* g, int bits);  /* one block, all KV heads; 0 if invalid */
 size_t      kv_ring_bytes(const kv_geometry* g);    /* one layer's ring: max_seqs*R*H_kv*D*2 */
 /* bytes of cache per token over all layers, bits_per_layer[l] in {2,4,8} or 16 (plain fp16);
@@ -97,7 +103,8 @@ double      kv_cache_bytes_per_token(const kv_geometry* g, const int* bits_per_l
  * copies the rows it needs to the device (one [max_seqs][max_pages_per_seq] table per layer). */
 typedef struct kv_alloc kv_alloc;
 
-/* capacity[l*3 + t] blocks in pool (l, t); bits[l] in {2,4,8} is layer l's current tier */
+/* capacity[l*KV_NUM_TIERS + t] blocks in pool (l, t); bits[l] in {2,4,8,16} is layer l's current
+   width (the tier its new blocks come from) */
 kv_status kv_alloc_create(const kv_geometry* g, const uint32_t* capacity, const int* bits,
                           uint64_t shuffle_seed, kv_alloc** out);
 /* forward-only: later pages of the layer come from the new tier's pool; existing blocks,

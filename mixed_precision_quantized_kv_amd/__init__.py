@@ -18,7 +18,8 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "kv_quant.h")
 
 KV_OK, KV_EINVAL, KV_ENOBLOCKS, KV_EUNSUPPORTED, KV_EHIP = range(5)
 KV_NO_BLOCK = 0xFFFFFFFF
-TIER_BITS = (2, 4, 8)
+TIER_BITS = (2, 4, 8, 16)       # tier index -> bits (16 = plain FP16)
+NUM_TIERS = 4
 
 
 class KVError(RuntimeError):
@@ -34,7 +35,7 @@ class Geometry(ctypes.Structure):
 
 
 class LayerPools(ctypes.Structure):
-    _fields_ = [("base", ctypes.c_void_p * 3), ("capacity", ctypes.c_uint32 * 3)]
+    _fields_ = [("base", ctypes.c_void_p * NUM_TIERS), ("capacity", ctypes.c_uint32 * NUM_TIERS)]
 
 
 _lib = None
@@ -132,10 +133,11 @@ def geometry(num_layers, num_q_heads, num_kv_heads, head_dim, max_seqs, max_page
 
 
 def layer_pools(bases, capacities) -> LayerPools:
+    """pools of one layer; lists of three leave the FP16 pool empty"""
     p = LayerPools()
-    for t in range(3):
-        p.base[t] = _addr(bases[t]) or None
-        p.capacity[t] = int(capacities[t])
+    for t in range(NUM_TIERS):
+        p.base[t] = (_addr(bases[t]) or None) if t < len(bases) else None
+        p.capacity[t] = int(capacities[t]) if t < len(capacities) else 0
     return p
 
 
@@ -184,7 +186,11 @@ class KVAlloc:
     def __init__(self, g: Geometry, capacity, bits, shuffle_seed: int = 0):
         import numpy as np
         self.g = g
-        cap = np.ascontiguousarray(capacity, dtype=np.uint32).reshape(-1)
+        cap = np.asarray(capacity, dtype=np.uint32).reshape(g.num_layers, -1)
+        if cap.shape[1] < NUM_TIERS:                # [L][3]: no FP16 pool
+            cap = np.concatenate([cap, np.zeros((g.num_layers, NUM_TIERS - cap.shape[1]),
+                                                dtype=np.uint32)], axis=1)
+        cap = np.ascontiguousarray(cap).reshape(-1)
         b = np.ascontiguousarray(bits, dtype=np.int32)
         h = ctypes.c_void_p()
         _check(lib().kv_alloc_create(ctypes.byref(g), cap.ctypes.data, b.ctypes.data,

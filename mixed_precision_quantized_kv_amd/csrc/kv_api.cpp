@@ -53,7 +53,11 @@ kv_status hip_status(hipError_t e, const char* what) {
     return fail(KV_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-int tier_of_bits(int bits) { return bits == 2 ? 0 : bits == 4 ? 1 : bits == 8 ? 2 : -1; }
+int tier_of_bits(int bits) {
+    return bits == 2 ? 0 : bits == 4 ? 1 : bits == 8 ? 2 : bits == 16 ? 3 : -1;
+}
+
+constexpr int kTiers = KV_NUM_TIERS;
 
 kv_status check_geometry(const kv_geometry* g) {
     if (!g) return fail(KV_EINVAL, "geometry is NULL");
@@ -78,7 +82,7 @@ kv_status check_geometry(const kv_geometry* g) {
 
 kv_status check_pools(const kv_geometry* g, const kv_layer_pools* p) {
     if (!p) return fail(KV_EINVAL, "pools is NULL");
-    for (int t = 0; t < 3; ++t) {
+    for (int t = 0; t < kTiers; ++t) {
         if (p->capacity[t] > 0x3fffffffu) return fail(KV_EINVAL, "pool %d capacity too large", t);
         if (p->capacity[t] > 0 && !p->base[t]) return fail(KV_EINVAL, "pool %d base is NULL", t);
         if (reinterpret_cast<uintptr_t>(p->base[t]) % 16 != 0)
@@ -90,7 +94,7 @@ kv_status check_pools(const kv_geometry* g, const kv_layer_pools* p) {
 
 kvq::PoolPtrs pool_ptrs(const kv_layer_pools* p) {
     kvq::PoolPtrs r;
-    for (int t = 0; t < 3; ++t) r.base[t] = static_cast<uint8_t*>(p->base[t]);
+    for (int t = 0; t < kTiers; ++t) r.base[t] = static_cast<uint8_t*>(p->base[t]);
     return r;
 }
 
@@ -120,8 +124,8 @@ int auto_pages_per_split(const kv_geometry& g, int batch, int max_pages) {
 struct kv_alloc {
     kv_geometry g;
     std::vector<int> bits;                       // current tier of each layer
-    std::vector<uint32_t> capacity;              // [L][3]
-    std::vector<std::vector<uint32_t>> free;     // [L*3]: free block indices, next at back
+    std::vector<uint32_t> capacity;              // [L][kTiers]
+    std::vector<std::vector<uint32_t>> free;     // [L*kTiers]: free block indices, next at back
     std::vector<int32_t> len;                    // tokens per sequence
 };
 
@@ -164,9 +168,7 @@ double kv_cache_bytes_per_token(const kv_geometry* g, const int* bits) {
     if (check_geometry(g) != KV_OK || !bits) return -1.0;
     double total = 0.0;
     for (int l = 0; l < g->num_layers; ++l) {
-        if (bits[l] == 16)
-            total += 4.0 * g->num_kv_heads * g->head_dim;
-        else if (tier_of_bits(bits[l]) >= 0)
+        if (tier_of_bits(bits[l]) >= 0)
             total += (double)kv_block_bytes(g, bits[l]) / g->page_size;
         else
             return -1.0;
@@ -182,15 +184,15 @@ kv_status kv_alloc_create(const kv_geometry* g, const uint32_t* capacity, const 
     if (!capacity || !bits || !out) return fail(KV_EINVAL, "NULL argument");
     for (int l = 0; l < g->num_layers; ++l) {
         if (tier_of_bits(bits[l]) < 0) return fail(KV_EINVAL, "layer %d bits %d", l, bits[l]);
-        for (int t = 0; t < 3; ++t)
-            if (capacity[l * 3 + t] > 0x3fffffffu) return fail(KV_EINVAL, "capacity too large");
+        for (int t = 0; t < kTiers; ++t)
+            if (capacity[l * kTiers + t] > 0x3fffffffu) return fail(KV_EINVAL, "capacity too large");
     }
     kv_alloc* a = new (std::nothrow) kv_alloc;
     if (!a) return fail(KV_EINVAL, "out of host memory");
     a->g = *g;
     a->bits.assign(bits, bits + g->num_layers);
-    a->capacity.assign(capacity, capacity + 3 * g->num_layers);
-    a->free.resize(3 * (size_t)g->num_layers);
+    a->capacity.assign(capacity, capacity + kTiers * g->num_layers);
+    a->free.resize(kTiers * (size_t)g->num_layers);
     uint64_t x = shuffle_seed;
     for (size_t i = 0; i < a->free.size(); ++i) {
         std::vector<uint32_t>& f = a->free[i];
@@ -224,14 +226,14 @@ kv_status kv_alloc_extend(kv_alloc* a, int seq, int32_t new_len, uint32_t* bt) {
         return fail(KV_EINVAL, "%lld pages exceed max_pages_per_seq", (long long)new_pages);
     const int64_t need = new_pages - old_pages;
     for (int l = 0; l < g.num_layers; ++l) {
-        const std::vector<uint32_t>& f = a->free[(size_t)l * 3 + tier_of_bits(a->bits[l])];
+        const std::vector<uint32_t>& f = a->free[(size_t)l * kTiers + tier_of_bits(a->bits[l])];
         if ((int64_t)f.size() < need)
-            return fail(KV_ENOBLOCKS, "layer %d: %lld free INT%d blocks, %lld needed", l,
+            return fail(KV_ENOBLOCKS, "layer %d: %lld free %d-bit blocks, %lld needed", l,
                         (long long)f.size(), a->bits[l], (long long)need);
     }
     for (int l = 0; l < g.num_layers; ++l) {
         const int t = tier_of_bits(a->bits[l]);
-        std::vector<uint32_t>& f = a->free[(size_t)l * 3 + t];
+        std::vector<uint32_t>& f = a->free[(size_t)l * kTiers + t];
         uint32_t* row = bt + ((size_t)l * g.max_seqs + seq) * g.max_pages_per_seq;
         for (int64_t p = old_pages; p < new_pages; ++p) {
             row[p] = ((uint32_t)t << 30) | f.back();
@@ -253,8 +255,8 @@ kv_status kv_alloc_free_seq(kv_alloc* a, int seq, uint32_t* bt) {
             const uint32_t h = row[p];
             if (h == KV_NO_BLOCK) continue;
             const uint32_t t = h >> 30;
-            if (t < 3 && (h & 0x3fffffffu) < a->capacity[(size_t)l * 3 + t])
-                a->free[(size_t)l * 3 + t].push_back(h & 0x3fffffffu);
+            if (t < (uint32_t)kTiers && (h & 0x3fffffffu) < a->capacity[(size_t)l * kTiers + t])
+                a->free[(size_t)l * kTiers + t].push_back(h & 0x3fffffffu);
         }
         for (int64_t p = 0; p < g.max_pages_per_seq; ++p) row[p] = KV_NO_BLOCK;
     }
@@ -269,7 +271,7 @@ int32_t kv_alloc_seq_len(const kv_alloc* a, int seq) {
 
 int64_t kv_alloc_free_blocks(const kv_alloc* a, int layer, int bits) {
     if (!a || layer < 0 || layer >= a->g.num_layers || tier_of_bits(bits) < 0) return -1;
-    return (int64_t)a->free[(size_t)layer * 3 + tier_of_bits(bits)].size();
+    return (int64_t)a->free[(size_t)layer * kTiers + tier_of_bits(bits)].size();
 }
 
 int kv_alloc_layer_bits(const kv_alloc* a, int layer) {
@@ -283,8 +285,8 @@ kv_status kv_check_block_table(const kv_alloc* a, const uint32_t* bt) {
     if (!a || !bt) return fail(KV_EINVAL, "NULL argument");
     const kv_geometry& g = a->g;
     for (int l = 0; l < g.num_layers; ++l) {
-        std::vector<std::vector<uint8_t>> used(3);
-        for (int t = 0; t < 3; ++t) used[t].assign(a->capacity[(size_t)l * 3 + t], 0);
+        std::vector<std::vector<uint8_t>> used(kTiers);
+        for (int t = 0; t < kTiers; ++t) used[t].assign(a->capacity[(size_t)l * kTiers + t], 0);
         for (int s = 0; s < g.max_seqs; ++s) {
             const uint32_t* row = bt + ((size_t)l * g.max_seqs + s) * g.max_pages_per_seq;
             const int64_t pages = (a->len[s] + g.page_size - 1) / g.page_size;
@@ -297,7 +299,7 @@ kv_status kv_check_block_table(const kv_alloc* a, const uint32_t* bt) {
                     continue;
                 }
                 const uint32_t t = h >> 30, i = h & 0x3fffffffu;
-                if (h == KV_NO_BLOCK || t > 2 || i >= a->capacity[(size_t)l * 3 + t])
+                if (h == KV_NO_BLOCK || t >= (uint32_t)kTiers || i >= a->capacity[(size_t)l * kTiers + t])
                     return fail(KV_EINVAL, "layer %d seq %d page %lld: invalid handle 0x%08x", l,
                                 s, (long long)p, h);
                 if (used[t][i]++)

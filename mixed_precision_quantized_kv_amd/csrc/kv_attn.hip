@@ -86,16 +86,28 @@ struct PageSrc {
     const uint8_t* base0;
     const uint8_t* base1;
     const uint8_t* base2;
+    const uint8_t* base3;     // FP16 tier
     const uint32_t* bt_row;   // this sequence's block-table row
     int H;
 };
+
+// pool base of a tier by arithmetic rather than a select chain, which the compiler would
+// otherwise turn into a lookup table in scratch memory
+__device__ __forceinline__ const uint8_t* tier_base(const PageSrc& a, int tier) {
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(a.base0);
+    return reinterpret_cast<const uint8_t*>(
+        b0 + (uintptr_t)(tier == 1) * (reinterpret_cast<uintptr_t>(a.base1) - b0) +
+        (uintptr_t)(tier == 2) * (reinterpret_cast<uintptr_t>(a.base2) - b0) +
+        (uintptr_t)(tier == 3) * (reinterpret_cast<uintptr_t>(a.base3) - b0));
+}
 
 // Loads of one page for this lane, width read from its handle. The instruction sequence is the
 // same for every tier (two 16-byte K loads, two 16-byte V loads, one scale dword, one scale pair):
 // the second 16 bytes are only needed by INT8, so INT2/INT4 re-read their first 16 bytes (same
 // cache lines, all inside the section). A fixed count lets the compiler wait for exactly one
 // page's loads while the next pairs' loads stay in flight. `page` must be a valid page index
-// even when `present` is false.
+// even when `present` is false. An FP16 page (bits 16) is read later, by its own path: here its
+// lane loads use INT2 offsets, which stay inside its (larger) section, and are not used.
 template <int D>
 __device__ __forceinline__ void load_page(const PageSrc& a, int kv, int page, bool present,
                                           int ctx, int lane, PageRaw& r) {
@@ -105,20 +117,16 @@ __device__ __forceinline__ void load_page(const PageSrc& a, int kv, int page, bo
     const int bits = bits_of_tier(tier);
     r.bits = present ? bits : 0;
     r.ntok = present ? min(kPage, ctx - page * kPage) : 0;
-    const uint32_t code_bytes = kPage * D * bits / 8;
-    const uint32_t sec_bytes = 2 * code_bytes + 2 * D + 2 * kPage;
-    // pool base by arithmetic rather than a select chain, which the compiler would otherwise
-    // turn into a lookup table in scratch memory
-    const uintptr_t b0 = reinterpret_cast<uintptr_t>(a.base0);
-    const uint8_t* base = reinterpret_cast<const uint8_t*>(
-        b0 + (uintptr_t)(tier == 1) * (reinterpret_cast<uintptr_t>(a.base1) - b0) +
-        (uintptr_t)(tier == 2) * (reinterpret_cast<uintptr_t>(a.base2) - b0));
-    const uint8_t* sec = base + ((size_t)idx * a.H + kv) * sec_bytes;
+    const bool f16 = tier == kFp16Tier;
+    const uint32_t sec_bytes = f16 ? 4u * kPage * D : kPage * D * bits / 4 + 2 * D + 2 * kPage;
+    const uint8_t* sec = tier_base(a, tier) + ((size_t)idx * a.H + kv) * sec_bytes;
+    const int lb = f16 ? 2 : bits;                  // the layout the lane offsets follow
+    const uint32_t code_bytes = kPage * D * lb / 8;
     const int t = lane & 15, G = lane >> 4;
-    const int ch = D * bits / 32;                   // bytes of one lane chunk
-    const uint8_t* kp = sec + t * (D * bits / 8) + G * ch;
-    const uint8_t* vp = sec + code_bytes + 2 * D + (G * D + t * (D / 16)) * bits / 2;
-    const int second = bits == 8 ? 16 : 0;
+    const int ch = D * lb / 32;                     // bytes of one lane chunk
+    const uint8_t* kp = sec + t * (D * lb / 8) + G * ch;
+    const uint8_t* vp = sec + code_bytes + 2 * D + (G * D + t * (D / 16)) * lb / 2;
+    const int second = lb == 8 ? 16 : 0;
     const uint4 k0 = *reinterpret_cast<const uint4*>(kp);
     const uint4 k1 = *reinterpret_cast<const uint4*>(kp + second);
     const uint4 v0 = *reinterpret_cast<const uint4*>(vp);
@@ -561,6 +569,186 @@ __device__ __forceinline__ void run_pair(const PageRaw& A, const PageRaw& B, con
         process_pair<D, BITS>(A, B, qf, lds_ks, lane, scale_log2, st);
 }
 
+
+// ---------------------------------------------------------------- FP16 tier
+// One FP16 page as this lane needs it: K of token lane%16 for channels [G*D/4, +D/4) (the order
+// of the query fragment) and V of token quad G for channels [(lane%16)*D/16, +D/16), four tokens
+// a channel -- the operand layouts of the INT paths, with fp16 values in place of codes.
+template <int D>
+struct PageF16 {
+    uint32_t k[D / 8];
+    uint32_t v[D / 8];
+};
+
+template <int D>
+__device__ __forceinline__ void load_page_f16(const uint8_t* sec, int lane, PageF16<D>& r) {
+    const int t = lane & 15, G = lane >> 4;
+    const uint4* kp = reinterpret_cast<const uint4*>(sec + t * 2 * D + G * (D / 2));
+    const uint4* vp = reinterpret_cast<const uint4*>(sec + 2 * kPage * D + (G * D + t * (D / 16)) * 8);
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+        const uint4 kk = kp[i], vv = vp[i];
+        r.k[4 * i] = kk.x; r.k[4 * i + 1] = kk.y; r.k[4 * i + 2] = kk.z; r.k[4 * i + 3] = kk.w;
+        r.v[4 * i] = vv.x; r.v[4 * i + 1] = vv.y; r.v[4 * i + 2] = vv.z; r.v[4 * i + 3] = vv.w;
+    }
+}
+
+// A pair of FP16 pages (B may be absent): the same QK, online softmax and PV as the INT pairs,
+// with the keys and values used as they are (each MFMA product of two fp16 values is exact in
+// fp32) and the softmax weights split into fp16 hi + lo. The INT pages accumulate o in units of
+// 2^-24 (their V codes enter as subnormals); SCALED brings o to plain units around this pair's
+// PV product and back, both exact power-of-two scalings. Without SCALED the caller keeps o in
+// plain units and converts it once.
+template <int D, bool HALF, bool SCALED>
+__device__ __forceinline__ void process_pair_f16(const PageF16<D>& A, const PageF16<D>& B,
+                                                 bool has_b, int ntok_a, int ntok_b,
+                                                 const uint32_t* qf, int lane, float scale_log2,
+                                                 WaveState<D>& st) {
+    const int G = lane >> 4;
+    float4v acca = {0.f, 0.f, 0.f, 0.f}, accb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+        const half8 qq = make_half8(qf[4 * i], qf[4 * i + 1], qf[4 * i + 2], qf[4 * i + 3]);
+        acca = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            make_half8(A.k[4 * i], A.k[4 * i + 1], A.k[4 * i + 2], A.k[4 * i + 3]), qq, acca, 0, 0, 0);
+        if (has_b)
+            accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                make_half8(B.k[4 * i], B.k[4 * i + 1], B.k[4 * i + 2], B.k[4 * i + 3]), qq, accb, 0, 0, 0);
+    }
+    const uint32_t one = 0x3C003C00u;                   // unit "V scales": weights are p itself
+    uint32_t wh[4], wl[4];
+    if constexpr (HALF) {
+        const bool side = (lane & 8) != 0;
+        const int ntok = side ? (has_b ? ntok_b : 0) : ntok_a;
+        float4v lg = (side ? accb : acca) * scale_log2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (4 * G + i >= ntok) lg[i] = -INFINITY;
+        float mx = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 8, 64));
+        mx = rows_max(mx);
+        const float m_new = fmaxf(st.m, mx);            // finite: page A holds >= 1 valid token
+        if (__builtin_amdgcn_ballot_w64(m_new != st.m)) {
+            const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+            st.l *= alpha;
+#pragma unroll
+            for (int k = 0; k < D / 16; ++k) st.o[k] *= alpha;
+            st.m = m_new;
+        }
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(lg[i] - m_new);
+        st.l += (p[0] + p[1]) + (p[2] + p[3]);
+        uint32_t h2[2], l2[2];
+        page_weights(one, one, ntok, p, G, h2, l2);
+        const uint32_t z = 0u;
+        wh[0] = side ? z : h2[0]; wh[1] = side ? z : h2[1]; wh[2] = side ? h2[0] : z; wh[3] = side ? h2[1] : z;
+        wl[0] = side ? z : l2[0]; wl[1] = side ? z : l2[1]; wl[2] = side ? l2[0] : z; wl[3] = side ? l2[1] : z;
+    } else {
+        float4v la = acca * scale_log2;
+        float4v lb = accb * scale_log2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (4 * G + i >= ntok_a) la[i] = -INFINITY;
+            if (!has_b || 4 * G + i >= ntok_b) lb[i] = -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(fmaxf(la[0], la[1]), fmaxf(la[2], la[3])),
+                         fmaxf(fmaxf(lb[0], lb[1]), fmaxf(lb[2], lb[3])));
+        mx = rows_max(mx);
+        const float m_new = fmaxf(st.m, mx);
+        if (__builtin_amdgcn_ballot_w64(m_new != st.m)) {
+            const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+            st.l *= alpha;
+#pragma unroll
+            for (int k = 0; k < D / 16; ++k) st.o[k] *= alpha;
+            st.m = m_new;
+        }
+        float pa[4], pb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pa[i] = __builtin_amdgcn_exp2f(la[i] - m_new);
+            pb[i] = __builtin_amdgcn_exp2f(lb[i] - m_new);
+        }
+        st.l += ((pa[0] + pa[1]) + (pa[2] + pa[3])) + ((pb[0] + pb[1]) + (pb[2] + pb[3]));
+        page_weights(one, one, ntok_a, pa, G, wh, wl);
+        page_weights(one, one, has_b ? ntok_b : 0, pb, G, wh + 2, wl + 2);
+    }
+    const half8 ph = make_half8(wh[0], wh[1], wh[2], wh[3]);
+    const half8 pl = make_half8(wl[0], wl[1], wl[2], wl[3]);
+    if constexpr (SCALED) {
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k) st.o[k] *= kTwo24;
+    }
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) {
+        const uint32_t vb0 = has_b ? B.v[2 * k] : 0u, vb1 = has_b ? B.v[2 * k + 1] : 0u;
+        const half8 vv = make_half8(A.v[2 * k], A.v[2 * k + 1], vb0, vb1);
+        st.o[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vv, ph, st.o[k], 0, 0, 0);
+        st.o[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vv, pl, st.o[k], 0, 0, 0);
+    }
+    if constexpr (SCALED) {
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k) st.o[k] *= 1.0f / kTwo24;
+    }
+}
+
+// A wave's chunk of FP16 pages, handles in `hv` (lane i: page cb + i). Pairs are loaded and
+// used in turn; o is kept in plain units and brought to the INT pages' 2^-24 units at the end
+// (a wave takes one chunk, so o starts at zero).
+template <int D, bool HALF>
+__device__ __forceinline__ void wave_chunk_f16(const uint8_t* base, uint32_t hv, int H, int kv,
+                                               int cb, int npg, int ctx, int lane,
+                                               const uint32_t* qf, float scale_log2,
+                                               WaveState<D>& st) {
+    constexpr uint32_t sec_bytes = 4u * kPage * D;
+    const int nq = (npg + 1) / 2;
+    for (int q = 0; q < nq; ++q) {
+        const int pa = 2 * q;
+        const bool has_b = pa + 1 < npg;
+        const uint32_t ia = (uint32_t)__builtin_amdgcn_readlane((int)hv, pa) & 0x3fffffffu;
+        const uint32_t ib =
+            (uint32_t)__builtin_amdgcn_readlane((int)hv, has_b ? pa + 1 : pa) & 0x3fffffffu;
+        PageF16<D> A, B;
+        load_page_f16<D>(base + ((size_t)ia * H + kv) * sec_bytes, lane, A);
+        load_page_f16<D>(base + ((size_t)ib * H + kv) * sec_bytes, lane, B);
+        const int page = cb + pa;
+        process_pair_f16<D, HALF, false>(A, B, has_b, min(kPage, ctx - page * kPage),
+                                         has_b ? min(kPage, ctx - (page + 1) * kPage) : 0, qf,
+                                         lane, scale_log2, st);
+    }
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) st.o[k] *= 1.0f / kTwo24;
+}
+
+// one pair of the general loop: pairs with an FP16 page go page by page, each FP16 page read
+// here from its section (its PageRaw holds only its width and token count)
+template <int D, bool HALF>
+__device__ __forceinline__ void run_pair_any(const PageSrc& src, int kv, int page, const PageRaw& A,
+                                             const PageRaw& B, const uint32_t* qf,
+                                             uint32_t* lds_ks, int lane, float scale_log2,
+                                             WaveState<D>& st) {
+    if (A.bits != 16 && B.bits != 16) {
+        run_pair<D, 0, HALF>(A, B, qf, lds_ks, lane, scale_log2, st);
+        return;
+    }
+    PageRaw none = A;
+    none.bits = 0;
+    none.ntok = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const PageRaw& X = j == 0 ? A : B;
+        if (X.bits == 16) {
+            const uint32_t handle = ((const_u32_ptr)src.bt_row)[page + j];
+            const uint8_t* sec = src.base3 + ((size_t)(handle & 0x3fffffffu) * src.H + kv) * (4u * kPage * D);
+            PageF16<D> F;
+            load_page_f16<D>(sec, lane, F);
+            process_pair_f16<D, HALF, true>(F, F, false, X.ntok, 0, qf, lane, scale_log2, st);
+        } else if (X.bits) {
+            run_pair<D, 0, HALF>(X, none, qf, lds_ks, lane, scale_log2, st);
+        }
+    }
+}
+
 template <int D, int BITS>
 __device__ __forceinline__ void load_pair_t(const uint8_t* base, uint32_t hv, int H, int kv, int cb,
                                             int npg, int q, int nq, int ctx, int lane, PageRaw& x,
@@ -617,10 +805,10 @@ __device__ __forceinline__ void wave_chunk_mixed(const PageSrc& src, int kv, int
     load_pair<D>(src, kv, cb, cb + npg, 0, nq, ctx, lane, a0, a1);
     while (true) {
         load_pair<D>(src, kv, cb, cb + npg, q + 1, nq, ctx, lane, b0, b1);
-        run_pair<D, 0, HALF>(a0, a1, qf, ks_slot, lane, scale_log2, st);
+        run_pair_any<D, HALF>(src, kv, cb + 2 * q, a0, a1, qf, ks_slot, lane, scale_log2, st);
         if (++q >= nq) break;
         load_pair<D>(src, kv, cb, cb + npg, q + 1, nq, ctx, lane, a0, a1);
-        run_pair<D, 0, HALF>(b0, b1, qf, ks_slot, lane, scale_log2, st);
+        run_pair_any<D, HALF>(src, kv, cb + 2 * q, b0, b1, qf, ks_slot, lane, scale_log2, st);
         if (++q >= nq) break;
     }
 }
@@ -734,9 +922,12 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
         else if (uniform && tier0 == 2)
             wave_chunk_uniform<D, 8, 2, HALF>(a.pools.base[2], hv, a.H, kv, cb, npg, ctx, lane, qf, ks_slot,
                                      a.scale_log2, st);
+        else if (uniform && tier0 == kFp16Tier)
+            wave_chunk_f16<D, HALF>(a.pools.base[3], hv, a.H, kv, cb, npg, ctx, lane, qf,
+                                    a.scale_log2, st);
         else {
             const PageSrc src = {a.pools.base[0], a.pools.base[1], a.pools.base[2],
-                                 bt_row, a.H};
+                                 a.pools.base[3], bt_row, a.H};
             wave_chunk_mixed<D, HALF>(src, kv, cb, npg, ctx, lane, qf, ks_slot, a.scale_log2, st);
         }
     }

@@ -21,17 +21,20 @@ struct Section {
     uint32_t bytes;        // whole section
 };
 
+// (b = 16, the FP16 tier: K values then V values, no scales)
 __host__ __device__ inline Section section_layout(int D, int bits) {
     Section s;
+    const uint32_t scales = bits == 16 ? 0u : 1u;
     s.code_bytes = (uint32_t)(kPage * D * bits / 8);
     s.kscale_off = s.code_bytes;
-    s.vcode_off = s.code_bytes + 2u * D;
-    s.vscale_off = 2u * s.code_bytes + 2u * D;
-    s.bytes = 2u * s.code_bytes + 2u * D + 2u * kPage;
+    s.vcode_off = s.code_bytes + scales * 2u * D;
+    s.vscale_off = 2u * s.code_bytes + scales * 2u * D;
+    s.bytes = 2u * s.code_bytes + scales * (2u * D + 2u * kPage);
     return s;
 }
 
-__host__ __device__ inline int bits_of_tier(int tier) { return 2 << tier; }  // 0,1,2 -> 2,4,8
+__host__ __device__ inline int bits_of_tier(int tier) { return 2 << tier; }  // 0..3 -> 2,4,8,16
+constexpr int kFp16Tier = 3;
 
 // bit position of code k (0 .. 32/b-1) inside its 32-bit word: even codes fill the low half,
 // odd codes the high half, each half low-first. A word thus unpacks into consecutive fp16 pairs

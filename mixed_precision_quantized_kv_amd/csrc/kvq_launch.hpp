@@ -10,7 +10,7 @@
 namespace kvq {
 
 struct PoolPtrs {
-    uint8_t* base[3];
+    uint8_t* base[KV_NUM_TIERS];   // INT2, INT4, INT8, FP16
 };
 
 hipError_t launch_quant_write(const kv_geometry& g, PoolPtrs pools, const uint32_t* bt,

@@ -4,7 +4,8 @@
 // EchoKV, "How EchoKV works": the step's key enters the per-layer FP16 ring before it is
 // quantized into the paged cache. Behavior-Guided KV-Cache Quantization, "K/V Role-Aware
 // Low-Bit Quantization": keys get one scale per channel (over the page's tokens), values one
-// scale per token (over its channels); "Online inference": pack and store.
+// scale per token (over its channels); "Online inference": pack and store. Pages of the FP16
+// tier (a layer before the canary first fires) take the new keys and values as they are.
 //
 // Thread (t, g) = (tid / 16, tid % 16) owns token slot t of the page and channels
 // [g*D/16, (g+1)*D/16): every input element is fetched by exactly one 8- or 16-byte load,
@@ -58,7 +59,8 @@ __device__ __forceinline__ uint8_t* pool_base(const PoolPtrs& pools, int tier) {
     const uintptr_t b0 = reinterpret_cast<uintptr_t>(pools.base[0]);
     return reinterpret_cast<uint8_t*>(
         b0 + (uintptr_t)(tier == 1) * (reinterpret_cast<uintptr_t>(pools.base[1]) - b0) +
-        (uintptr_t)(tier == 2) * (reinterpret_cast<uintptr_t>(pools.base[2]) - b0));
+        (uintptr_t)(tier == 2) * (reinterpret_cast<uintptr_t>(pools.base[2]) - b0) +
+        (uintptr_t)(tier == 3) * (reinterpret_cast<uintptr_t>(pools.base[3]) - b0));
 }
 
 // Write page p0/P + j of sequence s, KV head kv, for the call's new tokens [p0, p0 + n_new):
@@ -102,6 +104,7 @@ __device__ __forceinline__ void write_page(const WriteArgs& a, int s, int kv, in
     if (active) handle = a.bt[(size_t)s * a.max_pages + page];
     const int tier = (int)(handle >> 30);
     const int bits = bits_of_tier(tier);
+    const bool fp16 = tier == kFp16Tier;
     const Section L = section_layout(D, bits);
     uint8_t* sec = pool_base(a.pools, tier) + ((size_t)(handle & 0x3fffffffu) * a.H + kv) * L.bytes;
     const uint32_t qoff = 1u << (bits - 1);
@@ -113,7 +116,7 @@ __device__ __forceinline__ void write_page(const WriteArgs& a, int s, int kv, in
     // words w of its channel group with w % 4 == r. A quad seen for the first time is written
     // whole (its empty slots get the zero code); a quad that already holds tokens is read,
     // merged with the new fields and written back (its other fields are kept).
-    const int cw = 8 / bits;                    // channels per V word
+    const int cw = fp16 ? 1 : 8 / bits;         // channels per V word (FP16: unused)
     const int nwv = CPT / cw;                   // V words per (quad, channel group): 1..8
     const int quad = t >> 2, r = t & 3;
     const bool quad_old = 4 * quad < told;      // the quad holds tokens cached before the call
@@ -122,7 +125,7 @@ __device__ __forceinline__ void write_page(const WriteArgs& a, int s, int kv, in
     uint32_t* vwords = reinterpret_cast<uint32_t*>(sec + L.vcode_off);
     const int wbase = ((quad * D + c0) * 4) / (32 / bits);  // first V word of this (quad, group)
     uint32_t vold[2] = {0u, 0u};                // at most 8 words / 4 lanes
-    if (quad_store && quad_old) {
+    if (quad_store && quad_old && !fp16) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int w = r + 4 * i;
@@ -144,6 +147,26 @@ __device__ __forceinline__ void write_page(const WriteArgs& a, int s, int kv, in
     }
     __syncthreads();
     if (!active) return;
+    if (fp16) {
+        // FP16 tier: the new tokens' keys and values as they are, zeros in the empty slots; the
+        // slots of tokens cached before the call are not touched
+        if (t >= told) {
+            uint16_t kb[CPT], vb[CPT];
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                kb[i] = present ? f16_bits((_Float16)kf[i]) : (uint16_t)0;
+                vb[i] = is_new ? f16_bits((_Float16)vf[i]) : (uint16_t)0;
+            }
+            uint16_t* krow = reinterpret_cast<uint16_t*>(sec) + (size_t)t * D + c0;
+#pragma unroll
+            for (int i = 0; i < CPT; i += 2)
+                reinterpret_cast<uint32_t*>(krow)[i / 2] = kb[i] | ((uint32_t)kb[i + 1] << 16);
+            uint16_t* vvals = reinterpret_cast<uint16_t*>(sec + L.vcode_off);
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) vvals[((size_t)(quad * D + c0 + i)) * 4 + r] = vb[i];
+        }
+        return;
+    }
     uint16_t ks[CPT];
     uint32_t ku[CPT];
 #pragma unroll

@@ -155,7 +155,7 @@ def handle(tier: int, index: int) -> int:
     return (int(tier) << 30) | int(index)
 
 
-TIER_OF_BITS = {2: 0, 4: 1, 8: 2}
+TIER_OF_BITS = {2: 0, 4: 1, 8: 2, 16: 3}
 NO_BLOCK = 0xFFFFFFFF
 
 
@@ -166,7 +166,7 @@ def block_table(page_tiers: Sequence[Sequence[int]], max_pages: int, capacity: S
     Each tier pool hands out its blocks in a seeded random order; returns [B][max_pages] uint32.
     """
     order = [list(g.permutation(int(c))) for c in capacity]
-    nxt = [0, 0, 0]
+    nxt = [0] * len(capacity)
     bt = np.full((len(page_tiers), max_pages), NO_BLOCK, dtype=np.uint32)
     for s, tiers in enumerate(page_tiers):
         for i, t in enumerate(tiers):

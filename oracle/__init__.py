@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvq_oracle.c")
 LIB_PATH = os.path.join(_HERE, "libkvq_oracle.so")
 
-TIER_BITS = (2, 4, 8)
+TIER_BITS = (2, 4, 8, 16)
 
 
 def build(verbose: bool = False) -> str:
@@ -92,12 +92,14 @@ def geom(num_q_heads, num_kv_heads, head_dim, page_size=16, ring_size=64) -> Geo
 
 
 class Pools:
-    """Host byte arrays for the three tier pools of one layer."""
+    """Host byte arrays for the four tier pools of one layer (INT2, INT4, INT8, FP16); a
+    capacity list of three leaves the FP16 pool empty."""
 
     def __init__(self, g: Geom, capacity):
-        self.arrays = [np.zeros(int(capacity[t]) * block_bytes(g, TIER_BITS[t]), dtype=np.uint8)
-                       for t in range(3)]
-        self._ptrs = (ctypes.c_void_p * 3)(*[a.ctypes.data for a in self.arrays])
+        cap = [int(c) for c in capacity] + [0] * (4 - len(capacity))
+        self.arrays = [np.zeros(max(1, cap[t] * block_bytes(g, TIER_BITS[t])), dtype=np.uint8)
+                       for t in range(4)]
+        self._ptrs = (ctypes.c_void_p * 4)(*[a.ctypes.data for a in self.arrays])
 
     @property
     def ptr(self):

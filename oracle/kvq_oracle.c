@@ -161,12 +161,15 @@ void orc_unpack(const uint8_t* in, int n, int bits, int* q) {
 /* ------------------------------------------------------------------------------------------ */
 /* Layout                                                                                       */
 
-int orc_bits_of_tier(int tier) { return tier == 0 ? 2 : tier == 1 ? 4 : tier == 2 ? 8 : 0; }
+int orc_bits_of_tier(int tier) {
+    return tier == 0 ? 2 : tier == 1 ? 4 : tier == 2 ? 8 : tier == 3 ? 16 : 0;
+}
 
 static size_t code_bytes(const orc_geom* g, int bits) {
     return (size_t)g->page_size * g->head_dim * bits / 8;
 }
 size_t orc_section_bytes(const orc_geom* g, int bits) {
+    if (bits == 16) return 2 * code_bytes(g, bits);       /* FP16 keys and values, no scales */
     return 2 * code_bytes(g, bits) + 2 * (size_t)g->head_dim + 2 * (size_t)g->page_size;
 }
 size_t orc_block_bytes(const orc_geom* g, int bits) {
@@ -174,6 +177,7 @@ size_t orc_block_bytes(const orc_geom* g, int bits) {
 }
 static size_t off_kscale(const orc_geom* g, int bits) { return code_bytes(g, bits); }
 static size_t off_vcodes(const orc_geom* g, int bits) {
+    if (bits == 16) return code_bytes(g, bits);
     return code_bytes(g, bits) + 2 * (size_t)g->head_dim;
 }
 static size_t off_vscale(const orc_geom* g, int bits) {
@@ -199,7 +203,7 @@ double orc_v_scale(const orc_geom* g, const uint8_t* sec, int bits, int t) {
 }
 
 /* the section of (handle, kv head), or NULL for an invalid handle */
-static uint8_t* section_of(const orc_geom* g, uint8_t* const pools[3], uint32_t handle, int kv,
+static uint8_t* section_of(const orc_geom* g, uint8_t* const pools[4], uint32_t handle, int kv,
                            int* bits_out) {
     if (handle == 0xffffffffu) return NULL;
     int tier = (int)(handle >> 30);
@@ -218,7 +222,7 @@ static uint8_t* section_of(const orc_geom* g, uint8_t* const pools[3], uint32_t 
 /* keys), new positions come from k_new.  Each new value vector is quantized over its D         */
 /* channels into its token slot.  Then the new keys enter the ring.                             */
 
-int orc_quant_write(const orc_geom* g, uint8_t* const pools[3], const uint32_t* bt, int max_pages,
+int orc_quant_write(const orc_geom* g, uint8_t* const pools[4], const uint32_t* bt, int max_pages,
                     const int32_t* pos, int batch, int n_new,
                     const uint16_t* k_new, const uint16_t* v_new, uint16_t* ring) {
     const int P = g->page_size, D = g->head_dim, H = g->num_kv_heads, R = g->ring_size;
@@ -241,6 +245,21 @@ int orc_quant_write(const orc_geom* g, uint8_t* const pools[3], const uint32_t* 
                 int bits = 0;
                 uint8_t* sec = section_of(g, pools, bt[(size_t)s * max_pages + page], kv, &bits);
                 if (!sec) { status = -1; break; }
+                if (bits == 16) {
+                    /* FP16 tier: new tokens' keys and values stored as they are, empty slots +0,
+                       tokens cached before untouched */
+                    for (int t = 0; t < P; ++t) {
+                        const int p = lo + t;
+                        if (p < p0) continue;
+                        for (int c = 0; c < D; ++c) {
+                            const uint16_t kb = p < hi ? kn[((size_t)(p - p0) * H + kv) * D + c] : 0;
+                            const uint16_t vb = p < hi ? vn[((size_t)(p - p0) * H + kv) * D + c] : 0;
+                            wr16(sec + 2 * (size_t)k_index(g, t, c), kb);
+                            wr16(sec + off_vcodes(g, bits) + 2 * (size_t)v_index(g, t, c), vb);
+                        }
+                    }
+                    continue;
+                }
                 /* gather the page's present keys [lo, hi) */
                 for (int p = lo; p < hi; ++p)
                     for (int c = 0; c < D; ++c)
@@ -290,7 +309,7 @@ int orc_quant_write(const orc_geom* g, uint8_t* const pools[3], const uint32_t* 
 /* ------------------------------------------------------------------------------------------ */
 /* Dequantized cache: K^_t[c] = code * s_K(page(t), c),  V^_t[c] = code * s_V(t); exact doubles. */
 
-int orc_dequant_kv(const orc_geom* g, uint8_t* const pools[3], const uint32_t* bt_row, int n,
+int orc_dequant_kv(const orc_geom* g, uint8_t* const pools[4], const uint32_t* bt_row, int n,
                    int kv, double* K, double* V) {
     const int P = g->page_size, D = g->head_dim;
     for (int t = 0; t < n; ++t) {
@@ -298,6 +317,14 @@ int orc_dequant_kv(const orc_geom* g, uint8_t* const pools[3], const uint32_t* b
         const uint8_t* sec = section_of(g, pools, bt_row[t / P], kv, &bits);
         if (!sec) return -1;
         const int slot = t % P;
+        if (bits == 16) {                                /* FP16 tier: the values themselves */
+            for (int c = 0; c < D; ++c) {
+                K[(size_t)t * D + c] = orc_f16_to_f64(rd16(sec + 2 * (size_t)k_index(g, slot, c)));
+                V[(size_t)t * D + c] =
+                    orc_f16_to_f64(rd16(sec + off_vcodes(g, bits) + 2 * (size_t)v_index(g, slot, c)));
+            }
+            continue;
+        }
         const double sv = orc_v_scale(g, sec, bits, slot);
         for (int c = 0; c < D; ++c) {
             K[(size_t)t * D + c] = orc_k_code(g, sec, bits, slot, c) * orc_k_scale(g, sec, bits, c);
@@ -328,7 +355,7 @@ static void attend(const double* qd, const double* K, const double* V, int n, in
     for (int c = 0; c < D; ++c) out[c] /= sum;
 }
 
-int orc_decode_attn_row(const orc_geom* g, uint8_t* const pools[3], const uint32_t* bt_row,
+int orc_decode_attn_row(const orc_geom* g, uint8_t* const pools[4], const uint32_t* bt_row,
                         int ctx_len, const uint16_t* q_row, int h, float softmax_scale,
                         double* out) {
     const int D = g->head_dim, grp = g->num_q_heads / g->num_kv_heads;
@@ -346,7 +373,7 @@ int orc_decode_attn_row(const orc_geom* g, uint8_t* const pools[3], const uint32
     return rc;
 }
 
-int orc_decode_attn(const orc_geom* g, uint8_t* const pools[3], const uint32_t* bt, int max_pages,
+int orc_decode_attn(const orc_geom* g, uint8_t* const pools[4], const uint32_t* bt, int max_pages,
                     const int32_t* ctx_len, int batch, const uint16_t* q, float softmax_scale,
                     double* out) {
     const int D = g->head_dim, Hq = g->num_q_heads, H = g->num_kv_heads, grp = Hq / H;

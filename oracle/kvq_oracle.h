@@ -37,6 +37,9 @@
  *   A code sequence is stored as 32-bit little-endian words of 32/b codes; code k of a word
  *   (k = i mod 32/b) is the unsigned field u = q + 2^(b-1) at bit 16*(k%2) + b*(k/2).
  *   Token slots of a page that hold no token yet carry the zero code and a zero scale.
+ *   tier 3 <-> b = 16, plain FP16 (EchoKV, "How EchoKV works": a layer's initial state before
+ *   the canary first fires): a section is 4*P*D bytes, the keys at index t*D + c then the values
+ *   at index ((t/4)*D + c)*4 + t%4, fp16 each, no scales; empty slots are +0.
  */
 #ifndef KVQ_ORACLE_H
 #define KVQ_ORACLE_H
@@ -85,23 +88,23 @@ double orc_k_scale(const orc_geom* g, const uint8_t* sec, int bits, int c);
 double orc_v_scale(const orc_geom* g, const uint8_t* sec, int bits, int t);
 
 /* ---- quantize-on-write: one layer, `batch` sequences, n_new tokens each ----
- * pools[tier]: host copies of the tier pools; bt: [batch][max_pages] handles;
+ * pools[tier]: host copies of the four tier pools (INT2, INT4, INT8, FP16); bt: [batch][max_pages] handles;
  * pos[s]: tokens already cached; k_new, v_new: [batch][n_new][H_kv][D] fp16 bits;
  * ring: [batch][R][H_kv][D] fp16 bits, updated in place.  Returns 0, or -1 on a bad handle. */
-int orc_quant_write(const orc_geom* g, uint8_t* const pools[3], const uint32_t* bt, int max_pages,
+int orc_quant_write(const orc_geom* g, uint8_t* const pools[4], const uint32_t* bt, int max_pages,
                     const int32_t* pos, int batch, int n_new,
                     const uint16_t* k_new, const uint16_t* v_new, uint16_t* ring);
 
 /* ---- dequantized cache of one (sequence, kv head): K, V as [n][D] doubles ---- */
-int orc_dequant_kv(const orc_geom* g, uint8_t* const pools[3], const uint32_t* bt_row, int n,
+int orc_dequant_kv(const orc_geom* g, uint8_t* const pools[4], const uint32_t* bt_row, int n,
                    int kv, double* K, double* V);
 
 /* ---- decode attention: out [batch][H_q][D] in double ---- */
-int orc_decode_attn(const orc_geom* g, uint8_t* const pools[3], const uint32_t* bt, int max_pages,
+int orc_decode_attn(const orc_geom* g, uint8_t* const pools[4], const uint32_t* bt, int max_pages,
                     const int32_t* ctx_len, int batch, const uint16_t* q, float softmax_scale,
                     double* out);
 /* one output row (sequence s, query head h); bt_row = that sequence's block table */
-int orc_decode_attn_row(const orc_geom* g, uint8_t* const pools[3], const uint32_t* bt_row,
+int orc_decode_attn_row(const orc_geom* g, uint8_t* const pools[4], const uint32_t* bt_row,
                         int ctx_len, const uint16_t* q_row, int h, float softmax_scale, double* out);
 
 /* ---- canary: kl3[b] = mean over batch*H_q rows of KL(P_ref || P_b), b = 2,4,8;

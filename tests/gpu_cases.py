@@ -38,7 +38,7 @@ class LayerPair:
         self.g = kvq.geometry(1, hq, hkv, d, batch, max_pages, ring_size=R)
         self.og = oracle.geom(hq, hkv, d, 16, R)
         if capacity is None:
-            capacity = [max(1, sum(t == tier for row in page_tiers for t in row)) for tier in range(3)]
+            capacity = [max(1, sum(t == tier for row in page_tiers for t in row)) for tier in range(4)]
         self.capacity = list(capacity)
         self.bt = synth.block_table(page_tiers, max_pages, self.capacity,
                                     np.random.default_rng(seed + 1000))

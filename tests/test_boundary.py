@@ -32,7 +32,7 @@ def test_exports_every_header_symbol():
     L = kvq.lib()
     for n in names:
         assert getattr(L, n) is not None
-    assert kvq.kv_abi_version() == 1
+    assert kvq.kv_abi_version() == 2                  # four tier pools (FP16 added)
 
 
 def geom(**kw):
@@ -60,21 +60,25 @@ def test_geometry_validation(kw, status):
 
 def test_sizes_match_format():
     g = geom(head_dim=128, num_q_heads=40, num_kv_heads=8)
-    # S_b = P*D*b/4 + 2D + 2P per KV head
+    # S_b = P*D*b/4 + 2D + 2P per KV head; the FP16 tier 4*P*D (keys and values, no scales)
     assert [kvq.kv_block_bytes(g, b) for b in (2, 4, 8)] == [8 * 1312, 8 * 2336, 8 * 4384]
+    assert kvq.kv_block_bytes(g, 16) == 8 * 4 * 16 * 128
     assert kvq.kv_block_bytes(g, 3) == 0
     assert kvq.kv_ring_bytes(g) == 4 * 64 * 8 * 128 * 2
     assert kvq.kv_cache_bytes_per_token(g, [16, 16]) == 2 * 2 * 8 * 128 * 2
     assert kvq.kv_cache_bytes_per_token(g, [2, 8]) == 8 * (82 + 274)
     assert kvq.kv_handle(4, 7) == (1 << 30) | 7
     assert kvq.kv_handle(3, 7) == kvq.KV_NO_BLOCK
+    assert kvq.kv_handle(16, 7) == (3 << 30) | 7
+    # a layer at FP16 costs what the page's FP16 accounting says: 2 (K, V) * H_kv * D * 2 bytes
+    assert kvq.kv_cache_bytes_per_token(g, [16, 16]) == 2 * kvq.kv_block_bytes(g, 16) / 16
 
 
 def test_sizes_agree_with_oracle(orc):
     for hq, hkv, d in ((8, 2, 64), (40, 8, 128), (28, 4, 128)):
         g = geom(num_q_heads=hq, num_kv_heads=hkv, head_dim=d)
         og = orc.geom(hq, hkv, d)
-        for b in (2, 4, 8):
+        for b in (2, 4, 8, 16):
             assert kvq.kv_block_bytes(g, b) == orc.block_bytes(og, b)
         bits = [2, 16]
         assert kvq.kv_cache_bytes_per_token(g, bits) == orc.cache_bytes_per_token(og, bits)
@@ -131,6 +135,27 @@ def test_extend_assigns_current_tier_and_checks():
         assert np.all(row[3:] == kvq.KV_NO_BLOCK)
         assert a.kv_alloc_free_blocks(l, b) == 13
     a.kv_check_block_table()
+
+
+def test_fp16_layers_start_in_their_own_pool():
+    g = geom(num_layers=2)
+    capacity = np.full((2, 4), 8, dtype=np.uint32)          # INT2, INT4, INT8, FP16 pools
+    a = kvq.KVAlloc(g, capacity, [16, 8], 3)
+    a.kv_alloc_extend(0, 20)                                 # two pages per layer
+    assert [int(h) >> 30 for h in a.bt[0, 0, :2]] == [3, 3]
+    assert [int(h) >> 30 for h in a.bt[1, 0, :2]] == [2, 2]
+    assert a.kv_alloc_free_blocks(0, 16) == 6
+    a.kv_alloc_set_layer_bits(0, 4)                          # the canary has fired
+    a.kv_alloc_extend(0, 50)
+    assert [int(h) >> 30 for h in a.bt[0, 0, :4]] == [3, 3, 1, 1]
+    a.kv_check_block_table()
+    a.kv_alloc_free_seq(0)
+    assert a.kv_alloc_free_blocks(0, 16) == 8 and a.kv_alloc_free_blocks(0, 4) == 8
+    # [L][3] capacities (no FP16 pool): an FP16 layer has no blocks to give
+    b = make_alloc(bits=(16, 4))
+    with pytest.raises(kvq.KVError) as e:
+        b.kv_alloc_extend(0, 1)
+    assert e.value.status == kvq.KV_ENOBLOCKS
 
 
 def test_tier_switch_is_forward_only():

@@ -99,10 +99,7 @@ def test_apply_routes_later_blocks_only():
     with pytest.raises(kvq.KVError):
         c3.kv_controller_apply(alloc)
     assert [alloc.kv_alloc_layer_bits(l) for l in range(L)] == [2, 4]
-    # a layer still at its initial width may hold one the allocator has no pool for: refused,
-    # all-or-nothing
-    c_odd = kvq.KVController([4, 16])
-    if kvq.kv_block_bytes(g, 16) == 0:
-        with pytest.raises(kvq.KVError):
-            c_odd.kv_controller_apply(alloc)
-        assert [alloc.kv_alloc_layer_bits(l) for l in range(L)] == [2, 4]
+    # a layer still at its initial FP16 width routes to the FP16 pool
+    c16 = kvq.KVController([4, 16])
+    c16.kv_controller_apply(alloc)
+    assert [alloc.kv_alloc_layer_bits(l) for l in range(L)] == [4, 16]

@@ -35,8 +35,8 @@ def test_controller_loop():
     alloc = kvq.KVAlloc(g, cap, [8] * L, shuffle_seed=99)
     pools_t, pools, rings, opools, orings = [], [], [], [], []
     for l in range(L):
-        pt = [torch.zeros(int(cap[l, t]) * kvq.kv_block_bytes(g, b), dtype=torch.uint8, device=DEV)
-              for t, b in enumerate(kvq.TIER_BITS)]
+        pt = [torch.zeros(int(cap[l, t]) * kvq.kv_block_bytes(g, kvq.TIER_BITS[t]), dtype=torch.uint8,
+                          device=DEV) for t in range(cap.shape[1])]
         pools_t.append(pt)
         pools.append(kvq.layer_pools(pt, cap[l]))
         rings.append(torch.zeros((B, R, HKV, D), dtype=torch.float16, device=DEV))
