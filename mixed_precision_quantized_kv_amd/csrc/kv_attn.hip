@@ -36,6 +36,9 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
 
 // read-only tables indexed by wave-uniform values: the constant address space lets the compiler
 // use scalar loads, so block-table lookups never wait on the vector-memory counter
@@ -266,6 +269,28 @@ __device__ __forceinline__ half8 make_half8(uint32_t a, uint32_t b, uint32_t c, 
 __device__ __forceinline__ float rows_max(float x) {
     x = fmaxf(x, __shfl_xor(x, 16, 64));
     return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+// max / sum over all 64 lanes: within each row of 16 by DPP (quad swaps, then rotations by 4
+// and 8), across the rows by two shuffles
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_max_dpp(float x) {
+    x = fmaxf(x, dpp_mov<0xB1>(x));      // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp_mov<0x4E>(x));      // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp_mov<0x124>(x));     // row_ror:4
+    x = fmaxf(x, dpp_mov<0x128>(x));     // row_ror:8
+    x = fmaxf(x, __shfl_xor(x, 16, 64));
+    return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+    x += dpp_mov<0xB1>(x);
+    x += dpp_mov<0x4E>(x);
+    x += dpp_mov<0x124>(x);
+    x += dpp_mov<0x128>(x);
+    x += __shfl_xor(x, 16, 64);
+    return x + __shfl_xor(x, 32, 64);
 }
 __device__ __forceinline__ float rows_sum(float x) {
     x += __shfl_xor(x, 16, 64);
@@ -813,6 +838,337 @@ __device__ __forceinline__ void wave_chunk_mixed(const PageSrc& src, int kv, int
     }
 }
 
+// ---------------------------------------------------------------- uniform-width fast path
+// A wave's chunk of pages of one width, for groups of at most 8 query heads, in rounds of RP
+// page pairs. The loads of round r+1 are in flight while round r is computed; inside a round
+// every QK product comes first, then one update of the running maxima, then every PV product,
+// so the MFMA chains of one pair overlap the unpacking of the next and no branch splits the
+// round. As in process_pair_half, lanes with h = lane % 16 < 8 own page A of a pair for head h,
+// lanes h >= 8 page B for head h - 8. The PV product instead puts the two fp16 parts of the
+// weights in the two column halves -- columns 0..7 the high parts of heads 0..7 over both
+// pages' tokens, columns 8..15 the low parts -- so one MFMA per channel chunk covers a pair;
+// the halves fold at the end exactly as the page halves of process_pair_half do.
+//
+// The running maximum is lazy: the reference m sits kLazy (log2 units) above the largest logit
+// seen when it was last raised, so every weight is at most 2^-kLazy <= 1 and the accumulators
+// are rescaled only when a logit exceeds m -- in practice once per chunk.
+constexpr float kLazy = 3.0f;
+#ifndef KVQ_RP2
+#define KVQ_RP2 1
+#endif
+#ifndef KVQ_RP4
+#define KVQ_RP4 1
+#endif
+#ifndef KVQ_RP8
+#define KVQ_RP8 1
+#endif
+constexpr int kRoundPairs2 = KVQ_RP2;   // page pairs per round, by width
+constexpr int kRoundPairs4 = KVQ_RP4;
+constexpr int kRoundPairs8 = KVQ_RP8;
+
+template <int D, int BITS>
+struct FastPair {
+    static constexpr int KW = D * BITS / 128;    // dwords of this lane's K chunk and V chunk
+    uint32_t ka[KW], kb[KW], va[KW], vb[KW];
+    uint32_t ksa, ksb;                           // K-scale dwords (channels 2*lane, 2*lane+1)
+    uint32_t vs0, vs1;                           // V scales, quad G of this lane's side page
+    int ntok_a, ntok_b;                          // valid tokens; 0 for an absent page
+};
+
+template <int KW>
+__device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* w) {
+    if constexpr (KW == 1) {
+        w[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else if constexpr (KW == 2) {
+        const uint2 x = *reinterpret_cast<const uint2*>(p);
+        w[0] = x.x; w[1] = x.y;
+    } else {
+#pragma unroll
+        for (int h = 0; h < KW / 4; ++h) {
+            const uint4 x = *reinterpret_cast<const uint4*>(p + 16 * h);
+            w[4 * h] = x.x; w[4 * h + 1] = x.y; w[4 * h + 2] = x.z; w[4 * h + 3] = x.w;
+        }
+    }
+}
+
+// this lane's byte offsets inside a section
+struct LaneOffsets {
+    uint32_t k, v, ks, vs;
+};
+
+template <int D, int BITS>
+__device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
+    constexpr uint32_t code_bytes = kPage * D * BITS / 8;
+    const int t = lane & 15, G = lane >> 4;
+    LaneOffsets o;
+    o.k = t * (D * BITS / 8) + G * (D * BITS / 32);
+    o.v = code_bytes + 2 * D + (G * D + t * (D / 16)) * BITS / 2;
+    o.ks = code_bytes + 4 * (lane & (D / 2 - 1));
+    o.vs = 2 * code_bytes + 2 * D + 8 * G;
+    return o;
+}
+
+// pair q of a chunk whose handles sit in hv (lane i: page cb + i); pairs past the end reload
+// the last pair and carry no tokens
+template <int D, int BITS>
+__device__ __forceinline__ void load_pair_fast(const uint8_t* base, uint32_t hv, int H, int kv,
+                                               int cb, int npg, int q, int nq, int ctx,
+                                               const LaneOffsets& lo, bool side,
+                                               FastPair<D, BITS>& P) {
+    constexpr uint32_t sec_bytes = 2 * (kPage * D * BITS / 8) + 2 * D + 2 * kPage;
+    constexpr int KW = FastPair<D, BITS>::KW;
+    const bool real = q < nq;
+    const int pa = 2 * min(q, nq - 1);
+    const bool has_b = pa + 1 < npg;
+    const uint32_t ia = (uint32_t)__builtin_amdgcn_readlane((int)hv, pa) & 0x3fffffffu;
+    const uint32_t ib = (uint32_t)__builtin_amdgcn_readlane((int)hv, has_b ? pa + 1 : pa) & 0x3fffffffu;
+    const uint8_t* sa = base + ((size_t)ia * H + kv) * sec_bytes;
+    const uint8_t* sb = base + ((size_t)ib * H + kv) * sec_bytes;
+    load_words<KW>(sa + lo.k, P.ka);
+    load_words<KW>(sb + lo.k, P.kb);
+    load_words<KW>(sa + lo.v, P.va);
+    load_words<KW>(sb + lo.v, P.vb);
+    P.ksa = *reinterpret_cast<const uint32_t*>(sa + lo.ks);
+    P.ksb = *reinterpret_cast<const uint32_t*>(sb + lo.ks);
+    const uint2 vs = *reinterpret_cast<const uint2*>((side ? sb : sa) + lo.vs);
+    P.vs0 = vs.x;
+    P.vs1 = vs.y;
+    const int page = cb + pa;
+    P.ntok_a = real ? min(kPage, ctx - page * kPage) : 0;
+    P.ntok_b = real && has_b ? min(kPage, ctx - (page + 1) * kPage) : 0;
+}
+
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t bits) {
+    return (w & mask) | bits;
+}
+
+__device__ __forceinline__ uint32_t hfma(uint32_t x, float mul, float add) {
+    const half2v m = {(_Float16)mul, (_Float16)mul};
+    const half2v c = {(_Float16)add, (_Float16)add};
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(half2v, x), m, c));
+}
+
+// K chunk -> D/8 dwords of signed fp16 code pairs in code order. A field f of a 16-bit half
+// sitting at bit 2^k inside the low ten bits is turned into the fp16 value 1024 + 2^k * f by one
+// AND-OR with the exponent bits of 1024; one exact fused multiply-add, x * 2^-k - (1024 * 2^-k
+// + 2^(b-1)), then gives the signed code. Fields above bit 9 are shifted down by 8 first.
+template <int D, int BITS>
+__device__ __forceinline__ void unpack_k_fast(const uint32_t* w, uint32_t* out) {
+    // the exponent bits of 1024 in a VGPR: gfx9 VOP3 instructions take no literals, so with a
+    // register operand the AND-OR is one v_and_or_b32 (mask from an SGPR) instead of two ops
+    uint32_t E;
+    asm("v_mov_b32 %0, 0x64006400" : "=v"(E));
+    if constexpr (BITS == 2) {
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) {
+            const uint32_t s = w[i] >> 8;
+            out[8 * i + 0] = hsub(and_or(w[i], 0x00030003u, E), 1026.0f);
+            out[8 * i + 1] = hfma(and_or(w[i], 0x000C000Cu, E), 0.25f, -258.0f);
+            out[8 * i + 2] = hfma(and_or(w[i], 0x00300030u, E), 0.0625f, -66.0f);
+            out[8 * i + 3] = hfma(and_or(w[i], 0x00C000C0u, E), 0.015625f, -18.0f);
+            out[8 * i + 4] = hfma(and_or(w[i], 0x03000300u, E), 0.00390625f, -6.0f);
+            out[8 * i + 5] = hfma(and_or(s, 0x000C000Cu, E), 0.25f, -258.0f);
+            out[8 * i + 6] = hfma(and_or(s, 0x00300030u, E), 0.0625f, -66.0f);
+            out[8 * i + 7] = hfma(and_or(s, 0x00C000C0u, E), 0.015625f, -18.0f);
+        }
+    } else if constexpr (BITS == 4) {
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) {
+            const uint32_t s = w[i] >> 8;
+            out[4 * i + 0] = hsub(and_or(w[i], 0x000F000Fu, E), 1032.0f);
+            out[4 * i + 1] = hfma(and_or(w[i], 0x00F000F0u, E), 0.0625f, -72.0f);
+            out[4 * i + 2] = hsub(and_or(s, 0x000F000Fu, E), 1032.0f);
+            out[4 * i + 3] = hfma(and_or(s, 0x00F000F0u, E), 0.0625f, -72.0f);
+        }
+    } else {
+        unpack_k<D>(w, 8, out);
+    }
+}
+
+__device__ __forceinline__ uint32_t dpp_ror8(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xf, 0xf, false);
+}
+
+// the K scales of page slot `slot` of the round staged in LDS: D/8 dwords of channel group G
+template <int D>
+__device__ __forceinline__ void read_kscales(const uint32_t* ks_lds, int slot, int G, uint32_t* ks) {
+    const uint32_t* src = ks_lds + slot * 64 + G * (D / 8);
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src + 4 * i);
+        ks[4 * i] = v.x; ks[4 * i + 1] = v.y; ks[4 * i + 2] = v.z; ks[4 * i + 3] = v.w;
+    }
+}
+
+// S^T of one pair for this lane's side (tokens 4G..4G+3 of its page, head h % 8), log2 units
+template <int D, int BITS>
+__device__ __forceinline__ float4v pair_logits(const FastPair<D, BITS>& P, int j, const uint32_t* qf,
+                                               const uint32_t* ks_lds, int lane, bool side,
+                                               float scale_log2) {
+    const int G = lane >> 4;
+    float4v acca = {0.f, 0.f, 0.f, 0.f}, accb = {0.f, 0.f, 0.f, 0.f};
+    uint32_t kfa[D / 8], kfb[D / 8];
+    unpack_k_fast<D, BITS>(P.ka, kfa);
+    unpack_k_fast<D, BITS>(P.kb, kfb);
+    if constexpr (BITS == 2) {
+        // codes -1, 0, 1: code * scale is exact in fp16, so the scales fold into the keys
+        uint32_t ksa[D / 8], ksb[D / 8];
+        read_kscales<D>(ks_lds, 2 * j, G, ksa);
+        read_kscales<D>(ks_lds, 2 * j + 1, G, ksb);
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) {
+            kfa[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, kfa[i]) * __builtin_bit_cast(half2v, ksa[i]));
+            kfb[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, kfb[i]) * __builtin_bit_cast(half2v, ksb[i]));
+        }
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) {
+            const half8 qq = make_half8(qf[4 * i], qf[4 * i + 1], qf[4 * i + 2], qf[4 * i + 3]);
+            acca = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                make_half8(kfa[4 * i], kfa[4 * i + 1], kfa[4 * i + 2], kfa[4 * i + 3]), qq, acca, 0, 0, 0);
+            accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                make_half8(kfb[4 * i], kfb[4 * i + 1], kfb[4 * i + 2], kfb[4 * i + 3]), qq, accb, 0, 0, 0);
+        }
+    } else {
+        // q * Kscale of this lane's side page as fp16 hi + lo, against both pages' keys
+        uint32_t ks[D / 8];
+        read_kscales<D>(ks_lds, 2 * j + (side ? 1 : 0), G, ks);
+        uint32_t qh[D / 8], ql[D / 8];
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) {
+            const half2v q2 = __builtin_bit_cast(half2v, qf[i]);
+            const half2v s2 = __builtin_bit_cast(half2v, ks[i]);
+            const half2v hi = q2 * s2;
+            qh[i] = __builtin_bit_cast(uint32_t, hi);
+            ql[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q2, s2, -hi));
+        }
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) {
+            const half8 hq = make_half8(qh[4 * i], qh[4 * i + 1], qh[4 * i + 2], qh[4 * i + 3]);
+            const half8 lq = make_half8(ql[4 * i], ql[4 * i + 1], ql[4 * i + 2], ql[4 * i + 3]);
+            const half8 ka = make_half8(kfa[4 * i], kfa[4 * i + 1], kfa[4 * i + 2], kfa[4 * i + 3]);
+            const half8 kb = make_half8(kfb[4 * i], kfb[4 * i + 1], kfb[4 * i + 2], kfb[4 * i + 3]);
+            acca = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, hq, acca, 0, 0, 0);
+            acca = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, lq, acca, 0, 0, 0);
+            accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, hq, accb, 0, 0, 0);
+            accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, lq, accb, 0, 0, 0);
+        }
+    }
+    return (side ? accb : acca) * scale_log2;
+}
+
+// weights p * Vscale of this lane's four tokens as fp16 hi + lo, exchanged with the partner
+// lane (h xor 8) into the PV operand: columns 0..7 hi parts, columns 8..15 lo parts, k slots
+// 0..3 page A's tokens 4G..4G+3, slots 4..7 page B's
+__device__ __forceinline__ half8 pair_weights(const float* p, uint32_t vs0, uint32_t vs1, bool side,
+                                              bool partial, int ntok, int G) {
+    const half2v s01 = __builtin_bit_cast(half2v, vs0);
+    const half2v s23 = __builtin_bit_cast(half2v, vs1);
+    float w[4] = {p[0] * (float)s01[0], p[1] * (float)s01[1], p[2] * (float)s23[0], p[3] * (float)s23[1]};
+    if (partial) {                       // masked slots may hold any bits as their scale
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (4 * G + i >= ntok) w[i] = 0.f;
+    }
+    half2v h01, h23, l01, l23;
+    h01[0] = (_Float16)w[0]; h01[1] = (_Float16)w[1];
+    h23[0] = (_Float16)w[2]; h23[1] = (_Float16)w[3];
+    l01[0] = (_Float16)(w[0] - (float)h01[0]); l01[1] = (_Float16)(w[1] - (float)h01[1]);
+    l23[0] = (_Float16)(w[2] - (float)h23[0]); l23[1] = (_Float16)(w[3] - (float)h23[1]);
+    const uint32_t H0 = __builtin_bit_cast(uint32_t, h01), H1 = __builtin_bit_cast(uint32_t, h23);
+    const uint32_t L0 = __builtin_bit_cast(uint32_t, l01), L1 = __builtin_bit_cast(uint32_t, l23);
+    const uint32_t r0 = dpp_ror8(side ? H0 : L0), r1 = dpp_ror8(side ? H1 : L1);
+    return make_half8(side ? r0 : H0, side ? r1 : H1, side ? L0 : r0, side ? L1 : r1);
+}
+
+template <int D, int BITS, int RP>
+__device__ __forceinline__ void round_fast(const FastPair<D, BITS>* P, const uint32_t* qf,
+                                           uint32_t* ks_lds, int lane, float scale_log2,
+                                           WaveState<D>& st) {
+    const int G = lane >> 4;
+    const bool side = (lane & 8) != 0;
+    // stage the K scales of the round's pages (a wave's LDS requests complete in order; the
+    // wave barriers keep the compiler from moving LDS accesses across them)
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < RP; ++j) {
+        ks_lds[(2 * j) * 64 + lane] = P[j].ksa;
+        ks_lds[(2 * j + 1) * 64 + lane] = P[j].ksb;
+    }
+    __builtin_amdgcn_wave_barrier();
+    float4v lg[RP];
+#pragma unroll
+    for (int j = 0; j < RP; ++j) {
+        lg[j] = pair_logits<D, BITS>(P[j], j, qf, ks_lds, lane, side, scale_log2);
+        if (P[j].ntok_a < kPage || P[j].ntok_b < kPage) {      // uniform: a partial or absent page
+            const int ntok = side ? P[j].ntok_b : P[j].ntok_a;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * G + i >= ntok) lg[j][i] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < RP; ++j) mx = fmaxf(mx, fmaxf(fmaxf(lg[j][0], lg[j][1]), fmaxf(lg[j][2], lg[j][3])));
+    mx = fmaxf(mx, __builtin_bit_cast(float, dpp_ror8(__builtin_bit_cast(uint32_t, mx))));
+    mx = rows_max(mx);
+    if (__builtin_amdgcn_ballot_w64(mx > st.m)) {            // finite: the round holds a token
+        const float m_new = fmaxf(st.m, mx + kLazy);
+        const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);   // 0 on the first round
+        st.l *= alpha;
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k) st.o[k] *= alpha;
+        st.m = m_new;
+    }
+#pragma unroll
+    for (int j = 0; j < RP; ++j) {
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(lg[j][i] - st.m);
+        st.l += (p[0] + p[1]) + (p[2] + p[3]);
+        const half8 wop = pair_weights(p, P[j].vs0, P[j].vs1, side,
+                                       P[j].ntok_a < kPage || P[j].ntok_b < kPage,
+                                       side ? P[j].ntok_b : P[j].ntok_a, G);
+        uint32_t va[D / 8], vb[D / 8];
+        unpack_v<D>(P[j].va, BITS, va);
+        unpack_v<D>(P[j].vb, BITS, vb);
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k)
+            st.o[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                make_half8(va[2 * k], va[2 * k + 1], vb[2 * k], vb[2 * k + 1]), wop, st.o[k], 0, 0, 0);
+    }
+}
+
+template <int D, int BITS, int RP>
+__device__ __forceinline__ void wave_chunk_fast(const uint8_t* base, uint32_t hv, int H, int kv,
+                                                int cb, int npg, int ctx, int lane,
+                                                const uint32_t* qf, uint32_t* ks_lds,
+                                                float scale_log2, WaveState<D>& st) {
+    const int nq = (npg + 1) / 2;
+    const int nr = (nq + RP - 1) / RP;
+    const bool side = (lane & 8) != 0;
+    const LaneOffsets lo = lane_offsets<D, BITS>(lane);
+    FastPair<D, BITS> b0[RP], b1[RP];
+#pragma unroll
+    for (int j = 0; j < RP; ++j)
+        load_pair_fast<D, BITS>(base, hv, H, kv, cb, npg, j, nq, ctx, lo, side, b0[j]);
+    for (int r = 0;; r += 2) {
+        if (r + 1 < nr) {
+#pragma unroll
+            for (int j = 0; j < RP; ++j)
+                load_pair_fast<D, BITS>(base, hv, H, kv, cb, npg, (r + 1) * RP + j, nq, ctx, lo, side, b1[j]);
+        }
+        round_fast<D, BITS, RP>(b0, qf, ks_lds, lane, scale_log2, st);
+        if (r + 1 >= nr) break;
+        if (r + 2 < nr) {
+#pragma unroll
+            for (int j = 0; j < RP; ++j)
+                load_pair_fast<D, BITS>(base, hv, H, kv, cb, npg, (r + 2) * RP + j, nq, ctx, lo, side, b0[j]);
+        }
+        round_fast<D, BITS, RP>(b1, qf, ks_lds, lane, scale_log2, st);
+        if (r + 2 >= nr) break;
+    }
+}
+
 // HALF: the group has at most 8 query heads (see process_pair_half). FUSED: the kernel first
 // writes the step's new tokens (at most 16 per sequence, so at most two pages): the workgroup
 // whose split holds a touched page quantizes it (256 threads a page) and, for the first page,
@@ -824,8 +1180,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) float lds_o[kWaves][kMaxGroup][D];
     __shared__ float lds_m[kWaves][kMaxGroup];
     __shared__ float lds_l[kWaves][kMaxGroup];
-    __shared__ float lds_w[kMaxSplits][kMaxGroup];   // split weights in the final merge
-    __shared__ float lds_lk[kMaxSplits][kMaxGroup];  // split sums in the final merge
+    __shared__ float2 lds_ml[kMaxGroup][kMaxSplits]; // (max, sum) of every split in the final merge
     __shared__ float lds_L[kMaxGroup];
     __shared__ int lds_last;
 
@@ -913,7 +1268,17 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
             tier0 = (int)((uint32_t)__builtin_amdgcn_readfirstlane((int)hv) >> 30);
             uniform = __builtin_amdgcn_ballot_w64((int)(hv >> 30) != tier0) == 0;
         }
-        if (uniform && tier0 == 0)
+        uint32_t* ks_round = reinterpret_cast<uint32_t*>(&lds_o[wave][0][0]);  // free until the merge
+        if (HALF && uniform && tier0 == 0)
+            wave_chunk_fast<D, 2, kRoundPairs2>(a.pools.base[0], hv, a.H, kv, cb, npg, ctx, lane, qf,
+                                                ks_round, a.scale_log2, st);
+        else if (HALF && uniform && tier0 == 1)
+            wave_chunk_fast<D, 4, kRoundPairs4>(a.pools.base[1], hv, a.H, kv, cb, npg, ctx, lane, qf,
+                                                ks_round, a.scale_log2, st);
+        else if (HALF && uniform && tier0 == 2)
+            wave_chunk_fast<D, 8, kRoundPairs8>(a.pools.base[2], hv, a.H, kv, cb, npg, ctx, lane, qf,
+                                                ks_round, a.scale_log2, st);
+        else if (uniform && tier0 == 0)
             wave_chunk_uniform<D, 2, 2, HALF>(a.pools.base[0], hv, a.H, kv, cb, npg, ctx, lane, qf, ks_slot,
                                      a.scale_log2, st);
         else if (uniform && tier0 == 1)
@@ -933,54 +1298,69 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
     }
 
     // ---- this wave's partial -> LDS; the V codes carried the 2^-24 of their subnormal form
-    float lsum = rows_sum(st.l);
-    if constexpr (HALF) {                              // fold page-B columns 8..15 into 0..7
-        lsum += __shfl_xor(lsum, 8, 64);
+    float lsum = st.l;
+    if constexpr (HALF) {                              // fold columns 8..15 into 0..7
+        lsum += __builtin_bit_cast(float, dpp_ror8(__builtin_bit_cast(uint32_t, lsum)));
 #pragma unroll
         for (int k = 0; k < D / 16; ++k)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) st.o[k][r] += __shfl_xor(st.o[k][r], 8, 64);
+            for (int r = 0; r < 4; ++r) {
+                // through a scalar: a bit cast applied to a vector element itself reads the
+                // vector's first element with this compiler
+                const float x = st.o[k][r];
+                st.o[k][r] = x + __builtin_bit_cast(float, dpp_ror8(__builtin_bit_cast(uint32_t, x)));
+            }
     }
+    lsum = rows_sum(lsum);
     if (h < grp) {
         if (G == 0) {
             lds_m[wave][h] = st.m;
             lds_l[wave][h] = lsum;
         }
+        // element r of o[k] is channel G*D/4 + r*D/16 + k: for each r the D/16 channels are
+        // consecutive, written as float4s
 #pragma unroll
-        for (int k = 0; k < D / 16; ++k)
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                lds_o[wave][h][G * (D / 4) + r * (D / 16) + k] = st.o[k][r] * kTwo24;
+            for (int k4 = 0; k4 < D / 64; ++k4)
+                *reinterpret_cast<float4v*>(&lds_o[wave][h][G * (D / 4) + r * (D / 16) + 4 * k4]) =
+                    float4v{st.o[4 * k4][r], st.o[4 * k4 + 1][r], st.o[4 * k4 + 2][r], st.o[4 * k4 + 3][r]} * kTwo24;
     }
     __syncthreads();
 
-    // ---- merge the waves (fixed order) into this split's partial
+    // ---- merge the waves (fixed order) into this split's partial: one float4 of one head per
+    // thread. Partials travel through device-coherent (sc1) stores and loads, which bypass the
+    // per-XCD L2s, so no cache write-back or invalidate is needed.
+    constexpr int kSc1 = 16;                              // cache-policy bit: device coherent
     const bool single = nsplit == 1;
-    const size_t part = (size_t)group * a.splits + split;
-    for (int i = tid; i < grp * D; i += kWaves * 64) {
-        const int hh = i / D, c = i - hh * D;
+    const int nslot = grp * D / 4;
+    const __amdgpu_buffer_rsrc_t o_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        a.ws_o + (size_t)group * a.splits * grp * D, (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ml_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        a.ws_ml + (size_t)group * a.splits * grp * 2, (short)0, 0x7fffffff, 0x00020000);
+    for (int sl = tid; sl < nslot; sl += kWaves * 64) {
+        const int hh = sl / (D / 4), c4 = sl - hh * (D / 4);
         float M = -INFINITY;
+#pragma unroll
         for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lds_m[w][hh]);
-        float acc = 0.f, L = 0.f;
+        float L = 0.f;
+        float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
         for (int w = 0; w < kWaves; ++w) {
             const float mw = lds_m[w][hh];
             const float e = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-            acc += e * lds_o[w][hh][c];
+            acc += e * *reinterpret_cast<const float4v*>(&lds_o[w][hh][4 * c4]);
             L += e * lds_l[w][hh];
         }
         if (single) {
-            a.out[((size_t)s * a.Hq + kv * grp + hh) * D + c] = L > 0.f ? acc / L : 0.f;
+            const float inv = L > 0.f ? 1.f / L : 0.f;
+            *reinterpret_cast<float4v*>(a.out + ((size_t)s * a.Hq + kv * grp + hh) * D + 4 * c4) = acc * inv;
         } else {
-            // partials travel through device-coherent (agent-scope) stores and loads, which
-            // bypass the per-XCD L2s, so no cache write-back or invalidate is needed
-            __hip_atomic_store(a.ws_o + part * grp * D + i, acc, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-            if (c == 0) {
-                __hip_atomic_store(a.ws_ml + (part * grp + hh) * 2, M, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(a.ws_ml + (part * grp + hh) * 2 + 1, L, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            }
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), o_rsrc,
+                                                   (int)((split * grp + hh) * D + 4 * c4) * 4, 0, kSc1);
+            if (c4 == 0)
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, float2v{M, L}), ml_rsrc,
+                                                      (split * grp + hh) * 8, 0, kSc1);
         }
     }
     if (single) return;
@@ -996,27 +1376,20 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
     __syncthreads();
     if (!lds_last) return;
 
-    // Coherent (sc1) reads of the partials as plain buffer loads. Output slot `slot` (four
-    // channels of one head) is summed over the splits by `parts` threads, each over a contiguous
-    // run of at most kBatch splits per round; every thread issues its (max, sum) pair and its first
-    // round of partial outputs before it waits on the pair, so the merge costs one memory round
-    // trip in the common case. Loads past a thread's range re-read a valid entry and are ignored.
-    constexpr int kSc1 = 16;                              // cache-policy bit: device coherent
+    // Output slot `slot` (four channels of one head) is summed over the splits by `parts`
+    // threads, each over a contiguous run of at most kBatch splits per round. Every thread
+    // issues its first round of partial loads together with the (max, sum) pairs, so the merge
+    // costs one memory round trip in the common case; loads past a thread's range re-read a
+    // valid entry and are ignored. Each thread then forms its head's split weights itself from
+    // the pairs staged in LDS (all threads of a head read the same words), and the splits are
+    // always combined in index order.
     constexpr int kBatch = 16;
-    const __amdgpu_buffer_rsrc_t ml_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        a.ws_ml + (size_t)group * a.splits * grp * 2, (short)0, 0x7fffffff, 0x00020000);
-    const __amdgpu_buffer_rsrc_t o_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        a.ws_o + (size_t)group * a.splits * grp * D, (short)0, 0x7fffffff, 0x00020000);
-    const int npair_ml = nsplit * grp;
-    const uint2 ml_first = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
-        ml_rsrc, min(tid, npair_ml - 1) * 8, 0, kSc1));
-    const int slots = grp * D / 4;
-    const int parts = max(1, min(nsplit, (kWaves * 64) / slots));
+    const int parts = max(1, min(nsplit, (kWaves * 64) / nslot));
     const int per_part = (nsplit + parts - 1) / parts;
-    const bool has_job = tid < slots * parts;
+    const bool has_job = tid < nslot * parts;
     const int job = has_job ? tid : 0;
-    const int slot = job % slots, pidx = job / slots;
-    const int hh = slot * 4 / D;
+    const int slot = job % nslot, pidx = job / nslot;
+    const int hh = slot / (D / 4);
     const int k0 = pidx * per_part;                      // this job's splits: [k0, k1)
     const int k1 = min(nsplit, k0 + per_part);
     float4v buf[kBatch];
@@ -1024,36 +1397,33 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
     for (int i = 0; i < kBatch; ++i)
         buf[i] = __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(
             o_rsrc, (min(k0 + i, nsplit - 1) * grp * D + slot * 4) * 4, 0, kSc1));
-    if (tid < npair_ml) {
-        lds_w[tid / grp][tid % grp] = __builtin_bit_cast(float, ml_first.x);   // max, then weight
-        lds_lk[tid / grp][tid % grp] = __builtin_bit_cast(float, ml_first.y);  // sum
-    }
-    for (int i = tid + kWaves * 64; i < npair_ml; i += kWaves * 64) {
+    const int npair = nsplit * grp;
+    for (int i = tid; i < npair; i += kWaves * 64) {
         const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(ml_rsrc, i * 8, 0, kSc1));
-        lds_w[i / grp][i % grp] = __builtin_bit_cast(float, v.x);
-        lds_lk[i / grp][i % grp] = __builtin_bit_cast(float, v.y);
+        lds_ml[i % grp][i / grp] = float2{__builtin_bit_cast(float, v.x), __builtin_bit_cast(float, v.y)};
     }
     __syncthreads();
-    // split weights, one wave per head: global max, e_k = 2^(m_k - M), L = sum_k e_k * l_k
+    // split weights, one wave per head, one lane per split: M = max_k m_k, e_k = 2^(m_k - M),
+    // L = sum_k e_k * l_k; the weights go back to LDS for the accumulation
     for (int h2 = wave; h2 < grp; h2 += kWaves) {
         float M = -INFINITY;
-        for (int k = lane; k < nsplit; k += 64) M = fmaxf(M, lds_w[k][h2]);
-        M = wave_max(M);
+        for (int k = lane; k < nsplit; k += 64) M = fmaxf(M, lds_ml[h2][k].x);
+        M = wave_max_dpp(M);
         float L = 0.f;
         for (int k = lane; k < nsplit; k += 64) {
-            const float mk = lds_w[k][h2];
-            const float e = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk - M);
-            lds_w[k][h2] = e;
-            L += e * lds_lk[k][h2];
+            const float2 ml = lds_ml[h2][k];
+            const float e = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
+            lds_ml[h2][k].x = e;
+            L += e * ml.y;
         }
-        L = wave_sum(L);
+        L = wave_sum_dpp(L);
         if (lane == 0) lds_L[h2] = L;
     }
     __syncthreads();
     float4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < kBatch; ++i)
-        if (k0 + i < k1) acc += lds_w[k0 + i][hh] * buf[i];
+        if (k0 + i < k1) acc += lds_ml[hh][k0 + i].x * buf[i];
     for (int kb = k0 + kBatch; kb < k1; kb += kBatch) {         // long split lists only
 #pragma unroll
         for (int i = 0; i < kBatch; ++i)
@@ -1061,18 +1431,17 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
                 o_rsrc, (min(kb + i, nsplit - 1) * grp * D + slot * 4) * 4, 0, kSc1));
 #pragma unroll
         for (int i = 0; i < kBatch; ++i)
-            if (kb + i < k1) acc += lds_w[kb + i][hh] * buf[i];
+            if (kb + i < k1) acc += lds_ml[hh][kb + i].x * buf[i];
     }
     float4v* part_acc = reinterpret_cast<float4v*>(&lds_o[0][0][0]);   // [parts][slots]
-    if (has_job) part_acc[pidx * slots + slot] = acc;
+    if (has_job) part_acc[pidx * nslot + slot] = acc;
     __syncthreads();
-    for (int sl = tid; sl < slots; sl += kWaves * 64) {
-        float4v sum = part_acc[sl];
-        for (int pi = 1; pi < parts; ++pi) sum += part_acc[pi * slots + sl];
-        const float L = lds_L[sl * 4 / D];
+    if (tid < nslot) {
+        float4v sum = part_acc[tid];
+        for (int pi = 1; pi < parts; ++pi) sum += part_acc[pi * nslot + tid];
+        const float L = lds_L[tid / (D / 4)];
         const float inv = L > 0.f ? 1.f / L : 0.f;
-        float* o = a.out + ((size_t)s * a.Hq + kv * grp) * D + sl * 4;
-        *reinterpret_cast<float4*>(o) = make_float4(sum[0] * inv, sum[1] * inv, sum[2] * inv, sum[3] * inv);
+        *reinterpret_cast<float4v*>(a.out + ((size_t)s * a.Hq + kv * grp) * D + tid * 4) = sum * inv;
     }
     if (tid == 0)
         __hip_atomic_store(&a.counters[group], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
