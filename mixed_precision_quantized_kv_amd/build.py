@@ -33,7 +33,10 @@ FLAGS = ["-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 # 16-byte global loads, and the kernel runs at the same speed.
 # The controller keeps its averages bit-identical to a plain binary64 evaluation, so it is built
 # without floating-point contraction.
-EXTRA = {"kv_attn.hip": ["-mllvm", "-amdgpu-load-store-vectorizer=0"],
+# The attention kernel's first twelve argument dwords (block table, lengths, q, shape) are preloaded into
+# SGPRs at wave launch (gfx950 kernel-argument preloading).
+EXTRA = {"kv_attn.hip": ["-mllvm", "-amdgpu-load-store-vectorizer=0",
+                         "-mllvm", "-amdgpu-kernarg-preload-count=12"],
          "kv_controller.cpp": ["-ffp-contract=off"]}
 
 

@@ -1175,7 +1175,16 @@ __device__ __forceinline__ void wave_chunk_fast(const uint8_t* base, uint32_t hv
 // updates the ring, then makes its writes visible to its own loads and attends over
 // pos + n_new tokens. No other workgroup reads those pages, so one launch does both steps.
 template <int D, bool HALF, bool FUSED>
-__global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
+// The block table, the lengths (ctx_len, or pos for the fused step), q and the shape integers
+// that address them come first as plain arguments: the build preloads the first twelve
+// kernel-argument dwords into SGPRs at wave launch, so the first loads need not wait for the
+// argument segment.
+__global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t* __restrict__ bt,
+                                                                  const int32_t* __restrict__ lens,
+                                                                  const uint16_t* __restrict__ qv,
+                                                                  int groups, int H, int max_pages,
+                                                                  int pps, int Hq, int grp,
+                                                                  AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t lds_ks[kWaves][2][64];
     __shared__ __attribute__((aligned(16))) float lds_o[kWaves][kMaxGroup][D];
     __shared__ float lds_m[kWaves][kMaxGroup];
@@ -1184,33 +1193,32 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(AttnArgs a) {
     __shared__ float lds_L[kMaxGroup];
     __shared__ int lds_last;
 
-    const int split = blockIdx.x / a.groups, group = blockIdx.x % a.groups;
-    const int s = group / a.H, kv = group % a.H;
+    const int split = blockIdx.x / groups, group = blockIdx.x % groups;
+    const int s = group / H, kv = group % H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps page math scalar
-    const int grp = a.grp;
     // The handles of this wave's chunk are requested before the context length arrives, on the
     // guess that the split is full (every split but a sequence's last); the guess is checked
     // once the length is known and the last split re-reads its own.
-    const int pbeg = split * a.pps;
-    const int cb_full = pbeg + (wave * a.pps) / kWaves;
-    const int npg_full = pbeg + ((wave + 1) * a.pps) / kWaves - cb_full;
-    const uint32_t* bt_row = a.bt + (size_t)s * a.max_pages;
+    const int pbeg = split * pps;
+    const int cb_full = pbeg + (wave * pps) / kWaves;
+    const int npg_full = pbeg + ((wave + 1) * pps) / kWaves - cb_full;
+    const uint32_t* bt_row = bt + (size_t)s * max_pages;
     uint32_t hv_full = 0;
     if (npg_full > 0 && npg_full <= 64)
-        hv_full = bt_row[min(cb_full + min(lane, npg_full - 1), a.max_pages - 1)];
+        hv_full = bt_row[min(cb_full + min(lane, npg_full - 1), max_pages - 1)];
     // q fragment: lane (h, G) holds q[h][G*D/4 .. +D/4) as fp16 pairs (zero for h >= grp)
     const int h = lane & 15, G = lane >> 4;
     const int hq = HALF ? (h & 7) : h;                 // the query head of this lane's column
     uint32_t qf[D / 8];
     {
         const uint32_t* qp = reinterpret_cast<const uint32_t*>(
-            a.q + ((size_t)s * a.Hq + kv * grp + min(hq, grp - 1)) * D + G * (D / 4));
+            qv + ((size_t)s * Hq + kv * grp + min(hq, grp - 1)) * D + G * (D / 4));
 #pragma unroll
         for (int i = 0; i < D / 8; ++i) qf[i] = hq < grp ? qp[i] : 0u;
     }
 
-    const int ctx = FUSED ? ((const_i32_ptr)a.pos)[s] + a.n_new : ((const_i32_ptr)a.ctx_len)[s];
+    const int ctx = ((const_i32_ptr)lens)[s] + (FUSED ? a.n_new : 0);
     const int npages = (ctx + kPage - 1) / kPage;
     const int nsplit = (npages + a.pps - 1) / a.pps;
 
@@ -1492,11 +1500,15 @@ hipError_t launch(const kv_geometry& g, const AttnArgs& a, int splits, hipStream
     dim3 grid((unsigned)(splits * a.groups));
     const bool half = a.grp <= 8;
     if (g.head_dim == 128) {
-        if (half) hipLaunchKernelGGL((decode_attn_kernel<128, true, FUSED>), grid, dim3(kWaves * 64), 0, stream, a);
-        else hipLaunchKernelGGL((decode_attn_kernel<128, false, FUSED>), grid, dim3(kWaves * 64), 0, stream, a);
+        if (half) hipLaunchKernelGGL((decode_attn_kernel<128, true, FUSED>), grid, dim3(kWaves * 64), 0, stream, a.bt,
+                           FUSED ? a.pos : a.ctx_len, a.q, a.groups, a.H, a.max_pages, a.pps, a.Hq, a.grp, a);
+        else hipLaunchKernelGGL((decode_attn_kernel<128, false, FUSED>), grid, dim3(kWaves * 64), 0, stream, a.bt,
+                           FUSED ? a.pos : a.ctx_len, a.q, a.groups, a.H, a.max_pages, a.pps, a.Hq, a.grp, a);
     } else {
-        if (half) hipLaunchKernelGGL((decode_attn_kernel<64, true, FUSED>), grid, dim3(kWaves * 64), 0, stream, a);
-        else hipLaunchKernelGGL((decode_attn_kernel<64, false, FUSED>), grid, dim3(kWaves * 64), 0, stream, a);
+        if (half) hipLaunchKernelGGL((decode_attn_kernel<64, true, FUSED>), grid, dim3(kWaves * 64), 0, stream, a.bt,
+                           FUSED ? a.pos : a.ctx_len, a.q, a.groups, a.H, a.max_pages, a.pps, a.Hq, a.grp, a);
+        else hipLaunchKernelGGL((decode_attn_kernel<64, false, FUSED>), grid, dim3(kWaves * 64), 0, stream, a.bt,
+                           FUSED ? a.pos : a.ctx_len, a.q, a.groups, a.H, a.max_pages, a.pps, a.Hq, a.grp, a);
     }
     return hipGetLastError();
 }
