@@ -191,6 +191,8 @@ def run(args):
     dev = "cuda:0"
     w = synth.WORKLOADS[args.workload]
     L, B, nn = w.num_layers, w.batch, w.new_tokens
+    # the fused step writes at most 16 tokens per sequence; wider writes take the two-call step
+    unfused = args.unfused or nn > 16
     steps_total = args.warmup + args.steps
     t0 = time.time()
     m = Model(w, steps_total, torch, kvq, synth, dev)
@@ -206,7 +208,10 @@ def run(args):
     pos_all = torch.stack([lens0 - 1 + i * nn for i in range(steps_total)]).contiguous()
     ctx_all = (pos_all + nn).contiguous()
     scale = 1.0 / math.sqrt(w.head_dim)
-    pps = args.pages_per_split or kvq.kv_decode_pages_per_split(m.g, B, m.max_ctx)
+    # the split plan for the batch's lengths at the first timed step (the library's plan for
+    # known lengths: one round for equal lengths, smaller balanced splits for a ragged batch)
+    pps = args.pages_per_split or kvq.kv_decode_pages_per_split_for(
+        m.g, (m.lens0 + args.warmup * nn).astype(np.int32))
     wsb = kvq.kv_decode_workspace_bytes(m.g, B, m.max_ctx, pps)
     ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
     out = torch.empty((B, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
@@ -218,7 +223,7 @@ def run(args):
 
     def writes_and_attention(i, sp_):
         for l in range(L):
-            if args.unfused:
+            if unfused:
                 kvq.kv_quant_write(m.g, m.pools[l], m.bt[l], pos_all[i], B, nn, k_all[i, l],
                                    v_all[i, l], m.ring[l], stream=sp_)
                 kvq.kv_decode_attn(m.g, m.pools[l], m.bt[l], ctx_all[i], B, m.max_ctx, q_all[i, l],
@@ -230,7 +235,7 @@ def run(args):
 
     def attention_only(i, sp_):
         for l in range(L):
-            if args.unfused:
+            if unfused:
                 kvq.kv_decode_attn(m.g, m.pools[l], m.bt[l], ctx_all[i], B, m.max_ctx, q_all[i, l],
                                    scale, out, ws, wsb, pps, stream=sp_)
             else:          # the step's own kernel; replaying its write stores the same bytes again
@@ -309,7 +314,7 @@ def run(args):
         ctx = lens + (args.warmup + j) * nn
         for l, b in enumerate(m.bits):
             per_launch_bytes[j, l] = sum(attn_bytes(w, int(c), b) for c in ctx)
-            if not args.unfused:
+            if not unfused:
                 per_launch_bytes[j, l] += sum(write_bytes(w, int(c) - nn, nn, b) for c in ctx)
         step_bytes.append(sum(attn_bytes(w, int(c), b) for c in ctx for b in m.bits))
     step_bytes = float(np.mean(step_bytes))
@@ -320,7 +325,7 @@ def run(args):
     value = step_bytes / (ms_step * 1e-3) / 1e9
     probes = hbm_probes(torch, dev)
     traffic = None
-    if (ATTN_TRAFFIC["source_sha256"] == source_digest(ATTN_SRC) and not args.unfused
+    if (ATTN_TRAFFIC["source_sha256"] == source_digest(ATTN_SRC) and not unfused
             and args.workload == "qwen14b_32k" and not args.pages_per_split):
         traffic = ATTN_TRAFFIC["bytes_per_launch"]      # taken on the fused kernel, default workload
     tiers = {b: m.bits.count(b) for b in (2, 4, 8)}
@@ -352,7 +357,7 @@ def run(args):
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "decode_attn_kernel<128> (unfused)" if args.unfused else
+            "kernel": "decode_attn_kernel<128> (unfused)" if unfused else
                       "decode_attn_kernel<128> fused with the write (kv_decode_step)",
             "bytes_per_launch": int(avg_launch_bytes),
             "traffic_over_algorithmic": (round(traffic / ATTN_TRAFFIC["algorithmic_bytes_per_launch"], 4)

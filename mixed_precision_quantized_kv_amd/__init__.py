@@ -79,6 +79,7 @@ def lib() -> ctypes.CDLL:
             "kv_quant_write": (i32, [G, ctypes.POINTER(LayerPools), P, P, i32, i32, P, P, P, P]),
             "kv_decode_workspace_bytes": (sz, [G, i32, i32, i32]),
             "kv_decode_pages_per_split": (i32, [G, i32, i32]),
+            "kv_decode_pages_per_split_for": (i32, [G, i32, P]),
             "kv_decode_attn": (i32, [G, ctypes.POINTER(LayerPools), P, P, i32, i32, P,
                                      ctypes.c_float, P, P, sz, i32, P]),
             "kv_decode_step": (i32, [G, ctypes.POINTER(LayerPools), P, P, i32, i32, P, P, P, i32,
@@ -173,6 +174,13 @@ def kv_decode_workspace_bytes(g: Geometry, batch: int, max_ctx_len: int, pages_p
 
 def kv_decode_pages_per_split(g: Geometry, batch: int, max_ctx_len: int) -> int:
     return lib().kv_decode_pages_per_split(ctypes.byref(g), batch, max_ctx_len)
+
+
+def kv_decode_pages_per_split_for(g: Geometry, ctx_len_host) -> int:
+    """split plan for known lengths (host int32 array, one per sequence)"""
+    import numpy as np
+    a = np.ascontiguousarray(ctx_len_host, dtype=np.int32)
+    return lib().kv_decode_pages_per_split_for(ctypes.byref(g), int(a.size), a.ctypes.data)
 
 
 def kv_canary_workspace_bytes(g: Geometry, batch: int) -> int:

@@ -106,6 +106,8 @@ uint64_t splitmix64(uint64_t& x) {
     return z ^ (z >> 31);
 }
 
+constexpr int64_t kMaxPagesPerSplit = 512;      // 8 waves x 64 pages
+
 int auto_pages_per_split(const kv_geometry& g, int batch, int max_pages) {
     // one workgroup per CU (the kernel holds one 8-wave workgroup per CU): split each
     // (sequence, KV head) so that the grid has about 256 workgroups, pages in pairs, at most
@@ -114,6 +116,8 @@ int auto_pages_per_split(const kv_geometry& g, int batch, int max_pages) {
     int64_t splits = std::max<int64_t>(1, (256 + groups - 1) / groups);
     int64_t pps = (max_pages + splits - 1) / splits;
     pps = std::max<int64_t>(pps, 2);
+    // a wave keeps the handles of at most 64 pages in registers (the width-specialised loop)
+    pps = std::min<int64_t>(pps, kMaxPagesPerSplit);
     pps = std::max<int64_t>(pps, (max_pages + 255) / 256);
     pps += pps & 1;
     return (int)pps;
@@ -334,6 +338,28 @@ int kv_decode_pages_per_split(const kv_geometry* g, int batch, int max_ctx_len) 
     if (check_geometry(g) != KV_OK || batch < 1 || max_ctx_len < 0) return 0;
     const int max_pages = std::max(1, (max_ctx_len + g->page_size - 1) / g->page_size);
     return auto_pages_per_split(*g, batch, max_pages);
+}
+
+int kv_decode_pages_per_split_for(const kv_geometry* g, int batch, const int32_t* ctx_len_host) {
+    if (check_geometry(g) != KV_OK || batch < 1 || batch > g->max_seqs || !ctx_len_host) return 0;
+    int64_t total = 0, longest = 0;
+    for (int s = 0; s < batch; ++s) {
+        if (ctx_len_host[s] < 0 || (int64_t)ctx_len_host[s] > (int64_t)g->max_pages_per_seq * g->page_size)
+            return 0;
+        const int64_t pages = (ctx_len_host[s] + g->page_size - 1) / g->page_size;
+        total += pages;
+        longest = std::max(longest, pages);
+    }
+    const int uniform = auto_pages_per_split(*g, batch, (int)std::max<int64_t>(1, longest));
+    if (10 * total >= 9 * longest * batch) return uniform;
+    // ragged: about two workgroups of pages per compute unit over the whole batch (measured on
+    // 64 log-uniform lengths in [1K, 32K]: smaller splits add per-workgroup round trips, larger
+    // ones leave compute units idle at the end)
+    int64_t pps = (total * g->num_kv_heads + 511) / 512;
+    pps = std::min<int64_t>(std::max<int64_t>(pps, 2), uniform);
+    pps = std::max<int64_t>(pps, (longest + 255) / 256);
+    pps += pps & 1;
+    return (int)pps;
 }
 
 static kv_status decode_plan(const kv_geometry* g, int batch, int max_ctx_len, int pps_in,

@@ -116,6 +116,32 @@ def test_split_plan():
     assert -(-2048 // pps) * 8 >= 248            # about one workgroup per CU
     g4 = geom(max_seqs=1, max_pages_per_seq=9000)
     assert kvq.kv_decode_pages_per_split(g4, 1, 131072) * 256 >= 8192
+    # many groups: one split each, capped so that a wave holds at most 64 pages
+    g5 = geom(head_dim=128, num_q_heads=28, num_kv_heads=4, max_seqs=64, max_pages_per_seq=2100)
+    assert kvq.kv_decode_pages_per_split(g5, 64, 32768) == 512
+
+
+def test_split_plan_for_lengths():
+    g = geom(head_dim=128, num_q_heads=40, num_kv_heads=8, max_seqs=1, max_pages_per_seq=2100)
+    # equal (here: one) lengths: the plan for the longest length
+    assert kvq.kv_decode_pages_per_split_for(g, [32768]) == kvq.kv_decode_pages_per_split(g, 1, 32768)
+    g5 = geom(head_dim=128, num_q_heads=28, num_kv_heads=4, max_seqs=64, max_pages_per_seq=2100)
+    lens = np.full(64, 20000, dtype=np.int32)
+    lens[:3] = 20100
+    assert kvq.kv_decode_pages_per_split_for(g5, lens) == kvq.kv_decode_pages_per_split(g5, 64, 20100)
+    # ragged lengths: splits small enough that the batch makes about two workgroups per CU
+    rng = np.random.default_rng(0)
+    lens = np.round(np.exp(rng.uniform(np.log(1024), np.log(32768), 64))).astype(np.int32)
+    pps = kvq.kv_decode_pages_per_split_for(g5, lens)
+    pages = (lens + 15) // 16
+    assert pps % 2 == 0 and 2 <= pps < kvq.kv_decode_pages_per_split(g5, 64, int(lens.max()))
+    wgs = int(((pages + pps - 1) // pps).sum()) * 4
+    assert 450 <= wgs <= 800, wgs
+    assert -(-int(pages.max()) // pps) <= 256
+    # invalid lengths
+    assert kvq.kv_decode_pages_per_split_for(g5, np.array([-1] * 64, np.int32)) == 0
+    assert kvq.kv_decode_pages_per_split_for(g5, np.array([2100 * 16 + 1] + [5] * 63, np.int32)) == 0
+    assert kvq.kv_decode_pages_per_split_for(g5, np.zeros(65, np.int32)) == 0   # batch > max_seqs
 
 
 # ------------------------------------------------------------------ allocator
