@@ -1128,9 +1128,11 @@ __device__ __forceinline__ void round_fast(const FastPair<D, BITS>* P, const uin
         const half8 wop = pair_weights(p, P[j].vs0, P[j].vs1, side,
                                        P[j].ntok_a < kPage || P[j].ntok_b < kPage,
                                        side ? P[j].ntok_b : P[j].ntok_a, G);
+        // V codes as exact fp16 integers, decoded like the K codes (the two word layouts put
+        // codes in the same positions); this loop's o is therefore in plain units
         uint32_t va[D / 8], vb[D / 8];
-        unpack_v<D>(P[j].va, BITS, va);
-        unpack_v<D>(P[j].vb, BITS, vb);
+        unpack_k_fast<D, BITS>(P[j].va, va);
+        unpack_k_fast<D, BITS>(P[j].vb, vb);
 #pragma unroll
         for (int k = 0; k < D / 16; ++k)
             st.o[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
@@ -1167,6 +1169,9 @@ __device__ __forceinline__ void wave_chunk_fast(const uint8_t* base, uint32_t hv
         round_fast<D, BITS, RP>(b1, qf, ks_lds, lane, scale_log2, st);
         if (r + 2 >= nr) break;
     }
+    // to the 2^-24 units the other loops keep (their V codes are fp16 subnormals); exact
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) st.o[k] *= 1.0f / kTwo24;
 }
 
 // HALF: the group has at most 8 query heads (see process_pair_half). FUSED: the kernel first
