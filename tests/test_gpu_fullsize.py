@@ -34,10 +34,16 @@ CASES = (first_layer_of_each_width("llama8b_8k") + first_layer_of_each_width("qw
 
 def check_attention_and_canary(L, q):
     ref = L.oracle_attn(q)
-    got, _ = L.attn(q)                                  # pages_per_split 0: the library's plan
-    err = rowwise_rel_err(got, ref)
-    print(f"  attention rows {err.size}: max rel err {err.max():.3e}", flush=True)
-    assert err.max() <= ATTN_TOL, (err.max(), np.unravel_index(np.argmax(err), err.shape))
+    plans = [0]                                         # 0: the library's plan from the longest length
+    pps_for = kvq.kv_decode_pages_per_split_for(L.g, L.len)
+    if pps_for != kvq.kv_decode_pages_per_split(L.g, L.batch, int(L.len.max())):
+        plans.append(pps_for)                           # the plan for the lengths (ragged batches)
+    for pps in plans:
+        got, _ = L.attn(q, pages_per_split=pps)
+        err = rowwise_rel_err(got, ref)
+        print(f"  attention rows {err.size} (pages per split {pps}): max rel err {err.max():.3e}",
+              flush=True)
+        assert err.max() <= ATTN_TOL, (pps, err.max(), np.unravel_index(np.argmax(err), err.shape))
     kl, rows = L.canary(q)
     okl, orows = L.oracle_canary(q)
     print(f"  canary {kl} vs {okl}; max row err {np.abs(rows - orows).max():.3e}", flush=True)

@@ -168,6 +168,35 @@ def test_many_page_pairs_per_wave(hq, hkv, d, mix):
         assert err.max() <= ATTN_TOL, (pps, err.max())
 
 
+@pytest.mark.parametrize("tier", [0, 1, 2])
+@pytest.mark.parametrize("direction", ["rising", "falling"])
+def test_logits_rising_or_falling_across_pages(tier, direction):
+    """the running maximum of the page loop: keys whose logit climbs by ~6 (log2 units) every
+    page, so the maximum is raised in every round, and the reverse order, where it never is"""
+    case_banner(f"{direction} logits, tier {tier}")
+    N = 700
+    g = np.random.default_rng(31 + tier)
+    ramp = np.arange(N, dtype=np.float32)           # logit +0.25 a token: ~5.8 log2 units a page
+    if direction == "falling":
+        ramp = ramp[::-1].copy()
+    K = (g.standard_normal((1, N, 2, 64), dtype=np.float32) * 0.1)
+    K[:, :, :, 0] += ramp[None, :, None]
+    K = K.astype(np.float16).view(np.uint16)
+    V = synth.normal_f16(g, (1, N, 2, 64))
+    L = LayerPair(8, 2, 64, 1, 46, [[tier] * 44], seed=tier)
+    L.write(K, V)
+    qf = np.zeros((1, 8, 64), dtype=np.float32)
+    qf[:, :, 0] = 2.0
+    qf[:, :, 1:] = g.standard_normal((1, 8, 63), dtype=np.float32) * 0.1
+    q = qf.astype(np.float16).view(np.uint16)
+    ref = L.oracle_attn(q)
+    for pps in (0, 4, 16, 44):
+        got, _ = L.attn(q, pages_per_split=pps)
+        err = rowwise_rel_err(got, ref)
+        print(f"  attn pps={pps} max rel err {err.max():.3e}")
+        assert err.max() <= ATTN_TOL, (pps, err.max())
+
+
 def test_deterministic_and_workspace_reuse():
     case_banner("determinism")
     L = tiny_layer(2)
