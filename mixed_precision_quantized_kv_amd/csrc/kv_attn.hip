@@ -1249,11 +1249,12 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
                 __syncthreads();                         // the first page's ring reads are done
                 write_ring<D>(a.wr, s, kv, p0, tid, kWaves * 64);
             }
-            // the writes reach memory before any wave of this workgroup reads the pages, and
-            // this compute unit's vector cache forgets what the write phase loaded
+            // the writes complete before any wave of this workgroup reads the pages: only this
+            // workgroup reads them in this launch, and stores from this compute unit are seen
+            // by its own later loads (workgroup scope), so no cache invalidation is needed (an
+            // agent-scope acquire here invalidated the L2 and cost 1-5 us per workgroup)
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
     }
 
