@@ -13,12 +13,13 @@
 // (v_mfma_f32_16x16x32_f16):
 //   S^T[t][h] = sum_c Kcode[t][c] * q'[h][c],  q' = q * Kscale(page, c)     (16 tokens a page)
 //   o^T[c][h] += sum_t Vcode[t][c] * p'[h][t], p' = p * Vscale(t)          (32 tokens a pair)
-// K codes become exact fp16 integers (byte masks + v_perm_b32 + one packed add). The K scales
-// fold into q: exactly for INT2 (code * scale is exact when |code| <= 1), otherwise as two fp16
-// parts hi + lo of q * scale so the products stay exact to ~2^-22. V codes enter the MFMA as
-// signed fp16 subnormals code * 2^-24, taken from the packed word with a shift and a mask and one
-// exact packed subtract of the field offset 2^(b-1) * 2^-24; the weights p * Vscale enter as two
-// fp16 parts hi + lo of their fp32 product (two MFMAs), so no term carries more than ~2^-22 of
+// K and V codes become exact fp16 integers (masks, then v_perm_b32 or v_and_or_b32 with the
+// exponent of 1024, then one exact packed add or fused multiply-add). Normal numbers on purpose:
+// fp16 subnormal MFMA operands lose precision once their products mix with larger ones (measured
+// on gfx950: about 2^-12.5 of the sum of magnitudes, against 2^-22 for normal operands). The K
+// scales fold into q: exactly for INT2 (code * scale is exact when |code| <= 1), otherwise as two
+// fp16 parts hi + lo of q * scale so the products stay exact to ~2^-22; the weights p * Vscale
+// enter as two fp16 parts hi + lo of their fp32 product, so no term carries more than ~2^-22 of
 // rounding and nothing cancels. Computing S and o transposed puts head h in lane h%16 of both
 // products, so the softmax output is the PV operand in place and the rescale by
 // exp(m_old - m_new) is lane-local. Query heads beyond the group are zero MFMA rows.
@@ -47,7 +48,6 @@ typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
 
 constexpr int kWaves = 8;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kTwo24 = 16777216.0f;
 constexpr int kMaxSplits = 256;
 
 struct AttnArgs {
@@ -230,36 +230,6 @@ __device__ __forceinline__ void unpack_k(const uint32_t* w, int bits, uint32_t* 
     }
 }
 
-// V chunk -> D/8 dwords of signed fp16 subnormal pairs (code_a * 2^-24, code_b * 2^-24), in code
-// order: the field u = code + 2^(b-1) as a subnormal, minus 2^(b-1) * 2^-24 (exact: both operands
-// are subnormals of the same exponent)
-__device__ __forceinline__ uint32_t sub_subnormal(uint32_t u, uint32_t offset) {
-    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, u) - __builtin_bit_cast(half2v, offset));
-}
-
-template <int D>
-__device__ __forceinline__ void unpack_v(const uint32_t* w, int bits, uint32_t* out) {
-    if (bits == 2) {
-#pragma unroll
-        for (int i = 0; i < D / 64; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                out[i * 8 + j] = sub_subnormal((w[i] >> (2 * j)) & 0x00030003u, 0x00020002u);
-    } else if (bits == 4) {
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                out[i * 4 + j] = sub_subnormal((w[i] >> (4 * j)) & 0x000F000Fu, 0x00080008u);
-    } else {
-#pragma unroll
-        for (int i = 0; i < D / 16; ++i) {
-            out[2 * i] = sub_subnormal(__builtin_amdgcn_perm(0u, w[i], 0x0C020C00u), 0x00800080u);
-            out[2 * i + 1] = sub_subnormal(__builtin_amdgcn_perm(0u, w[i], 0x0C030C01u), 0x00800080u);
-        }
-    }
-}
-
 __device__ __forceinline__ half8 make_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
     uint4 u = {a, b, c, d};
     return __builtin_bit_cast(half8, u);
@@ -433,9 +403,9 @@ __device__ __forceinline__ void process_pair(const PageRaw& A, const PageRaw& B,
     const half8 pl = make_half8(wl[0], wl[1], wl[2], wl[3]);
 
     uint32_t va[D / 8], vb[D / 8];
-    unpack_v<D>(A.v, bits_a, va);
+    unpack_k<D>(A.v, bits_a, va);
     if (B.bits) {
-        unpack_v<D>(B.v, bits_b, vb);
+        unpack_k<D>(B.v, bits_b, vb);
     } else {
 #pragma unroll
         for (int i = 0; i < D / 8; ++i) vb[i] = 0u;
@@ -568,9 +538,9 @@ __device__ __forceinline__ void process_pair_half(const PageRaw& A, const PageRa
     const half8 pl = make_half8(side ? z : wl[0], side ? z : wl[1], side ? wl[0] : z, side ? wl[1] : z);
 
     uint32_t va[D / 8], vb[D / 8];
-    unpack_v<D>(A.v, bits_a, va);
+    unpack_k<D>(A.v, bits_a, va);
     if (has_b) {
-        unpack_v<D>(B.v, bits_b, vb);
+        unpack_k<D>(B.v, bits_b, vb);
     } else {
 #pragma unroll
         for (int i = 0; i < D / 8; ++i) vb[i] = 0u;
@@ -620,11 +590,8 @@ __device__ __forceinline__ void load_page_f16(const uint8_t* sec, int lane, Page
 
 // A pair of FP16 pages (B may be absent): the same QK, online softmax and PV as the INT pairs,
 // with the keys and values used as they are (each MFMA product of two fp16 values is exact in
-// fp32) and the softmax weights split into fp16 hi + lo. The INT pages accumulate o in units of
-// 2^-24 (their V codes enter as subnormals); SCALED brings o to plain units around this pair's
-// PV product and back, both exact power-of-two scalings. Without SCALED the caller keeps o in
-// plain units and converts it once.
-template <int D, bool HALF, bool SCALED>
+// fp32) and the softmax weights split into fp16 hi + lo.
+template <int D, bool HALF>
 __device__ __forceinline__ void process_pair_f16(const PageF16<D>& A, const PageF16<D>& B,
                                                  bool has_b, int ntok_a, int ntok_b,
                                                  const uint32_t* qf, int lane, float scale_log2,
@@ -700,10 +667,6 @@ __device__ __forceinline__ void process_pair_f16(const PageF16<D>& A, const Page
     }
     const half8 ph = make_half8(wh[0], wh[1], wh[2], wh[3]);
     const half8 pl = make_half8(wl[0], wl[1], wl[2], wl[3]);
-    if constexpr (SCALED) {
-#pragma unroll
-        for (int k = 0; k < D / 16; ++k) st.o[k] *= kTwo24;
-    }
 #pragma unroll
     for (int k = 0; k < D / 16; ++k) {
         const uint32_t vb0 = has_b ? B.v[2 * k] : 0u, vb1 = has_b ? B.v[2 * k + 1] : 0u;
@@ -711,15 +674,10 @@ __device__ __forceinline__ void process_pair_f16(const PageF16<D>& A, const Page
         st.o[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vv, ph, st.o[k], 0, 0, 0);
         st.o[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vv, pl, st.o[k], 0, 0, 0);
     }
-    if constexpr (SCALED) {
-#pragma unroll
-        for (int k = 0; k < D / 16; ++k) st.o[k] *= 1.0f / kTwo24;
-    }
 }
 
 // A wave's chunk of FP16 pages, handles in `hv` (lane i: page cb + i). Pairs are loaded and
-// used in turn; o is kept in plain units and brought to the INT pages' 2^-24 units at the end
-// (a wave takes one chunk, so o starts at zero).
+// used in turn.
 template <int D, bool HALF>
 __device__ __forceinline__ void wave_chunk_f16(const uint8_t* base, uint32_t hv, int H, int kv,
                                                int cb, int npg, int ctx, int lane,
@@ -737,12 +695,10 @@ __device__ __forceinline__ void wave_chunk_f16(const uint8_t* base, uint32_t hv,
         load_page_f16<D>(base + ((size_t)ia * H + kv) * sec_bytes, lane, A);
         load_page_f16<D>(base + ((size_t)ib * H + kv) * sec_bytes, lane, B);
         const int page = cb + pa;
-        process_pair_f16<D, HALF, false>(A, B, has_b, min(kPage, ctx - page * kPage),
+        process_pair_f16<D, HALF>(A, B, has_b, min(kPage, ctx - page * kPage),
                                          has_b ? min(kPage, ctx - (page + 1) * kPage) : 0, qf,
                                          lane, scale_log2, st);
     }
-#pragma unroll
-    for (int k = 0; k < D / 16; ++k) st.o[k] *= 1.0f / kTwo24;
 }
 
 // one pair of the general loop: pairs with an FP16 page go page by page, each FP16 page read
@@ -767,7 +723,7 @@ __device__ __forceinline__ void run_pair_any(const PageSrc& src, int kv, int pag
             const uint8_t* sec = src.base3 + ((size_t)(handle & 0x3fffffffu) * src.H + kv) * (4u * kPage * D);
             PageF16<D> F;
             load_page_f16<D>(sec, lane, F);
-            process_pair_f16<D, HALF, true>(F, F, false, X.ntok, 0, qf, lane, scale_log2, st);
+            process_pair_f16<D, HALF>(F, F, false, X.ntok, 0, qf, lane, scale_log2, st);
         } else if (X.bits) {
             run_pair<D, 0, HALF>(X, none, qf, lds_ks, lane, scale_log2, st);
         }
@@ -1080,10 +1036,16 @@ __device__ __forceinline__ half8 pair_weights(const float* p, uint32_t vs0, uint
     return make_half8(side ? r0 : H0, side ? r1 : H1, side ? L0 : r0, side ? L1 : r1);
 }
 
+// max of two logits (finite or -inf) as one median-of-three against +inf held in a register
+// (the compiler turns a median against a literal +inf back into a max that first quiets NaNs)
+__device__ __forceinline__ float max2(float a, float b, float pinf) {
+    return __builtin_amdgcn_fmed3f(a, b, pinf);
+}
+
 template <int D, int BITS, int RP>
 __device__ __forceinline__ void round_fast(const FastPair<D, BITS>* P, const uint32_t* qf,
-                                           uint32_t* ks_lds, int lane, float scale_log2,
-                                           WaveState<D>& st) {
+                                           uint32_t* ks_lds, int lane, int bp16, int bp32, float pinf,
+                                           float scale_log2, WaveState<D>& st) {
     const int G = lane >> 4;
     const bool side = (lane & 8) != 0;
     // stage the K scales of the round's pages (a wave's LDS requests complete in order; the
@@ -1106,11 +1068,15 @@ __device__ __forceinline__ void round_fast(const FastPair<D, BITS>* P, const uin
                 if (4 * G + i >= ntok) lg[j][i] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    // the round's maximum per head: both page sides by DPP, the four lane rows by two LDS
+    // permutes whose addresses stay fixed for the chunk
+    float mx = max2(max2(lg[0][0], lg[0][1], pinf), max2(lg[0][2], lg[0][3], pinf), pinf);
 #pragma unroll
-    for (int j = 0; j < RP; ++j) mx = fmaxf(mx, fmaxf(fmaxf(lg[j][0], lg[j][1]), fmaxf(lg[j][2], lg[j][3])));
-    mx = fmaxf(mx, __builtin_bit_cast(float, dpp_ror8(__builtin_bit_cast(uint32_t, mx))));
-    mx = rows_max(mx);
+    for (int j = 1; j < RP; ++j)
+        mx = max2(mx, max2(max2(lg[j][0], lg[j][1], pinf), max2(lg[j][2], lg[j][3], pinf), pinf), pinf);
+    mx = max2(mx, __builtin_bit_cast(float, dpp_ror8(__builtin_bit_cast(uint32_t, mx))), pinf);
+    mx = max2(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(bp16, __builtin_bit_cast(int, mx))), pinf);
+    mx = max2(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(bp32, __builtin_bit_cast(int, mx))), pinf);
     if (__builtin_amdgcn_ballot_w64(mx > st.m)) {            // finite: the round holds a token
         const float m_new = fmaxf(st.m, mx + kLazy);
         const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);   // 0 on the first round
@@ -1129,7 +1095,7 @@ __device__ __forceinline__ void round_fast(const FastPair<D, BITS>* P, const uin
                                        P[j].ntok_a < kPage || P[j].ntok_b < kPage,
                                        side ? P[j].ntok_b : P[j].ntok_a, G);
         // V codes as exact fp16 integers, decoded like the K codes (the two word layouts put
-        // codes in the same positions); this loop's o is therefore in plain units
+        // codes in the same positions)
         uint32_t va[D / 8], vb[D / 8];
         unpack_k_fast<D, BITS>(P[j].va, va);
         unpack_k_fast<D, BITS>(P[j].vb, vb);
@@ -1149,6 +1115,9 @@ __device__ __forceinline__ void wave_chunk_fast(const uint8_t* base, uint32_t hv
     const int nr = (nq + RP - 1) / RP;
     const bool side = (lane & 8) != 0;
     const LaneOffsets lo = lane_offsets<D, BITS>(lane);
+    const int bp16 = (lane ^ 16) << 2, bp32 = (lane ^ 32) << 2;   // row-exchange addresses
+    float pinf;
+    asm("v_mov_b32 %0, 0x7f800000" : "=v"(pinf));
     FastPair<D, BITS> b0[RP], b1[RP];
 #pragma unroll
     for (int j = 0; j < RP; ++j)
@@ -1159,19 +1128,16 @@ __device__ __forceinline__ void wave_chunk_fast(const uint8_t* base, uint32_t hv
             for (int j = 0; j < RP; ++j)
                 load_pair_fast<D, BITS>(base, hv, H, kv, cb, npg, (r + 1) * RP + j, nq, ctx, lo, side, b1[j]);
         }
-        round_fast<D, BITS, RP>(b0, qf, ks_lds, lane, scale_log2, st);
+        round_fast<D, BITS, RP>(b0, qf, ks_lds, lane, bp16, bp32, pinf, scale_log2, st);
         if (r + 1 >= nr) break;
         if (r + 2 < nr) {
 #pragma unroll
             for (int j = 0; j < RP; ++j)
                 load_pair_fast<D, BITS>(base, hv, H, kv, cb, npg, (r + 2) * RP + j, nq, ctx, lo, side, b0[j]);
         }
-        round_fast<D, BITS, RP>(b1, qf, ks_lds, lane, scale_log2, st);
+        round_fast<D, BITS, RP>(b1, qf, ks_lds, lane, bp16, bp32, pinf, scale_log2, st);
         if (r + 2 >= nr) break;
     }
-    // to the 2^-24 units the other loops keep (their V codes are fp16 subnormals); exact
-#pragma unroll
-    for (int k = 0; k < D / 16; ++k) st.o[k] *= 1.0f / kTwo24;
 }
 
 // HALF: the group has at most 8 query heads (see process_pair_half). FUSED: the kernel first
@@ -1311,7 +1277,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
         }
     }
 
-    // ---- this wave's partial -> LDS; the V codes carried the 2^-24 of their subnormal form
+    // ---- this wave's partial -> LDS
     float lsum = st.l;
     if constexpr (HALF) {                              // fold columns 8..15 into 0..7
         lsum += __builtin_bit_cast(float, dpp_ror8(__builtin_bit_cast(uint32_t, lsum)));
@@ -1338,7 +1304,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
 #pragma unroll
             for (int k4 = 0; k4 < D / 64; ++k4)
                 *reinterpret_cast<float4v*>(&lds_o[wave][h][G * (D / 4) + r * (D / 16) + 4 * k4]) =
-                    float4v{st.o[4 * k4][r], st.o[4 * k4 + 1][r], st.o[4 * k4 + 2][r], st.o[4 * k4 + 3][r]} * kTwo24;
+                    float4v{st.o[4 * k4][r], st.o[4 * k4 + 1][r], st.o[4 * k4 + 2][r], st.o[4 * k4 + 3][r]};
     }
     __syncthreads();
 

@@ -168,14 +168,19 @@ def test_many_page_pairs_per_wave(hq, hkv, d, mix):
         assert err.max() <= ATTN_TOL, (pps, err.max())
 
 
-@pytest.mark.parametrize("tier", [0, 1, 2])
+@pytest.mark.parametrize("tier", [0, 1, 2, "mix"])
 @pytest.mark.parametrize("direction", ["rising", "falling"])
 def test_logits_rising_or_falling_across_pages(tier, direction):
     """the running maximum of the page loop: keys whose logit climbs by ~6 (log2 units) every
-    page, so the maximum is raised in every round, and the reverse order, where it never is"""
+    page, so the maximum is raised in every round, and the reverse order, where it never is.
+    One key channel is hundreds of times larger than the rest, so every logit is a large term
+    plus small ones: products of very different sizes meet in each MFMA. "mix" cycles the page
+    widths INT2, INT4, INT8, FP16 (the general loops)."""
     case_banner(f"{direction} logits, tier {tier}")
+    tiers = [p % 4 for p in range(44)] if tier == "mix" else [tier] * 44
+    seed = 3 if tier == "mix" else tier
     N = 700
-    g = np.random.default_rng(31 + tier)
+    g = np.random.default_rng(31 + seed)
     ramp = np.arange(N, dtype=np.float32)           # logit +0.25 a token: ~5.8 log2 units a page
     if direction == "falling":
         ramp = ramp[::-1].copy()
@@ -183,7 +188,7 @@ def test_logits_rising_or_falling_across_pages(tier, direction):
     K[:, :, :, 0] += ramp[None, :, None]
     K = K.astype(np.float16).view(np.uint16)
     V = synth.normal_f16(g, (1, N, 2, 64))
-    L = LayerPair(8, 2, 64, 1, 46, [[tier] * 44], seed=tier)
+    L = LayerPair(8, 2, 64, 1, 46, [tiers], seed=seed)
     L.write(K, V)
     qf = np.zeros((1, 8, 64), dtype=np.float32)
     qf[:, :, 0] = 2.0
