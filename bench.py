@@ -38,8 +38,8 @@ ATTN_SRC = [os.path.join(ROOT, "mixed_precision_quantized_kv_amd", "csrc", f)
 # (FETCH_SIZE, WRITE_SIZE) scaled by the same counters' reading for a plain copy kernel of known
 # size. It describes the kernel sources with this digest only; after any change to them
 # the bench reports traffic as null until the counters are taken again.
-ATTN_TRAFFIC = {"source_sha256": "cef2cc24db1bf7ef974d81cd16a52093466c012dc590f9d73b047ff9c26b9a8f",
-                "bytes_per_launch": 45333829,
+ATTN_TRAFFIC = {"source_sha256": "7f3d7be3f2684748ba6f15d663948feb5dfbab22edbee521ba3b8904429f1de5",
+                "bytes_per_launch": 45306425,
                 # the bench's algorithmic bytes per launch at the counter run's contexts
                 "algorithmic_bytes_per_launch": 41804027}
 
