@@ -1068,16 +1068,18 @@ __device__ __forceinline__ void round_fast(const FastPair<D, BITS>* P, const uin
                 if (4 * G + i >= ntok) lg[j][i] = -INFINITY;
         }
     }
-    // the round's maximum per head: both page sides by DPP, the four lane rows by two LDS
-    // permutes whose addresses stay fixed for the chunk
+    // The reference m of a head is the same in all eight of its lanes, so a logit above it
+    // shows in its own lane: the per-head maximum (both page sides by DPP, the four lane rows
+    // by two LDS permutes whose addresses stay fixed for the chunk) is formed only in a round
+    // that raises some m -- the first, and then rarely.
     float mx = max2(max2(lg[0][0], lg[0][1], pinf), max2(lg[0][2], lg[0][3], pinf), pinf);
 #pragma unroll
     for (int j = 1; j < RP; ++j)
         mx = max2(mx, max2(max2(lg[j][0], lg[j][1], pinf), max2(lg[j][2], lg[j][3], pinf), pinf), pinf);
-    mx = max2(mx, __builtin_bit_cast(float, dpp_ror8(__builtin_bit_cast(uint32_t, mx))), pinf);
-    mx = max2(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(bp16, __builtin_bit_cast(int, mx))), pinf);
-    mx = max2(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(bp32, __builtin_bit_cast(int, mx))), pinf);
     if (__builtin_amdgcn_ballot_w64(mx > st.m)) {            // finite: the round holds a token
+        mx = max2(mx, __builtin_bit_cast(float, dpp_ror8(__builtin_bit_cast(uint32_t, mx))), pinf);
+        mx = max2(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(bp16, __builtin_bit_cast(int, mx))), pinf);
+        mx = max2(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(bp32, __builtin_bit_cast(int, mx))), pinf);
         const float m_new = fmaxf(st.m, mx + kLazy);
         const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);   // 0 on the first round
         st.l *= alpha;
