@@ -795,32 +795,31 @@ __device__ __forceinline__ void wave_chunk_mixed(const PageSrc& src, int kv, int
 }
 
 // ---------------------------------------------------------------- uniform-width fast path
-// A wave's chunk of pages of one width, for groups of at most 8 query heads, in rounds of RP
-// page pairs. The loads of round r+1 are in flight while round r is computed; inside a round
-// every QK product comes first, then one update of the running maxima, then every PV product,
-// so the MFMA chains of one pair overlap the unpacking of the next and no branch splits the
-// round. As in process_pair_half, lanes with h = lane % 16 < 8 own page A of a pair for head h,
+// A wave's chunk of pages of one width, for groups of at most 8 query heads, a page pair per
+// round. The loads of the next DEPTH-1 pairs are in flight while a pair is computed; inside a
+// round the QK products come first, then the update of the running maxima, then the PV
+// products. As in process_pair_half, lanes with h = lane % 16 < 8 own page A of a pair for head h,
 // lanes h >= 8 page B for head h - 8. The PV product instead puts the two fp16 parts of the
 // weights in the two column halves -- columns 0..7 the high parts of heads 0..7 over both
 // pages' tokens, columns 8..15 the low parts -- so one MFMA per channel chunk covers a pair;
 // the halves fold at the end exactly as the page halves of process_pair_half do.
 //
-// The running maximum is lazy: the reference m sits kLazy (log2 units) above the largest logit
-// seen when it was last raised, so every weight is at most 2^-kLazy <= 1 and the accumulators
-// are rescaled only when a logit exceeds m -- in practice once per chunk.
+// The running maximum is lazy: the reference m is raised only when a logit exceeds it, and then
+// to kLazy (log2 units) above the largest logit seen, so every weight is at most 1 and the
+// accumulators are rescaled only when a logit exceeds m -- in practice about once per chunk.
 constexpr float kLazy = 3.0f;
-#ifndef KVQ_RP2
-#define KVQ_RP2 1
+#ifndef KVQ_DEPTH2
+#define KVQ_DEPTH2 2
 #endif
-#ifndef KVQ_RP4
-#define KVQ_RP4 1
+#ifndef KVQ_DEPTH4
+#define KVQ_DEPTH4 2
 #endif
-#ifndef KVQ_RP8
-#define KVQ_RP8 1
+#ifndef KVQ_DEPTH8
+#define KVQ_DEPTH8 2
 #endif
-constexpr int kRoundPairs2 = KVQ_RP2;   // page pairs per round, by width
-constexpr int kRoundPairs4 = KVQ_RP4;
-constexpr int kRoundPairs8 = KVQ_RP8;
+constexpr int kDepth2 = KVQ_DEPTH2;     // page pairs in flight per wave, by width
+constexpr int kDepth4 = KVQ_DEPTH4;
+constexpr int kDepth8 = KVQ_DEPTH8;
 
 template <int D, int BITS>
 struct FastPair {
@@ -1108,37 +1107,33 @@ __device__ __forceinline__ void round_fast(const FastPair<D, BITS>* P, const uin
     }
 }
 
-template <int D, int BITS, int RP>
+template <int D, int BITS, int DEPTH>
 __device__ __forceinline__ void wave_chunk_fast(const uint8_t* base, uint32_t hv, int H, int kv,
                                                 int cb, int npg, int ctx, int lane,
                                                 const uint32_t* qf, uint32_t* ks_lds,
                                                 float scale_log2, WaveState<D>& st) {
     const int nq = (npg + 1) / 2;
-    const int nr = (nq + RP - 1) / RP;
     const bool side = (lane & 8) != 0;
     const LaneOffsets lo = lane_offsets<D, BITS>(lane);
     const int bp16 = (lane ^ 16) << 2, bp32 = (lane ^ 32) << 2;   // row-exchange addresses
     float pinf;
     asm("v_mov_b32 %0, 0x7f800000" : "=v"(pinf));
-    FastPair<D, BITS> b0[RP], b1[RP];
+    // DEPTH buffers in rotation: pair q is computed while pairs q+1 .. q+DEPTH-1 load; the
+    // rotation is unrolled so every buffer index is a constant
+    FastPair<D, BITS> b[DEPTH];
 #pragma unroll
-    for (int j = 0; j < RP; ++j)
-        load_pair_fast<D, BITS>(base, hv, H, kv, cb, npg, j, nq, ctx, lo, side, b0[j]);
-    for (int r = 0;; r += 2) {
-        if (r + 1 < nr) {
+    for (int j = 0; j < DEPTH - 1; ++j)
+        if (j < nq) load_pair_fast<D, BITS>(base, hv, H, kv, cb, npg, j, nq, ctx, lo, side, b[j]);
+    for (int r = 0;; r += DEPTH) {
 #pragma unroll
-            for (int j = 0; j < RP; ++j)
-                load_pair_fast<D, BITS>(base, hv, H, kv, cb, npg, (r + 1) * RP + j, nq, ctx, lo, side, b1[j]);
+        for (int i = 0; i < DEPTH; ++i) {
+            const int q = r + i;
+            if (q + DEPTH - 1 < nq)
+                load_pair_fast<D, BITS>(base, hv, H, kv, cb, npg, q + DEPTH - 1, nq, ctx, lo, side,
+                                        b[(i + DEPTH - 1) % DEPTH]);
+            round_fast<D, BITS, 1>(&b[i], qf, ks_lds, lane, bp16, bp32, pinf, scale_log2, st);
+            if (q + 1 >= nq) return;
         }
-        round_fast<D, BITS, RP>(b0, qf, ks_lds, lane, bp16, bp32, pinf, scale_log2, st);
-        if (r + 1 >= nr) break;
-        if (r + 2 < nr) {
-#pragma unroll
-            for (int j = 0; j < RP; ++j)
-                load_pair_fast<D, BITS>(base, hv, H, kv, cb, npg, (r + 2) * RP + j, nq, ctx, lo, side, b0[j]);
-        }
-        round_fast<D, BITS, RP>(b1, qf, ks_lds, lane, bp16, bp32, pinf, scale_log2, st);
-        if (r + 2 >= nr) break;
     }
 }
 
@@ -1252,14 +1247,14 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
         }
         uint32_t* ks_round = reinterpret_cast<uint32_t*>(&lds_o[wave][0][0]);  // free until the merge
         if (HALF && uniform && tier0 == 0)
-            wave_chunk_fast<D, 2, kRoundPairs2>(a.pools.base[0], hv, a.H, kv, cb, npg, ctx, lane, qf,
-                                                ks_round, a.scale_log2, st);
+            wave_chunk_fast<D, 2, kDepth2>(a.pools.base[0], hv, a.H, kv, cb, npg, ctx, lane, qf,
+                                           ks_round, a.scale_log2, st);
         else if (HALF && uniform && tier0 == 1)
-            wave_chunk_fast<D, 4, kRoundPairs4>(a.pools.base[1], hv, a.H, kv, cb, npg, ctx, lane, qf,
-                                                ks_round, a.scale_log2, st);
+            wave_chunk_fast<D, 4, kDepth4>(a.pools.base[1], hv, a.H, kv, cb, npg, ctx, lane, qf,
+                                           ks_round, a.scale_log2, st);
         else if (HALF && uniform && tier0 == 2)
-            wave_chunk_fast<D, 8, kRoundPairs8>(a.pools.base[2], hv, a.H, kv, cb, npg, ctx, lane, qf,
-                                                ks_round, a.scale_log2, st);
+            wave_chunk_fast<D, 8, kDepth8>(a.pools.base[2], hv, a.H, kv, cb, npg, ctx, lane, qf,
+                                           ks_round, a.scale_log2, st);
         else if (uniform && tier0 == 0)
             wave_chunk_uniform<D, 2, 2, HALF>(a.pools.base[0], hv, a.H, kv, cb, npg, ctx, lane, qf, ks_slot,
                                      a.scale_log2, st);
@@ -1361,11 +1356,12 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
     // Output slot `slot` (four channels of one head) is summed over the splits by `parts`
     // threads, each over a contiguous run of at most kBatch splits per round. Every thread
     // issues its first round of partial loads together with the (max, sum) pairs, so the merge
-    // costs one memory round trip in the common case; loads past a thread's range re-read a
-    // valid entry and are ignored. Each thread then forms its head's split weights itself from
-    // the pairs staged in LDS (all threads of a head read the same words), and the splits are
-    // always combined in index order.
+    // costs one memory round trip in the common case; loads past a thread's range take an
+    // offset outside the workspace and read zero without touching memory. The split weights
+    // are formed once per head from the pairs staged in LDS, and the splits are always
+    // combined in index order.
     constexpr int kBatch = 16;
+    constexpr uint32_t kNowhere = 0xffffff00u;           // past num_records for every dword
     const int parts = max(1, min(nsplit, (kWaves * 64) / nslot));
     const int per_part = (nsplit + parts - 1) / parts;
     const bool has_job = tid < nslot * parts;
@@ -1378,7 +1374,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
 #pragma unroll
     for (int i = 0; i < kBatch; ++i)
         buf[i] = __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(
-            o_rsrc, (min(k0 + i, nsplit - 1) * grp * D + slot * 4) * 4, 0, kSc1));
+            o_rsrc, k0 + i < k1 ? (uint32_t)(((k0 + i) * grp * D + slot * 4) * 4) : kNowhere, 0, kSc1));
     const int npair = nsplit * grp;
     for (int i = tid; i < npair; i += kWaves * 64) {
         const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(ml_rsrc, i * 8, 0, kSc1));
@@ -1410,7 +1406,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
 #pragma unroll
         for (int i = 0; i < kBatch; ++i)
             buf[i] = __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(
-                o_rsrc, (min(kb + i, nsplit - 1) * grp * D + slot * 4) * 4, 0, kSc1));
+                o_rsrc, kb + i < k1 ? (uint32_t)(((kb + i) * grp * D + slot * 4) * 4) : kNowhere, 0, kSc1));
 #pragma unroll
         for (int i = 0; i < kBatch; ++i)
             if (kb + i < k1) acc += lds_ml[hh][kb + i].x * buf[i];
