@@ -357,8 +357,8 @@ def run(args):
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "decode_attn_kernel<128> (unfused)" if unfused else
-                      "decode_attn_kernel<128> fused with the write (kv_decode_step)",
+            "kernel": f"decode_attn_kernel<{w.head_dim}> (unfused)" if unfused else
+                      f"decode_attn_kernel<{w.head_dim}> fused with the write (kv_decode_step)",
             "bytes_per_launch": int(avg_launch_bytes),
             "traffic_over_algorithmic": (round(traffic / ATTN_TRAFFIC["algorithmic_bytes_per_launch"], 4)
                                          if traffic else None),
