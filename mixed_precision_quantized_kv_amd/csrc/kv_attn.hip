@@ -1154,7 +1154,11 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
                                                                   int pps, int Hq, int grp,
                                                                   AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t lds_ks[kWaves][2][64];
-    __shared__ __attribute__((aligned(16))) float lds_o[kWaves][kMaxGroup][D];
+    // per-wave partials, one padded row per head: channel c of head h sits at h*kORow + c +
+    // 4*(c/32), so the float4 writes of a wave's 64 lanes (16 heads x 4 channel quarters) spread
+    // over all LDS banks instead of landing on the same four
+    constexpr int kORow = D + (D / 32) * 4 + 4;
+    __shared__ __attribute__((aligned(16))) float lds_o[kWaves][kMaxGroup * kORow];
     __shared__ float lds_m[kWaves][kMaxGroup];
     __shared__ float lds_l[kWaves][kMaxGroup];
     __shared__ float2 lds_ml[kMaxGroup][kMaxSplits]; // (max, sum) of every split in the final merge
@@ -1245,7 +1249,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
             tier0 = (int)((uint32_t)__builtin_amdgcn_readfirstlane((int)hv) >> 30);
             uniform = __builtin_amdgcn_ballot_w64((int)(hv >> 30) != tier0) == 0;
         }
-        uint32_t* ks_round = reinterpret_cast<uint32_t*>(&lds_o[wave][0][0]);  // free until the merge
+        uint32_t* ks_round = reinterpret_cast<uint32_t*>(&lds_o[wave][0]);  // free until the merge
         if (HALF && uniform && tier0 == 0)
             wave_chunk_fast<D, 2, kDepth2>(a.pools.base[0], hv, a.H, kv, cb, npg, ctx, lane, qf,
                                            ks_round, a.scale_log2, st);
@@ -1300,7 +1304,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
         for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int k4 = 0; k4 < D / 64; ++k4)
-                *reinterpret_cast<float4v*>(&lds_o[wave][h][G * (D / 4) + r * (D / 16) + 4 * k4]) =
+                *reinterpret_cast<float4v*>(&lds_o[wave][h * kORow + G * (D / 4) + r * (D / 16) + 4 * k4 +
+                                                         4 * ((G * (D / 4) + r * (D / 16)) / 32)]) =
                     float4v{st.o[4 * k4][r], st.o[4 * k4 + 1][r], st.o[4 * k4 + 2][r], st.o[4 * k4 + 3][r]};
     }
     __syncthreads();
@@ -1326,7 +1331,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
         for (int w = 0; w < kWaves; ++w) {
             const float mw = lds_m[w][hh];
             const float e = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-            acc += e * *reinterpret_cast<const float4v*>(&lds_o[w][hh][4 * c4]);
+            acc += e * *reinterpret_cast<const float4v*>(&lds_o[w][hh * kORow + 4 * c4 + 4 * (c4 / 8)]);
             L += e * lds_l[w][hh];
         }
         if (single) {
@@ -1411,7 +1416,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
         for (int i = 0; i < kBatch; ++i)
             if (kb + i < k1) acc += lds_ml[hh][kb + i].x * buf[i];
     }
-    float4v* part_acc = reinterpret_cast<float4v*>(&lds_o[0][0][0]);   // [parts][slots]
+    float4v* part_acc = reinterpret_cast<float4v*>(&lds_o[0][0]);   // [parts][slots]
     if (has_job) part_acc[pidx * nslot + slot] = acc;
     __syncthreads();
     if (tid < nslot) {
