@@ -944,14 +944,25 @@ __device__ __forceinline__ uint32_t dpp_ror8(uint32_t x) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xf, 0xf, false);
 }
 
-// the K scales of page slot `slot` of the round staged in LDS: D/8 dwords of channel group G
+// The K scales of a round's pages staged in LDS: slot t holds a page's D/2 scale dwords, the
+// D/8 dwords of channel quarter G at t*kKsSlot + G*kKsQuarter. The padding puts the four
+// quarters and the two slots of a pair in different banks, so the quarter reads of a wave (all
+// lanes of a quarter read the same words) do not conflict.
+template <int D> constexpr int kKsQuarter = D / 8 + 4;
+template <int D> constexpr int kKsSlot = 4 * kKsQuarter<D>;     // = 16 (mod 32) for D = 64, 128
+template <int D>
+__device__ __forceinline__ void stage_kscale(uint32_t* ks_lds, int slot, int lane, uint32_t v) {
+    const int d = lane & (D / 2 - 1);                            // the lane's scale dword
+    ks_lds[slot * kKsSlot<D> + (d / (D / 8)) * kKsQuarter<D> + d % (D / 8)] = v;
+}
 template <int D>
 __device__ __forceinline__ void read_kscales(const uint32_t* ks_lds, int slot, int G, uint32_t* ks) {
-    const uint32_t* src = ks_lds + slot * 64 + G * (D / 8);
+    const uint32_t* src = static_cast<const uint32_t*>(
+        __builtin_assume_aligned(ks_lds + slot * kKsSlot<D> + G * kKsQuarter<D>, 16));
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) {
-        const uint4 v = *reinterpret_cast<const uint4*>(src + 4 * i);
-        ks[4 * i] = v.x; ks[4 * i + 1] = v.y; ks[4 * i + 2] = v.z; ks[4 * i + 3] = v.w;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src + 4 * i);
+        ks[4 * i] = v[0]; ks[4 * i + 1] = v[1]; ks[4 * i + 2] = v[2]; ks[4 * i + 3] = v[3];
     }
 }
 
@@ -1052,8 +1063,8 @@ __device__ __forceinline__ void round_fast(const FastPair<D, BITS>* P, const uin
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int j = 0; j < RP; ++j) {
-        ks_lds[(2 * j) * 64 + lane] = P[j].ksa;
-        ks_lds[(2 * j + 1) * 64 + lane] = P[j].ksb;
+        stage_kscale<D>(ks_lds, 2 * j, lane, P[j].ksa);
+        stage_kscale<D>(ks_lds, 2 * j + 1, lane, P[j].ksb);
     }
     __builtin_amdgcn_wave_barrier();
     float4v lg[RP];
