@@ -1035,11 +1035,15 @@ __device__ __forceinline__ half8 pair_weights(const float* p, uint32_t vs0, uint
         for (int i = 0; i < 4; ++i)
             if (4 * G + i >= ntok) w[i] = 0.f;
     }
-    half2v h01, h23, l01, l23;
-    h01[0] = (_Float16)w[0]; h01[1] = (_Float16)w[1];
-    h23[0] = (_Float16)w[2]; h23[1] = (_Float16)w[3];
-    l01[0] = (_Float16)(w[0] - (float)h01[0]); l01[1] = (_Float16)(w[1] - (float)h01[1]);
-    l23[0] = (_Float16)(w[2] - (float)h23[0]); l23[1] = (_Float16)(w[3] - (float)h23[1]);
+    // hi = w rounded toward zero to fp16 (two per instruction); lo = w - hi, exact in fp32 and
+    // then rounded to fp16, one mixed-precision fused multiply-add each
+    const half2v h01 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w[0], w[1]));
+    const half2v h23 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(w[2], w[3]));
+    half2v l01, l23;
+    l01[0] = (_Float16)__builtin_fmaf((float)h01[0], -1.0f, w[0]);
+    l01[1] = (_Float16)__builtin_fmaf((float)h01[1], -1.0f, w[1]);
+    l23[0] = (_Float16)__builtin_fmaf((float)h23[0], -1.0f, w[2]);
+    l23[1] = (_Float16)__builtin_fmaf((float)h23[1], -1.0f, w[3]);
     const uint32_t H0 = __builtin_bit_cast(uint32_t, h01), H1 = __builtin_bit_cast(uint32_t, h23);
     const uint32_t L0 = __builtin_bit_cast(uint32_t, l01), L1 = __builtin_bit_cast(uint32_t, l23);
     const uint32_t r0 = dpp_ror8(side ? H0 : L0), r1 = dpp_ror8(side ? H1 : L1);
