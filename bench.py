@@ -209,9 +209,15 @@ def run(args):
     ctx_all = (pos_all + nn).contiguous()
     scale = 1.0 / math.sqrt(w.head_dim)
     # the split plan for the batch's lengths at the first timed step (the library's plan for
-    # known lengths: one round for equal lengths, smaller balanced splits for a ragged batch)
-    pps = args.pages_per_split or kvq.kv_decode_pages_per_split_for(
-        m.g, (m.lens0 + args.warmup * nn).astype(np.int32))
+    # known lengths: one round for equal lengths, smaller balanced splits for a ragged batch; the
+    # fused step's plan also keeps the last split, which writes, shorter)
+    if args.pages_per_split:
+        pps = args.pages_per_split
+    elif unfused:
+        pps = kvq.kv_decode_pages_per_split_for(m.g, (m.lens0 + args.warmup * nn).astype(np.int32))
+    else:
+        pps = kvq.kv_decode_step_pages_per_split_for(
+            m.g, (m.lens0 - 1 + args.warmup * nn).astype(np.int32), nn)
     wsb = kvq.kv_decode_workspace_bytes(m.g, B, m.max_ctx, pps)
     ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
     out = torch.empty((B, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)

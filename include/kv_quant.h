@@ -227,6 +227,17 @@ kv_status kv_decode_step(const kv_geometry* g, const kv_layer_pools* pools, cons
                          const uint16_t* v_new, uint16_t* ring, int max_ctx_len, const uint16_t* q,
                          float softmax_scale, float* out, void* workspace,
                          size_t workspace_bytes, int pages_per_split, void* stream);
+/* The split plan for a fused step whose positions are known on the host (pos_host int32
+ * [batch], each >= 0; not retained; n_new as for kv_decode_step): the plan of
+ * kv_decode_pages_per_split_for for the lengths pos + n_new, then -- when n_new > 0 and every
+ * sequence ends in the same split -- with the same split count but longer splits, so that the
+ * last split, whose workgroup also writes the step's tokens (about the loop time of 30 to 50
+ * pages), is 40 pages (at most half a split) shorter than the others. kv_decode_step with
+ * pages_per_split = 0 plans the same way from max_ctx_len; either plan fits the workspace of
+ * kv_decode_workspace_bytes(g, batch, max_ctx_len, 0), since the split count is kept. Returns 0
+ * on invalid arguments. */
+int       kv_decode_step_pages_per_split_for(const kv_geometry* g, int batch, const int32_t* pos_host,
+                                             int n_new);
 
 /* ---------------------------------------------------------------- canary
  * [EchoKV] "Show the math": delta_b = KL(softmax(Q K_ref^T) || softmax(Q quant_b(K_ref)^T)),

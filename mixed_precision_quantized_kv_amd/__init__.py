@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
             "kv_decode_workspace_bytes": (sz, [G, i32, i32, i32]),
             "kv_decode_pages_per_split": (i32, [G, i32, i32]),
             "kv_decode_pages_per_split_for": (i32, [G, i32, P]),
+            "kv_decode_step_pages_per_split_for": (i32, [G, i32, P, i32]),
             "kv_decode_attn": (i32, [G, ctypes.POINTER(LayerPools), P, P, i32, i32, P,
                                      ctypes.c_float, P, P, sz, i32, P]),
             "kv_decode_step": (i32, [G, ctypes.POINTER(LayerPools), P, P, i32, i32, P, P, P, i32,
@@ -181,6 +182,14 @@ def kv_decode_pages_per_split_for(g: Geometry, ctx_len_host) -> int:
     import numpy as np
     a = np.ascontiguousarray(ctx_len_host, dtype=np.int32)
     return lib().kv_decode_pages_per_split_for(ctypes.byref(g), int(a.size), a.ctypes.data)
+
+
+def kv_decode_step_pages_per_split_for(g: Geometry, pos_host, n_new: int) -> int:
+    """split plan of a fused step for known positions (host int32 array, one per sequence)"""
+    import numpy as np
+    a = np.ascontiguousarray(pos_host, dtype=np.int32)
+    return lib().kv_decode_step_pages_per_split_for(ctypes.byref(g), int(a.size), a.ctypes.data,
+                                                    int(n_new))
 
 
 def kv_canary_workspace_bytes(g: Geometry, batch: int) -> int:

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -121,6 +122,23 @@ int auto_pages_per_split(const kv_geometry& g, int batch, int max_pages) {
     pps = std::max<int64_t>(pps, (max_pages + 255) / 256);
     pps += pps & 1;
     return (int)pps;
+}
+
+// The fused step: the workgroup of a sequence's last split also writes the step's tokens
+// before it attends (four memory round trips, about 6 us: the loop time of 30 to 50 pages), so
+// the plan keeps the split count and moves pages out of the last split: pps grows until the
+// last split is at least kWriteReservePages (at most half a split) shorter than the others.
+constexpr int64_t kWriteReservePages = 40;
+
+int step_pages_per_split(int64_t max_pages, int pps) {
+    const int64_t splits = (max_pages + pps - 1) / pps;
+    if (splits < 2) return pps;
+    const int64_t reserve = std::min<int64_t>(kWriteReservePages, pps / 2);
+    int64_t p = (max_pages + reserve + splits - 1) / splits;
+    p += p & 1;
+    p = std::min<int64_t>(p, kMaxPagesPerSplit);
+    if (p <= pps || (max_pages + p - 1) / p != splits) return pps;   // keep the grid
+    return (int)p;
 }
 
 }  // namespace
@@ -362,13 +380,39 @@ int kv_decode_pages_per_split_for(const kv_geometry* g, int batch, const int32_t
     return (int)pps;
 }
 
+int kv_decode_step_pages_per_split_for(const kv_geometry* g, int batch, const int32_t* pos_host,
+                                       int n_new) {
+    if (check_geometry(g) != KV_OK || batch < 1 || batch > g->max_seqs || !pos_host ||
+        n_new < 0 || n_new > g->page_size)
+        return 0;
+    std::vector<int32_t> ctx(batch);
+    int64_t longest = 0, shortest = INT64_MAX;
+    for (int s = 0; s < batch; ++s) {
+        if (pos_host[s] < 0) return 0;
+        const int64_t c = (int64_t)pos_host[s] + n_new;
+        if (c > (int64_t)g->max_pages_per_seq * g->page_size) return 0;
+        ctx[s] = (int32_t)c;
+        longest = std::max(longest, c);
+        shortest = std::min(shortest, c);
+    }
+    const int pps = kv_decode_pages_per_split_for(g, batch, ctx.data());
+    if (pps == 0 || n_new == 0) return pps;
+    // the reserve suits a batch whose sequences end in the same split
+    const int64_t last_pages = (longest + g->page_size - 1) / g->page_size;
+    const int64_t first_pages = (shortest + g->page_size - 1) / g->page_size;
+    if ((last_pages - 1) / pps != (first_pages - 1) / pps) return pps;
+    return step_pages_per_split(last_pages, pps);
+}
+
+// step: the plan of the fused step when the caller leaves it to the library
 static kv_status decode_plan(const kv_geometry* g, int batch, int max_ctx_len, int pps_in,
-                             int* pps, int* splits) {
+                             int* pps, int* splits, bool step = false) {
     if (batch < 1 || batch > g->max_seqs) return fail(KV_EINVAL, "batch %d", batch);
     if (max_ctx_len < 0 || (int64_t)max_ctx_len > (int64_t)g->max_pages_per_seq * g->page_size)
         return fail(KV_EINVAL, "max_ctx_len %d", max_ctx_len);
     const int max_pages = std::max(1, (max_ctx_len + g->page_size - 1) / g->page_size);
     int p = pps_in ? pps_in : auto_pages_per_split(*g, batch, max_pages);
+    if (!pps_in && step) p = step_pages_per_split(max_pages, p);
     if (p < 2 || p % 2 != 0) return fail(KV_EINVAL, "pages_per_split %d: an even number >= 2", p);
     const int s = (max_pages + p - 1) / p;
     if (s > 256) return fail(KV_EINVAL, "pages_per_split %d gives %d splits (max 256)", p, s);
@@ -420,7 +464,7 @@ kv_status kv_decode_step(const kv_geometry* g, const kv_layer_pools* pools, cons
     if (n_new < 0 || n_new > g->page_size)
         return fail(KV_EINVAL, "n_new %d: the fused step writes 0..%d tokens", n_new, g->page_size);
     int pps, splits;
-    if ((st = decode_plan(g, batch, max_ctx_len, pages_per_split, &pps, &splits)) != KV_OK)
+    if ((st = decode_plan(g, batch, max_ctx_len, pages_per_split, &pps, &splits, n_new > 0)) != KV_OK)
         return st;
     if (!bt || !pos || !q || !out || !workspace) return fail(KV_EINVAL, "NULL device pointer");
     if (n_new > 0 && (!k_new || !v_new || !ring)) return fail(KV_EINVAL, "NULL device pointer");

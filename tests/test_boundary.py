@@ -144,6 +144,37 @@ def test_split_plan_for_lengths():
     assert kvq.kv_decode_pages_per_split_for(g5, np.zeros(65, np.int32)) == 0   # batch > max_seqs
 
 
+def test_split_plan_for_fused_step():
+    def splits(pages, pps):
+        return -(-pages // pps)
+    # 8 sequences at 8K + 1: the uniform plan leaves the writing (last) split nearly full
+    g2 = geom(head_dim=128, num_q_heads=32, num_kv_heads=8, max_seqs=8, max_pages_per_seq=600)
+    pos = np.full(8, 8192, dtype=np.int32)
+    base = kvq.kv_decode_pages_per_split_for(g2, pos + 1)
+    pps = kvq.kv_decode_step_pages_per_split_for(g2, pos, 1)
+    pages = (8192 + 1 + 15) // 16
+    assert pps % 2 == 0 and pps > base
+    assert splits(pages, pps) == splits(pages, base)             # same grid
+    last = pages - (splits(pages, pps) - 1) * pps
+    assert 1 <= last <= pps - min(40, base // 2)
+    # a step that writes nothing, or a last split already short, keeps the attention plan
+    assert kvq.kv_decode_step_pages_per_split_for(g2, pos, 0) == kvq.kv_decode_pages_per_split_for(g2, pos)
+    g3 = geom(head_dim=128, num_q_heads=40, num_kv_heads=8, max_seqs=1, max_pages_per_seq=2100)
+    assert (kvq.kv_decode_step_pages_per_split_for(g3, [32768], 1)
+            == kvq.kv_decode_pages_per_split_for(g3, [32769]))
+    # sequences ending in different splits keep the plan for their lengths
+    pos2 = np.array([8192, 2000, 8192, 8192, 8192, 8192, 8192, 8192], dtype=np.int32)
+    assert (kvq.kv_decode_step_pages_per_split_for(g2, pos2, 1)
+            == kvq.kv_decode_pages_per_split_for(g2, pos2 + 1))
+    # the workspace for the plan of max_ctx_len covers the step's plan (same split count)
+    assert (kvq.kv_decode_workspace_bytes(g2, 8, 8193, pps)
+            <= kvq.kv_decode_workspace_bytes(g2, 8, 8193, 0))
+    # invalid arguments
+    assert kvq.kv_decode_step_pages_per_split_for(g2, pos, 17) == 0
+    assert kvq.kv_decode_step_pages_per_split_for(g2, pos, -1) == 0
+    assert kvq.kv_decode_step_pages_per_split_for(g2, np.full(8, -2, np.int32), 1) == 0
+
+
 # ------------------------------------------------------------------ allocator
 def make_alloc(bits=(4, 8), cap=16, seed=1, **kw):
     g = geom(num_layers=len(bits), **kw)
