@@ -49,7 +49,7 @@ def fused_step(L, k_new, v_new, q, pps):
 
 
 @pytest.mark.parametrize("case", ["tiny_token_by_token", "ragged_mixed_n3", "ragged_mixed_n16",
-                                  "split_boundary"])
+                                  "split_boundary", "library_plan"])
 def test_fused_equals_separate(case):
     print(f"\n[case] fused {case}", flush=True)
     if case == "tiny_token_by_token":
@@ -62,17 +62,26 @@ def test_fused_equals_separate(case):
         gt = np.random.default_rng(11)
         tiers = [list(gt.integers(0, 3, size=70)) for _ in lens]
         max_pages = 70
-    else:                                   # the two touched pages fall in different splits
+    elif case == "split_boundary":          # the two touched pages fall in different splits
         hq, hkv, d, lens, pps, nn, steps = 40, 8, 128, [16 * 5 + 10], 2, 10, 1
         tiers = [[0, 1, 2, 0, 1, 2, 0, 1, 2]]
         max_pages = 9
+    else:                   # pages_per_split = 0: the library's fused-step plan (shorter last split)
+        hq, hkv, d, lens, pps, nn, steps = 32, 8, 128, [600] * 8, 0, 1, 2
+        gt = np.random.default_rng(12)
+        tiers = [list(gt.integers(0, 3, size=45)) for _ in lens]
+        max_pages = 45
     A, B, g = make_pair(hq, hkv, d, lens, tiers, max_pages, seed=5)
     for step in range(steps):
         k_new = synth.normal_f16(g, (len(lens), nn, hkv, d))
         v_new = synth.normal_f16(g, (len(lens), nn, hkv, d))
         q = synth.normal_f16(g, (len(lens), hq, d))
+        sep_pps = pps
+        if pps == 0:        # the separate attention at the plan the fused step makes for itself
+            sep_pps = kvq.kv_decode_step_pages_per_split_for(B.g, B.len, nn)
+            assert sep_pps != kvq.kv_decode_pages_per_split_for(B.g, B.len + nn)
         A.write(k_new, v_new)
-        ref_sep, _ = A.attn(q, pages_per_split=pps)
+        ref_sep, _ = A.attn(q, pages_per_split=sep_pps)
         got, ws = fused_step(B, k_new, v_new, q, pps)
         torch.cuda.synchronize()
         for a, b in zip(A.pools_t, B.pools_t):
