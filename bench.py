@@ -192,6 +192,8 @@ def run(args):
     w = synth.WORKLOADS[args.workload]
     L, B, nn = w.num_layers, w.batch, w.new_tokens
     # the fused step writes at most 16 tokens per sequence; wider writes take the two-call step
+    # the fused step takes up to 64 new tokens, but with more than 16 (over two pages, written
+    # two at a time by the last split's workgroup) the separate write launch measures faster
     unfused = args.unfused or nn > 16
     steps_total = args.warmup + args.steps
     t0 = time.time()

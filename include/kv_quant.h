@@ -215,13 +215,13 @@ kv_status kv_decode_attn(const kv_geometry* g, const kv_layer_pools* pools, cons
  * over ctx_len = pos[s] + n_new tokens exactly as kv_decode_attn runs it (same outputs). The
  * workgroup whose split holds a touched page writes it before it reads it; no other workgroup
  * reads that page.
- *   n_new            0 .. page_size (at most two pages per sequence); 0 = attention over pos
+ *   n_new            0 .. 64 (at most five pages per sequence); 0 = attention over pos
  *   pos, k_new, v_new, ring   as for kv_quant_write (k_new, v_new, ring 16-byte aligned)
  *   max_ctx_len      host upper bound on pos[s] + n_new
  *   q, softmax_scale, out, workspace, workspace_bytes, pages_per_split   as for kv_decode_attn
  *                    (the workspace is sized by kv_decode_workspace_bytes(g, batch, max_ctx_len,
  *                    pages_per_split))
- * Errors: as for the two calls it joins; n_new outside 0..page_size is KV_EINVAL. */
+ * Errors: as for the two calls it joins; n_new outside 0..64 is KV_EINVAL. */
 kv_status kv_decode_step(const kv_geometry* g, const kv_layer_pools* pools, const uint32_t* bt,
                          const int32_t* pos, int batch, int n_new, const uint16_t* k_new,
                          const uint16_t* v_new, uint16_t* ring, int max_ctx_len, const uint16_t* q,
@@ -231,8 +231,9 @@ kv_status kv_decode_step(const kv_geometry* g, const kv_layer_pools* pools, cons
  * [batch], each >= 0; not retained; n_new as for kv_decode_step): the plan of
  * kv_decode_pages_per_split_for for the lengths pos + n_new, then -- when n_new > 0 and every
  * sequence ends in the same split -- with the same split count but longer splits, so that the
- * last split, whose workgroup also writes the step's tokens (about the loop time of 30 to 50
- * pages), is 40 pages (at most half a split) shorter than the others. kv_decode_step with
+ * last split, whose workgroup also writes the step's tokens (two pages at a time, each round
+ * about the loop time of 30 to 50 pages), is 40 pages per round (at most half a split) shorter
+ * than the others. kv_decode_step with
  * pages_per_split = 0 plans the same way from max_ctx_len; either plan fits the workspace of
  * kv_decode_workspace_bytes(g, batch, max_ctx_len, 0), since the split count is kept. Returns 0
  * on invalid arguments. */

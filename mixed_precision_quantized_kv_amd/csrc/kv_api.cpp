@@ -125,15 +125,18 @@ int auto_pages_per_split(const kv_geometry& g, int batch, int max_pages) {
 }
 
 // The fused step: the workgroup of a sequence's last split also writes the step's tokens
-// before it attends (four memory round trips, about 6 us: the loop time of 30 to 50 pages), so
-// the plan keeps the split count and moves pages out of the last split: pps grows until the
-// last split is at least kWriteReservePages (at most half a split) shorter than the others.
-constexpr int64_t kWriteReservePages = 40;
+// before it attends (four memory round trips per two pages, about 6 us: the loop time of 30 to
+// 50 pages), so the plan keeps the split count and moves pages out of the last split: pps grows
+// until the last split is kWriteReservePages per round of writes (at most half a split) shorter
+// than the others.
+constexpr int64_t kWriteReservePages = 40;       // per round of two pages written
+constexpr int kMaxFusedNew = 64;                  // new tokens per sequence in one fused step
 
-int step_pages_per_split(int64_t max_pages, int pps) {
+int step_pages_per_split(int64_t max_pages, int pps, int n_new, int page_size) {
     const int64_t splits = (max_pages + pps - 1) / pps;
-    if (splits < 2) return pps;
-    const int64_t reserve = std::min<int64_t>(kWriteReservePages, pps / 2);
+    if (splits < 2 || n_new <= 0) return pps;
+    const int64_t touched = (n_new + page_size - 1) / page_size + 1;   // at most
+    const int64_t reserve = std::min<int64_t>(kWriteReservePages * ((touched + 1) / 2), pps / 2);
     int64_t p = (max_pages + reserve + splits - 1) / splits;
     p += p & 1;
     p = std::min<int64_t>(p, kMaxPagesPerSplit);
@@ -383,7 +386,7 @@ int kv_decode_pages_per_split_for(const kv_geometry* g, int batch, const int32_t
 int kv_decode_step_pages_per_split_for(const kv_geometry* g, int batch, const int32_t* pos_host,
                                        int n_new) {
     if (check_geometry(g) != KV_OK || batch < 1 || batch > g->max_seqs || !pos_host ||
-        n_new < 0 || n_new > g->page_size)
+        n_new < 0 || n_new > kMaxFusedNew)
         return 0;
     std::vector<int32_t> ctx(batch);
     int64_t longest = 0, shortest = INT64_MAX;
@@ -401,18 +404,19 @@ int kv_decode_step_pages_per_split_for(const kv_geometry* g, int batch, const in
     const int64_t last_pages = (longest + g->page_size - 1) / g->page_size;
     const int64_t first_pages = (shortest + g->page_size - 1) / g->page_size;
     if ((last_pages - 1) / pps != (first_pages - 1) / pps) return pps;
-    return step_pages_per_split(last_pages, pps);
+    return step_pages_per_split(last_pages, pps, n_new, g->page_size);
 }
 
-// step: the plan of the fused step when the caller leaves it to the library
+// step_new > 0: the plan of a fused step writing step_new tokens, when the caller leaves the
+// plan to the library
 static kv_status decode_plan(const kv_geometry* g, int batch, int max_ctx_len, int pps_in,
-                             int* pps, int* splits, bool step = false) {
+                             int* pps, int* splits, int step_new = 0) {
     if (batch < 1 || batch > g->max_seqs) return fail(KV_EINVAL, "batch %d", batch);
     if (max_ctx_len < 0 || (int64_t)max_ctx_len > (int64_t)g->max_pages_per_seq * g->page_size)
         return fail(KV_EINVAL, "max_ctx_len %d", max_ctx_len);
     const int max_pages = std::max(1, (max_ctx_len + g->page_size - 1) / g->page_size);
     int p = pps_in ? pps_in : auto_pages_per_split(*g, batch, max_pages);
-    if (!pps_in && step) p = step_pages_per_split(max_pages, p);
+    if (!pps_in && step_new > 0) p = step_pages_per_split(max_pages, p, step_new, g->page_size);
     if (p < 2 || p % 2 != 0) return fail(KV_EINVAL, "pages_per_split %d: an even number >= 2", p);
     const int s = (max_pages + p - 1) / p;
     if (s > 256) return fail(KV_EINVAL, "pages_per_split %d gives %d splits (max 256)", p, s);
@@ -461,10 +465,10 @@ kv_status kv_decode_step(const kv_geometry* g, const kv_layer_pools* pools, cons
     kv_status st = check_geometry(g);
     if (st != KV_OK) return st;
     if ((st = check_pools(g, pools)) != KV_OK) return st;
-    if (n_new < 0 || n_new > g->page_size)
-        return fail(KV_EINVAL, "n_new %d: the fused step writes 0..%d tokens", n_new, g->page_size);
+    if (n_new < 0 || n_new > kMaxFusedNew)
+        return fail(KV_EINVAL, "n_new %d: the fused step writes 0..%d tokens", n_new, kMaxFusedNew);
     int pps, splits;
-    if ((st = decode_plan(g, batch, max_ctx_len, pages_per_split, &pps, &splits, n_new > 0)) != KV_OK)
+    if ((st = decode_plan(g, batch, max_ctx_len, pages_per_split, &pps, &splits, n_new)) != KV_OK)
         return st;
     if (!bt || !pos || !q || !out || !workspace) return fail(KV_EINVAL, "NULL device pointer");
     if (n_new > 0 && (!k_new || !v_new || !ring)) return fail(KV_EINVAL, "NULL device pointer");

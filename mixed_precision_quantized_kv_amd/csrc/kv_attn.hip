@@ -1153,10 +1153,10 @@ __device__ __forceinline__ void wave_chunk_fast(const uint8_t* base, uint32_t hv
 }
 
 // HALF: the group has at most 8 query heads (see process_pair_half). FUSED: the kernel first
-// writes the step's new tokens (at most 16 per sequence, so at most two pages): the workgroup
-// whose split holds a touched page quantizes it (256 threads a page) and, for the first page,
-// updates the ring, then makes its writes visible to its own loads and attends over
-// pos + n_new tokens. No other workgroup reads those pages, so one launch does both steps.
+// writes the step's new tokens (at most 64 per sequence, so at most five pages): the workgroup
+// whose split holds a touched page quantizes it (256 threads a page, two pages at a time) and,
+// for the first page, updates the ring, then makes its writes visible to its own loads and
+// attends over pos + n_new tokens. No other workgroup reads those pages, so one launch does both steps.
 template <int D, bool HALF, bool FUSED>
 // The block table, the lengths (ctx_len, or pos for the fused step), q and the shape integers
 // that address them come first as plain arguments: the build preloads the first twelve
@@ -1221,16 +1221,17 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
         __shared__ float chan_max[2][4][D];
         const int p0 = ctx - a.n_new;
         const int first_page = p0 / kPage, last_page = (ctx - 1) / kPage;
-        const bool mine0 = first_page >= pbeg && first_page < pend;
-        const bool mine1 = last_page != first_page && last_page >= pbeg && last_page < pend;
-        if (a.n_new > 0 && (mine0 || mine1)) {          // uniform over the workgroup
-            const int half = tid >> 8;                   // threads 0..255: page 0, 256..511: page 1
-            write_page<D>(a.wr, s, kv, p0, half, tid & 255, half == 0 ? mine0 : mine1,
-                          chan_max[half]);
-            if (mine0) {
-                __syncthreads();                         // the first page's ring reads are done
-                write_ring<D>(a.wr, s, kv, p0, tid, kWaves * 64);
+        // the touched pages this split holds, two at a time (256 threads a page)
+        const int lo_page = max(first_page, pbeg), hi_page = min(last_page, pend - 1);
+        if (a.n_new > 0 && lo_page <= hi_page) {         // uniform over the workgroup
+            const int half = tid >> 8;                   // threads 0..255: even page, 256..511: odd
+            for (int pg = lo_page; pg <= hi_page; pg += 2) {
+                write_page<D>(a.wr, s, kv, p0, pg + half - first_page, tid & 255,
+                              pg + half <= hi_page, chan_max[half]);
+                __syncthreads();                         // chan_max is reused; ring reads done
             }
+            if (lo_page == first_page)                   // the first page's split: the ring
+                write_ring<D>(a.wr, s, kv, p0, tid, kWaves * 64);
             // the writes complete before any wave of this workgroup reads the pages: only this
             // workgroup reads them in this launch, and stores from this compute unit are seen
             // by its own later loads (workgroup scope), so no cache invalidation is needed (an

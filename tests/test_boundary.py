@@ -170,7 +170,10 @@ def test_split_plan_for_fused_step():
     assert (kvq.kv_decode_workspace_bytes(g2, 8, 8193, pps)
             <= kvq.kv_decode_workspace_bytes(g2, 8, 8193, 0))
     # invalid arguments
-    assert kvq.kv_decode_step_pages_per_split_for(g2, pos, 17) == 0
+    assert kvq.kv_decode_step_pages_per_split_for(g2, pos, 65) == 0
+    # 64 new tokens touch up to five pages, written in three rounds: a larger reserve
+    pps64 = kvq.kv_decode_step_pages_per_split_for(g2, pos - 63, 64)
+    assert pps64 >= pps and splits(pages, pps64) == splits(pages, base)
     assert kvq.kv_decode_step_pages_per_split_for(g2, pos, -1) == 0
     assert kvq.kv_decode_step_pages_per_split_for(g2, np.full(8, -2, np.int32), 1) == 0
 

@@ -49,7 +49,7 @@ def fused_step(L, k_new, v_new, q, pps):
 
 
 @pytest.mark.parametrize("case", ["tiny_token_by_token", "ragged_mixed_n3", "ragged_mixed_n16",
-                                  "split_boundary", "library_plan"])
+                                  "ragged_mixed_n64", "split_boundary", "library_plan"])
 def test_fused_equals_separate(case):
     print(f"\n[case] fused {case}", flush=True)
     if case == "tiny_token_by_token":
@@ -58,10 +58,10 @@ def test_fused_equals_separate(case):
         max_pages = 8
     elif case.startswith("ragged"):
         hq, hkv, d, lens, pps, steps = 32, 8, 128, [0, 1, 15, 16, 17, 300, 1000, 777], 16, 3
-        nn = 3 if case.endswith("n3") else 16
+        nn = int(case.split("_n")[1])       # 64: up to five touched pages, in three rounds
         gt = np.random.default_rng(11)
-        tiers = [list(gt.integers(0, 3, size=70)) for _ in lens]
-        max_pages = 70
+        max_pages = 80 if nn > 16 else 70
+        tiers = [list(gt.integers(0, 3, size=max_pages)) for _ in lens]
     elif case == "split_boundary":          # the two touched pages fall in different splits
         hq, hkv, d, lens, pps, nn, steps = 40, 8, 128, [16 * 5 + 10], 2, 10, 1
         tiers = [[0, 1, 2, 0, 1, 2, 0, 1, 2]]
@@ -100,7 +100,7 @@ def test_fused_rejects_too_many_tokens():
     L = LayerPair(8, 2, 64, 1, 8, [[1] * 8], seed=1)
     ws = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda")
     out = torch.empty((1, 8, 64), dtype=torch.float32, device="cuda")
-    z = torch.zeros((1, 17, 2, 64), dtype=torch.float16, device="cuda")
+    z = torch.zeros((1, 65, 2, 64), dtype=torch.float16, device="cuda")
     with pytest.raises(kvq.KVError):
-        kvq.kv_decode_step(L.g, L.pools, L.bt_dev, to_dev_i32(np.zeros(1, np.int32)), 1, 17, z, z,
-                           L.ring, 17, z, 0.1, out, ws, ws.numel(), 0)
+        kvq.kv_decode_step(L.g, L.pools, L.bt_dev, to_dev_i32(np.zeros(1, np.int32)), 1, 65, z, z,
+                           L.ring, 65, z, 0.1, out, ws, ws.numel(), 0)
