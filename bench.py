@@ -38,8 +38,8 @@ ATTN_SRC = [os.path.join(ROOT, "mixed_precision_quantized_kv_amd", "csrc", f)
 # (FETCH_SIZE, WRITE_SIZE) scaled by the same counters' reading for a plain copy kernel of known
 # size. It describes the kernel sources with this digest only; after any change to them
 # the bench reports traffic as null until the counters are taken again.
-ATTN_TRAFFIC = {"source_sha256": "bca75148734e47f55c06f342c22e6edb46528e3830d56f0210dc52ddf96f5ffe",
-                "bytes_per_launch": 45313469,
+ATTN_TRAFFIC = {"source_sha256": "f1d99e7479d0b5bccbe125e35b562c2647fd7e117aa8ca8943616a5744a270ea",
+                "bytes_per_launch": 45319805,
                 # the bench's algorithmic bytes per launch at the counter run's contexts
                 "algorithmic_bytes_per_launch": 41804027}
 
