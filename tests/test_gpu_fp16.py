@@ -102,7 +102,7 @@ def test_fp16_fused_step_equals_separate():
         A.write(K, V, rows=[s])
         B.write(K, V, rows=[s])
     scale = float(np.float32(1.0 / math.sqrt(d)))
-    for step, nn in enumerate([1, 3, 16, 1]):
+    for step, nn in enumerate([1, 3, 16, 64, 1]):       # 64: five pages, three rounds
         k_new = synth.normal_f16(g, (len(lens), nn, hkv, d))
         v_new = synth.normal_f16(g, (len(lens), nn, hkv, d))
         q = synth.normal_f16(g, (len(lens), hq, d))
