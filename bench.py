@@ -425,8 +425,15 @@ def cpu_baseline(w, bits, n_layers: int, reps: int, step_bytes: float) -> dict:
     t_step = t_layer * w.num_layers
     # the oracle's parallel loops run over (sequence, KV head) items
     cores = min(oracle.num_threads(), B * w.num_kv_heads)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(step_bytes / t_step / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle", "steps_per_s": round(1.0 / t_step, 5),
+            "host_cpus": os.cpu_count(), "cpu_model": model, "oracle_threads": oracle.num_threads(),
             "sample": f"{len(layers)} of {w.num_layers} layers, each {reps}x one decode step "
                       f"(write of the new token + attention at context {N}, batch {B}) plus the "
                       f"canary once (charged at 1/{CANARY_EVERY}); per-step time scaled to "
