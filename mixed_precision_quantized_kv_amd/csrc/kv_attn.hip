@@ -968,7 +968,7 @@ __device__ __forceinline__ void read_kscales(const uint32_t* ks_lds, int slot, i
 
 // S^T of one pair for this lane's side (tokens 4G..4G+3 of its page, head h % 8), log2 units
 template <int D, int BITS>
-__device__ __forceinline__ float4v pair_logits(const FastPair<D, BITS>& P, int j, const uint32_t* qf,
+__device__ __forceinline__ float4v pair_logits(const FastPair<D, BITS>& P, const uint32_t* qf,
                                                const uint32_t* ks_lds, int lane, bool side,
                                                float scale_log2) {
     const int G = lane >> 4;
@@ -979,8 +979,8 @@ __device__ __forceinline__ float4v pair_logits(const FastPair<D, BITS>& P, int j
     if constexpr (BITS == 2) {
         // codes -1, 0, 1: code * scale is exact in fp16, so the scales fold into the keys
         uint32_t ksa[D / 8], ksb[D / 8];
-        read_kscales<D>(ks_lds, 2 * j, G, ksa);
-        read_kscales<D>(ks_lds, 2 * j + 1, G, ksb);
+        read_kscales<D>(ks_lds, 0, G, ksa);
+        read_kscales<D>(ks_lds, 1, G, ksb);
 #pragma unroll
         for (int i = 0; i < D / 8; ++i) {
             kfa[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, kfa[i]) * __builtin_bit_cast(half2v, ksa[i]));
@@ -997,7 +997,7 @@ __device__ __forceinline__ float4v pair_logits(const FastPair<D, BITS>& P, int j
     } else {
         // q * Kscale of this lane's side page as fp16 hi + lo, against both pages' keys
         uint32_t ks[D / 8];
-        read_kscales<D>(ks_lds, 2 * j + (side ? 1 : 0), G, ks);
+        read_kscales<D>(ks_lds, side ? 1 : 0, G, ks);
         uint32_t qh[D / 8], ql[D / 8];
 #pragma unroll
         for (int i = 0; i < D / 8; ++i) {
@@ -1056,40 +1056,32 @@ __device__ __forceinline__ float max2(float a, float b, float pinf) {
     return __builtin_amdgcn_fmed3f(a, b, pinf);
 }
 
-template <int D, int BITS, int RP>
-__device__ __forceinline__ void round_fast(const FastPair<D, BITS>* P, const uint32_t* qf,
+// one page pair: QK, the running maxima, then PV
+template <int D, int BITS>
+__device__ __forceinline__ void round_fast(const FastPair<D, BITS>& P, const uint32_t* qf,
                                            uint32_t* ks_lds, int lane, int bp16, int bp32, float pinf,
                                            float scale_log2, WaveState<D>& st) {
     const int G = lane >> 4;
     const bool side = (lane & 8) != 0;
-    // stage the K scales of the round's pages (a wave's LDS requests complete in order; the
-    // wave barriers keep the compiler from moving LDS accesses across them)
+    const bool partial = P.ntok_a < kPage || P.ntok_b < kPage;   // uniform: a partial or absent page
+    const int ntok = side ? P.ntok_b : P.ntok_a;
+    // stage the K scales of the pair's pages (a wave's LDS requests complete in order; the wave
+    // barriers keep the compiler from moving LDS accesses across them)
     __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int j = 0; j < RP; ++j) {
-        stage_kscale<D>(ks_lds, 2 * j, lane, P[j].ksa);
-        stage_kscale<D>(ks_lds, 2 * j + 1, lane, P[j].ksb);
-    }
+    stage_kscale<D>(ks_lds, 0, lane, P.ksa);
+    stage_kscale<D>(ks_lds, 1, lane, P.ksb);
     __builtin_amdgcn_wave_barrier();
-    float4v lg[RP];
+    float4v lg = pair_logits<D, BITS>(P, qf, ks_lds, lane, side, scale_log2);
+    if (partial) {
 #pragma unroll
-    for (int j = 0; j < RP; ++j) {
-        lg[j] = pair_logits<D, BITS>(P[j], j, qf, ks_lds, lane, side, scale_log2);
-        if (P[j].ntok_a < kPage || P[j].ntok_b < kPage) {      // uniform: a partial or absent page
-            const int ntok = side ? P[j].ntok_b : P[j].ntok_a;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (4 * G + i >= ntok) lg[j][i] = -INFINITY;
-        }
+        for (int i = 0; i < 4; ++i)
+            if (4 * G + i >= ntok) lg[i] = -INFINITY;
     }
     // The reference m of a head is the same in all eight of its lanes, so a logit above it
     // shows in its own lane: the per-head maximum (both page sides by DPP, the four lane rows
     // by two LDS permutes whose addresses stay fixed for the chunk) is formed only in a round
     // that raises some m -- the first, and then rarely.
-    float mx = max2(max2(lg[0][0], lg[0][1], pinf), max2(lg[0][2], lg[0][3], pinf), pinf);
-#pragma unroll
-    for (int j = 1; j < RP; ++j)
-        mx = max2(mx, max2(max2(lg[j][0], lg[j][1], pinf), max2(lg[j][2], lg[j][3], pinf), pinf), pinf);
+    float mx = max2(max2(lg[0], lg[1], pinf), max2(lg[2], lg[3], pinf), pinf);
     if (__builtin_amdgcn_ballot_w64(mx > st.m)) {            // finite: the round holds a token
         mx = max2(mx, __builtin_bit_cast(float, dpp_ror8(__builtin_bit_cast(uint32_t, mx))), pinf);
         mx = max2(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(bp16, __builtin_bit_cast(int, mx))), pinf);
@@ -1101,25 +1093,20 @@ __device__ __forceinline__ void round_fast(const FastPair<D, BITS>* P, const uin
         for (int k = 0; k < D / 16; ++k) st.o[k] *= alpha;
         st.m = m_new;
     }
+    float p[4];
 #pragma unroll
-    for (int j = 0; j < RP; ++j) {
-        float p[4];
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(lg[i] - st.m);
+    st.l += (p[0] + p[1]) + (p[2] + p[3]);
+    const half8 wop = pair_weights(p, P.vs0, P.vs1, side, partial, ntok, G);
+    // V codes as exact fp16 integers, decoded like the K codes (the two word layouts put codes
+    // in the same positions)
+    uint32_t va[D / 8], vb[D / 8];
+    unpack_k_fast<D, BITS>(P.va, va);
+    unpack_k_fast<D, BITS>(P.vb, vb);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(lg[j][i] - st.m);
-        st.l += (p[0] + p[1]) + (p[2] + p[3]);
-        const half8 wop = pair_weights(p, P[j].vs0, P[j].vs1, side,
-                                       P[j].ntok_a < kPage || P[j].ntok_b < kPage,
-                                       side ? P[j].ntok_b : P[j].ntok_a, G);
-        // V codes as exact fp16 integers, decoded like the K codes (the two word layouts put
-        // codes in the same positions)
-        uint32_t va[D / 8], vb[D / 8];
-        unpack_k_fast<D, BITS>(P[j].va, va);
-        unpack_k_fast<D, BITS>(P[j].vb, vb);
-#pragma unroll
-        for (int k = 0; k < D / 16; ++k)
-            st.o[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                make_half8(va[2 * k], va[2 * k + 1], vb[2 * k], vb[2 * k + 1]), wop, st.o[k], 0, 0, 0);
-    }
+    for (int k = 0; k < D / 16; ++k)
+        st.o[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            make_half8(va[2 * k], va[2 * k + 1], vb[2 * k], vb[2 * k + 1]), wop, st.o[k], 0, 0, 0);
 }
 
 template <int D, int BITS, int DEPTH>
@@ -1146,7 +1133,7 @@ __device__ __forceinline__ void wave_chunk_fast(const uint8_t* base, uint32_t hv
             if (q + DEPTH - 1 < nq)
                 load_pair_fast<D, BITS>(base, hv, H, kv, cb, npg, q + DEPTH - 1, nq, ctx, lo, side,
                                         b[(i + DEPTH - 1) % DEPTH]);
-            round_fast<D, BITS, 1>(&b[i], qf, ks_lds, lane, bp16, bp32, pinf, scale_log2, st);
+            round_fast<D, BITS>(b[i], qf, ks_lds, lane, bp16, bp32, pinf, scale_log2, st);
             if (q + 1 >= nq) return;
         }
     }
