@@ -38,8 +38,8 @@ ATTN_SRC = [os.path.join(ROOT, "mixed_precision_quantized_kv_amd", "csrc", f)
 # (FETCH_SIZE, WRITE_SIZE) scaled by the same counters' reading for a plain copy kernel of known
 # size. It describes the kernel sources with this digest only; after any change to them
 # the bench reports traffic as null until the counters are taken again.
-ATTN_TRAFFIC = {"source_sha256": "f1d99e7479d0b5bccbe125e35b562c2647fd7e117aa8ca8943616a5744a270ea",
-                "bytes_per_launch": 45319805,
+ATTN_TRAFFIC = {"source_sha256": "5d7f56dd3a095ff1842d94b5ffad4ecaa2679f9855751b56940adee507f5ef5e",
+                "bytes_per_launch": 45318594,
                 # the bench's algorithmic bytes per launch at the counter run's contexts
                 "algorithmic_bytes_per_launch": 41804027}
 
