@@ -198,8 +198,8 @@ size_t    kv_decode_workspace_bytes(const kv_geometry* g, int batch, int max_ctx
 int       kv_decode_pages_per_split(const kv_geometry* g, int batch, int max_ctx_len);
 /* The split plan for known lengths (host int32 [batch], each >= 0; not retained): the plan of
  * kv_decode_pages_per_split for the longest length when the lengths are nearly equal (mean at
- * least 0.9 of the maximum); otherwise splits sized so that the batch's pages make about two
- * workgroups per compute unit, which the hardware scheduler then balances. Returns 0 on
+ * least 0.9 of the maximum); otherwise splits sized so that the batch's pages make about 1.8
+ * workgroups' worth per compute unit, which the hardware scheduler then balances. Returns 0 on
  * invalid arguments. */
 int       kv_decode_pages_per_split_for(const kv_geometry* g, int batch, const int32_t* ctx_len_host);
 kv_status kv_decode_attn(const kv_geometry* g, const kv_layer_pools* pools, const uint32_t* bt,
