@@ -241,26 +241,27 @@ __device__ __forceinline__ float rows_max(float x) {
     return fmaxf(x, __shfl_xor(x, 32, 64));
 }
 // max / sum over all 64 lanes: within each row of 16 by DPP (quad swaps, then rotations by 4
-// and 8), across the rows by two shuffles
+// and 8), across the four rows from one lane of each (readlane: no LDS round trip)
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float lane_value(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
 __device__ __forceinline__ float wave_max_dpp(float x) {
     x = fmaxf(x, dpp_mov<0xB1>(x));      // quad_perm [1,0,3,2]
     x = fmaxf(x, dpp_mov<0x4E>(x));      // quad_perm [2,3,0,1]
     x = fmaxf(x, dpp_mov<0x124>(x));     // row_ror:4
     x = fmaxf(x, dpp_mov<0x128>(x));     // row_ror:8
-    x = fmaxf(x, __shfl_xor(x, 16, 64));
-    return fmaxf(x, __shfl_xor(x, 32, 64));
+    return fmaxf(fmaxf(lane_value(x, 0), lane_value(x, 16)), fmaxf(lane_value(x, 32), lane_value(x, 48)));
 }
 __device__ __forceinline__ float wave_sum_dpp(float x) {
     x += dpp_mov<0xB1>(x);
     x += dpp_mov<0x4E>(x);
     x += dpp_mov<0x124>(x);
     x += dpp_mov<0x128>(x);
-    x += __shfl_xor(x, 16, 64);
-    return x + __shfl_xor(x, 32, 64);
+    return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
 }
 __device__ __forceinline__ float rows_sum(float x) {
     x += __shfl_xor(x, 16, 64);
@@ -757,20 +758,22 @@ __device__ __forceinline__ void wave_chunk_uniform(const uint8_t* base, uint32_t
 #pragma unroll
     for (int d = 0; d < DEPTH - 1; ++d)
         load_pair_t<D, BITS>(base, hv, H, kv, cb, npg, d, nq, ctx, lane, buf[d][0], buf[d][1]);
-    int q = 0;
-    bool done = false;
-    while (!done) {
+    // whole rotations in a loop with one exit and unconditional loads (see wave_chunk_fast),
+    // then the last nq % DEPTH pairs, already loaded
+    const int nfull = nq / DEPTH;
+    for (int r = 0; r < nfull * DEPTH; r += DEPTH) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
-            if (!done) {
-                const int nxt = (d + DEPTH - 1) % DEPTH;
-                load_pair_t<D, BITS>(base, hv, H, kv, cb, npg, q + DEPTH - 1, nq, ctx, lane,
-                                     buf[nxt][0], buf[nxt][1]);
-                run_pair<D, BITS, HALF>(buf[d][0], buf[d][1], qf, ks_slot, lane, scale_log2, st);
-                done = ++q >= nq;
-            }
+            const int nxt = (d + DEPTH - 1) % DEPTH;
+            load_pair_t<D, BITS>(base, hv, H, kv, cb, npg, r + d + DEPTH - 1, nq, ctx, lane,
+                                 buf[nxt][0], buf[nxt][1]);
+            run_pair<D, BITS, HALF>(buf[d][0], buf[d][1], qf, ks_slot, lane, scale_log2, st);
         }
     }
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d)
+        if (d < nq - nfull * DEPTH)
+            run_pair<D, BITS, HALF>(buf[d][0], buf[d][1], qf, ks_slot, lane, scale_log2, st);
 }
 
 // The same for a chunk whose pages may differ in width: handles from the block table, the
@@ -782,16 +785,17 @@ __device__ __forceinline__ void wave_chunk_mixed(const PageSrc& src, int kv, int
                                                  WaveState<D>& st) {
     const int nq = (npg + 1) / 2;
     PageRaw a0, a1, b0, b1;
-    int q = 0;
     load_pair<D>(src, kv, cb, cb + npg, 0, nq, ctx, lane, a0, a1);
-    while (true) {
+    // two pairs per trip, one exit, unconditional loads (see wave_chunk_fast); an odd last
+    // pair is already in a0, a1
+    for (int q = 0; q + 1 < nq; q += 2) {
         load_pair<D>(src, kv, cb, cb + npg, q + 1, nq, ctx, lane, b0, b1);
         run_pair_any<D, HALF>(src, kv, cb + 2 * q, a0, a1, qf, ks_slot, lane, scale_log2, st);
-        if (++q >= nq) break;
-        load_pair<D>(src, kv, cb, cb + npg, q + 1, nq, ctx, lane, a0, a1);
-        run_pair_any<D, HALF>(src, kv, cb + 2 * q, b0, b1, qf, ks_slot, lane, scale_log2, st);
-        if (++q >= nq) break;
+        load_pair<D>(src, kv, cb, cb + npg, q + 2, nq, ctx, lane, a0, a1);
+        run_pair_any<D, HALF>(src, kv, cb + 2 * (q + 1), b0, b1, qf, ks_slot, lane, scale_log2, st);
     }
+    if (nq & 1)
+        run_pair_any<D, HALF>(src, kv, cb + 2 * (nq - 1), a0, a1, qf, ks_slot, lane, scale_log2, st);
 }
 
 // ---------------------------------------------------------------- uniform-width fast path
@@ -1121,22 +1125,29 @@ __device__ __forceinline__ void wave_chunk_fast(const uint8_t* base, uint32_t hv
     float pinf;
     asm("v_mov_b32 %0, 0x7f800000" : "=v"(pinf));
     // DEPTH buffers in rotation: pair q is computed while pairs q+1 .. q+DEPTH-1 load; the
-    // rotation is unrolled so every buffer index is a constant
+    // rotation is unrolled so every buffer index is a constant. The loop runs whole rotations
+    // and has one exit, and every round in it issues its loads, also past the end of the chunk
+    // (they re-read the last pair, which the caches still hold). A load under a branch, or a
+    // second exit, gives the compiler a path into the loop head on which other loads are
+    // pending, and its wait counts there then make each round wait for the next pairs too.
     FastPair<D, BITS> b[DEPTH];
 #pragma unroll
     for (int j = 0; j < DEPTH - 1; ++j)
-        if (j < nq) load_pair_fast<D, BITS>(base, hv, H, kv, cb, npg, j, nq, ctx, lo, side, b[j]);
-    for (int r = 0;; r += DEPTH) {
+        load_pair_fast<D, BITS>(base, hv, H, kv, cb, npg, j, nq, ctx, lo, side, b[j]);
+    const int nfull = nq / DEPTH;
+    for (int r = 0; r < nfull * DEPTH; r += DEPTH) {
 #pragma unroll
         for (int i = 0; i < DEPTH; ++i) {
-            const int q = r + i;
-            if (q + DEPTH - 1 < nq)
-                load_pair_fast<D, BITS>(base, hv, H, kv, cb, npg, q + DEPTH - 1, nq, ctx, lo, side,
-                                        b[(i + DEPTH - 1) % DEPTH]);
+            load_pair_fast<D, BITS>(base, hv, H, kv, cb, npg, r + i + DEPTH - 1, nq, ctx, lo, side,
+                                    b[(i + DEPTH - 1) % DEPTH]);
             round_fast<D, BITS>(b[i], qf, ks_lds, lane, bp16, bp32, pinf, scale_log2, st);
-            if (q + 1 >= nq) return;
         }
     }
+    // the last nq % DEPTH pairs: the rotation has already loaded them into b[0 ..]
+#pragma unroll
+    for (int i = 0; i < DEPTH - 1; ++i)
+        if (i < nq - nfull * DEPTH)
+            round_fast<D, BITS>(b[i], qf, ks_lds, lane, bp16, bp32, pinf, scale_log2, st);
 }
 
 // HALF: the group has at most 8 query heads (see process_pair_half). FUSED: the kernel first
