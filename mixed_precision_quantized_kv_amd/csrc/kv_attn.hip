@@ -50,13 +50,21 @@ constexpr int kWaves = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxSplits = 256;
 
+// The split-ticket counters of different (sequence, KV head) groups sit 256 bytes apart: packed
+// into one line, the tickets of all groups -- taken within a microsecond of each other at the
+// end of a launch -- queue on that one line and the last returns microseconds later.
+#ifndef KVQ_CTR_STRIDE
+#define KVQ_CTR_STRIDE 64
+#endif
+constexpr int kCounterStride = KVQ_CTR_STRIDE;   // uint32 words per counter
+
 struct AttnArgs {
     PoolPtrs pools;
     const uint32_t* bt;
     const int32_t* ctx_len;
     const uint16_t* q;
     float* out;
-    uint32_t* counters;   // [groups]
+    uint32_t* counters;   // [groups][kCounterStride]: one counter per group, each in its own line
     float* ws_ml;         // [groups][splits][group][2] (max, sum) in log2 units
     float* ws_o;          // [groups][splits][group][D]
     int max_pages;
@@ -830,7 +838,7 @@ struct FastPair {
     static constexpr int KW = D * BITS / 128;    // dwords of this lane's K chunk and V chunk
     uint32_t ka[KW], kb[KW], va[KW], vb[KW];
     uint32_t ksa, ksb;                           // K-scale dwords (channels 2*lane, 2*lane+1)
-    uint32_t vs0, vs1;                           // V scales, quad G of this lane's side page
+    u32x2 vsa, vsb;                              // V scales, quad G of pages A and B
     int ntok_a, ntok_b;                          // valid tokens; 0 for an absent page
 };
 
@@ -867,8 +875,26 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
     return o;
 }
 
+template <int KW>
+__device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* w) {
+    if constexpr (KW == 1) {
+        w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    } else if constexpr (KW == 2) {
+        const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        w[0] = x[0]; w[1] = x[1];
+    } else {
+#pragma unroll
+        for (int h = 0; h < KW / 4; ++h) {
+            const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * h, 0, 0);
+            w[4 * h] = x[0]; w[4 * h + 1] = x[1]; w[4 * h + 2] = x[2]; w[4 * h + 3] = x[3];
+        }
+    }
+}
+
 // pair q of a chunk whose handles sit in hv (lane i: page cb + i); pairs past the end reload
-// the last pair and carry no tokens
+// the last pair and carry no tokens. Each page section is read through a buffer resource
+// built in scalar registers, so the lane offsets stay fixed VGPR offsets and no per-load
+// address arithmetic runs on the vector unit.
 template <int D, int BITS>
 __device__ __forceinline__ void load_pair_fast(const uint8_t* base, uint32_t hv, int H, int kv,
                                                int cb, int npg, int q, int nq, int ctx,
@@ -881,17 +907,19 @@ __device__ __forceinline__ void load_pair_fast(const uint8_t* base, uint32_t hv,
     const bool has_b = pa + 1 < npg;
     const uint32_t ia = (uint32_t)__builtin_amdgcn_readlane((int)hv, pa) & 0x3fffffffu;
     const uint32_t ib = (uint32_t)__builtin_amdgcn_readlane((int)hv, has_b ? pa + 1 : pa) & 0x3fffffffu;
-    const uint8_t* sa = base + ((size_t)ia * H + kv) * sec_bytes;
-    const uint8_t* sb = base + ((size_t)ib * H + kv) * sec_bytes;
-    load_words<KW>(sa + lo.k, P.ka);
-    load_words<KW>(sb + lo.k, P.kb);
-    load_words<KW>(sa + lo.v, P.va);
-    load_words<KW>(sb + lo.v, P.vb);
-    P.ksa = *reinterpret_cast<const uint32_t*>(sa + lo.ks);
-    P.ksb = *reinterpret_cast<const uint32_t*>(sb + lo.ks);
-    const uint2 vs = *reinterpret_cast<const uint2*>((side ? sb : sa) + lo.vs);
-    P.vs0 = vs.x;
-    P.vs1 = vs.y;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(base + ((size_t)ia * H + kv) * sec_bytes), (short)0, (int)sec_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(base + ((size_t)ib * H + kv) * sec_bytes), (short)0, (int)sec_bytes, 0x00020000);
+    load_words<KW>(ra, lo.k, P.ka);
+    load_words<KW>(rb, lo.k, P.kb);
+    load_words<KW>(ra, lo.v, P.va);
+    load_words<KW>(rb, lo.v, P.vb);
+    P.ksa = __builtin_amdgcn_raw_buffer_load_b32(ra, lo.ks, 0, 0);
+    P.ksb = __builtin_amdgcn_raw_buffer_load_b32(rb, lo.ks, 0, 0);
+    // the V scales of both pages (one cache line each); the round picks its side's
+    P.vsa = __builtin_amdgcn_raw_buffer_load_b64(ra, lo.vs, 0, 0);
+    P.vsb = __builtin_amdgcn_raw_buffer_load_b64(rb, lo.vs, 0, 0);
     const int page = cb + pa;
     P.ntok_a = real ? min(kPage, ctx - page * kPage) : 0;
     P.ntok_b = real && has_b ? min(kPage, ctx - (page + 1) * kPage) : 0;
@@ -1101,7 +1129,9 @@ __device__ __forceinline__ void round_fast(const FastPair<D, BITS>& P, const uin
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(lg[i] - st.m);
     st.l += (p[0] + p[1]) + (p[2] + p[3]);
-    const half8 wop = pair_weights(p, P.vs0, P.vs1, side, partial, ntok, G);
+    const u32x2 vsa = P.vsa, vsb = P.vsb;          // values, so the selects stay in registers
+    const uint32_t vs0 = side ? vsb[0] : vsa[0], vs1 = side ? vsb[1] : vsa[1];
+    const half8 wop = pair_weights(p, vs0, vs1, side, partial, ntok, G);
     // V codes as exact fp16 integers, decoded like the K codes (the two word layouts put codes
     // in the same positions)
     uint32_t va[D / 8], vb[D / 8];
@@ -1134,13 +1164,18 @@ __device__ __forceinline__ void wave_chunk_fast(const uint8_t* base, uint32_t hv
 #pragma unroll
     for (int j = 0; j < DEPTH - 1; ++j)
         load_pair_fast<D, BITS>(base, hv, H, kv, cb, npg, j, nq, ctx, lo, side, b[j]);
+    // The scheduling barriers keep each round's instructions between its loads and the next
+    // round's: the scheduler would otherwise start decoding the pair just requested inside
+    // this round, and the waits for that data would stall the round.
     const int nfull = nq / DEPTH;
     for (int r = 0; r < nfull * DEPTH; r += DEPTH) {
 #pragma unroll
         for (int i = 0; i < DEPTH; ++i) {
             load_pair_fast<D, BITS>(base, hv, H, kv, cb, npg, r + i + DEPTH - 1, nq, ctx, lo, side,
                                     b[(i + DEPTH - 1) % DEPTH]);
+            __builtin_amdgcn_sched_barrier(0);
             round_fast<D, BITS>(b[i], qf, ks_lds, lane, bp16, bp32, pinf, scale_log2, st);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     // the last nq % DEPTH pairs: the rotation has already loaded them into b[0 ..]
@@ -1367,7 +1402,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0)
-        lds_last = __hip_atomic_fetch_add(&a.counters[group], 1u, __ATOMIC_RELAXED,
+        lds_last = __hip_atomic_fetch_add(&a.counters[group * kCounterStride], 1u, __ATOMIC_RELAXED,
                                           __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(nsplit - 1);
     __syncthreads();
     if (!lds_last) return;
@@ -1441,7 +1476,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
         *reinterpret_cast<float4v*>(a.out + ((size_t)s * a.Hq + kv * grp) * D + tid * 4) = sum * inv;
     }
     if (tid == 0)
-        __hip_atomic_store(&a.counters[group], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.counters[group * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -1449,8 +1484,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
 size_t decode_workspace_bytes(const kv_geometry& g, int batch, int splits) {
     const size_t groups = (size_t)batch * g.num_kv_heads;
     const size_t grp = (size_t)(g.num_q_heads / g.num_kv_heads);
-    size_t bytes = 256;                                           // counters, padded
-    bytes += ((groups * 4 + 255) / 256) * 256;
+    size_t bytes = 256;
+    bytes += groups * kCounterStride * 4;                         // counters, a line each
     bytes += ((groups * splits * grp * 2 * sizeof(float) + 255) / 256) * 256;
     bytes += groups * splits * grp * g.head_dim * sizeof(float);
     return bytes;
@@ -1477,7 +1512,7 @@ AttnArgs attn_args(const kv_geometry& g, PoolPtrs pools, const uint32_t* bt, int
     const size_t groups = (size_t)a.groups;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     a.counters = reinterpret_cast<uint32_t*>(ws);
-    size_t off = ((groups * 4 + 255) / 256) * 256 + 256;
+    size_t off = groups * kCounterStride * 4 + 256;
     a.ws_ml = reinterpret_cast<float*>(ws + off);
     off += ((groups * splits * a.grp * 2 * sizeof(float) + 255) / 256) * 256;
     a.ws_o = reinterpret_cast<float*>(ws + off);
