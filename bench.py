@@ -38,8 +38,8 @@ ATTN_SRC = [os.path.join(ROOT, "mixed_precision_quantized_kv_amd", "csrc", f)
 # (FETCH_SIZE, WRITE_SIZE) scaled by the same counters' reading for a plain copy kernel of known
 # size. It describes the kernel sources with this digest only; after any change to them
 # the bench reports traffic as null until the counters are taken again.
-ATTN_TRAFFIC = {"source_sha256": "5d7f56dd3a095ff1842d94b5ffad4ecaa2679f9855751b56940adee507f5ef5e",
-                "bytes_per_launch": 45318594,
+ATTN_TRAFFIC = {"source_sha256": "ed570fe9480a34bfaa8b3514fbe504a90995c848f2be664ae17c13d1611de9ae",
+                "bytes_per_launch": 45350663,
                 # the bench's algorithmic bytes per launch at the counter run's contexts
                 "algorithmic_bytes_per_launch": 41804027}
 
