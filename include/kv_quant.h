@@ -188,7 +188,9 @@ kv_status kv_quant_write(const kv_geometry* g, const kv_layer_pools* pools, cons
  *   max_ctx_len    host upper bound on ctx_len, sizes the launch (<= max_pages_per_seq * P)
  *   pages_per_split  pages one workgroup reads (even, >= 2); 0 = chosen by the library
  *   workspace  dev, >= kv_decode_workspace_bytes(...) bytes, zero-filled before its first use;
- *              the call leaves it ready for the next call. One workspace per in-flight call.
+ *              the call leaves it ready for the next call on the same geometry, whatever that
+ *              call's batch and lengths (its own size requirement still applies); zero it again
+ *              before using it with another geometry. One workspace per in-flight call.
  * The split-K partials are merged in a fixed order, so results are bitwise reproducible. */
 size_t    kv_decode_workspace_bytes(const kv_geometry* g, int batch, int max_ctx_len,
                                     int pages_per_split);

@@ -1481,11 +1481,18 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
 
 }  // namespace
 
+// Workspace layout: the ticket counters of every (sequence slot, KV head) of the geometry --
+// sized by max_seqs, not by the call's batch, so every call on one geometry finds its counters
+// at the same place, left at zero by the call before -- then the per-split (max, sum) pairs
+// and partial outputs of this call, which each call writes before it reads them.
+static size_t counter_region_bytes(const kv_geometry& g) {
+    return (size_t)g.max_seqs * g.num_kv_heads * kCounterStride * 4 + 256;
+}
+
 size_t decode_workspace_bytes(const kv_geometry& g, int batch, int splits) {
     const size_t groups = (size_t)batch * g.num_kv_heads;
     const size_t grp = (size_t)(g.num_q_heads / g.num_kv_heads);
-    size_t bytes = 256;
-    bytes += groups * kCounterStride * 4;                         // counters, a line each
+    size_t bytes = counter_region_bytes(g);
     bytes += ((groups * splits * grp * 2 * sizeof(float) + 255) / 256) * 256;
     bytes += groups * splits * grp * g.head_dim * sizeof(float);
     return bytes;
@@ -1512,7 +1519,7 @@ AttnArgs attn_args(const kv_geometry& g, PoolPtrs pools, const uint32_t* bt, int
     const size_t groups = (size_t)a.groups;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     a.counters = reinterpret_cast<uint32_t*>(ws);
-    size_t off = groups * kCounterStride * 4 + 256;
+    size_t off = counter_region_bytes(g);
     a.ws_ml = reinterpret_cast<float*>(ws + off);
     off += ((groups * splits * a.grp * 2 * sizeof(float) + 255) / 256) * 256;
     a.ws_o = reinterpret_cast<float*>(ws + off);

@@ -11,7 +11,9 @@ import torch
 
 from mixed_precision_quantized_kv_amd import synth
 
-from gpu_cases import LayerPair, rowwise_rel_err
+import mixed_precision_quantized_kv_amd as kvq
+
+from gpu_cases import LayerPair, rowwise_rel_err, to_dev_f16, to_dev_i32
 
 pytestmark = pytest.mark.gpu
 
@@ -210,6 +212,37 @@ def test_deterministic_and_workspace_reuse():
     b, _ = L.attn(q, pages_per_split=16)
     assert np.array_equal(a, b)
     assert not ws[:256].any()                      # ticket counters are left at zero
+
+
+def test_workspace_reused_across_batch_sizes():
+    """one workspace for calls over 2, 8, 2 and 8 sequences of one geometry: each call finds its
+    split counters where the previous call left them at zero (their place does not move with
+    the batch), and its outputs equal those of a fresh workspace bit for bit"""
+    case_banner("workspace reuse across batch sizes")
+    lens = [3000, 1000, 2500, 17, 4000, 800, 1600, 3333]
+    B, hq, hkv, d = len(lens), 40, 8, 128
+    g = np.random.default_rng(5)
+    L = LayerPair(hq, hkv, d, B, 256, [[1] * 256 for _ in range(B)], seed=5)
+    for s, n in enumerate(lens):
+        L.write(synth.normal_f16(g, (1, n, hkv, d)), synth.normal_f16(g, (1, n, hkv, d)), rows=[s])
+    q = synth.normal_f16(g, (B, hq, d))
+    ctx = np.array(lens, dtype=np.int32)
+    wsb = max(kvq.kv_decode_workspace_bytes(L.g, b, int(ctx.max()), 16) for b in (2, B))
+
+    def call(batch, ws):
+        out = torch.empty((batch, hq, d), dtype=torch.float32, device="cuda")
+        kvq.kv_decode_attn(L.g, L.pools, L.bt_dev, to_dev_i32(ctx[:batch]), batch,
+                           int(ctx[:batch].max()), to_dev_f16(q[:batch]), 1.0 / math.sqrt(d), out,
+                           ws, wsb, 16)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    fresh = {b: call(b, torch.zeros(wsb, dtype=torch.uint8, device="cuda")) for b in (2, B)}
+    ref = L.oracle_attn(q)
+    assert rowwise_rel_err(fresh[B].astype(np.float64), ref).max() <= ATTN_TOL
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    for b in (2, B, 2, B):
+        assert np.array_equal(call(b, ws), fresh[b]), b
 
 
 def test_softmax_scale_zero_and_identical_keys():
