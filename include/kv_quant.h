@@ -252,7 +252,8 @@ int       kv_decode_step_pages_per_split_for(const kv_geometry* g, int batch, co
  *   q        dev fp16 [batch][H_q][D] (16-byte aligned)
  *   kl_out   dev fp32 [3]: mean over batch*H_q rows for b = 2, 4, 8
  *   kl_rows  dev fp32 [batch][H_q][3] or NULL
- *   workspace dev, >= kv_canary_workspace_bytes(g, batch), zero-filled before its first use */
+ *   workspace dev, >= kv_canary_workspace_bytes(g, batch), zero-filled before its first use;
+ *             the call leaves it ready for the next call, whatever that call's batch */
 size_t    kv_canary_workspace_bytes(const kv_geometry* g, int batch);
 kv_status kv_canary_kl(const kv_geometry* g, const uint16_t* ring, const int32_t* seq_len,
                        int batch, const uint16_t* q, float softmax_scale, float* kl_out,

@@ -30,9 +30,13 @@
 namespace kvq {
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kWavesC = kThreads / 64;
 constexpr int kMaxRing = 128;   // largest ring the geometry check accepts
+constexpr int kCtrStride = 64;  // uint32 words between the widths' counters (256 bytes)
+constexpr int kRowBatch = 16;   // row loads a lane has in flight in the final average
+constexpr uint32_t kNowhere = 0xffffff00u;   // a buffer offset past every range: reads zero
 
 struct CanaryArgs {
     const uint16_t* ring;
@@ -41,7 +45,7 @@ struct CanaryArgs {
     float* kl_out;
     float* kl_rows;       // optional
     float* ws_rows;       // [batch][Hq][3]
-    uint32_t* counter;
+    uint32_t* counter;    // [3][kCtrStride]: one ticket counter per width, each in its own line
     int H, Hq, grp, R, batch;
     float scale;
 };
@@ -90,21 +94,36 @@ __global__ __launch_bounds__(kThreads) void canary_kernel(CanaryArgs a) {
     const int s = blockIdx.x / a.H, kv = blockIdx.x % a.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int grp = a.grp;
+
+    // ---- every ring slot of this (sequence, KV head), 8 fp16 a load, requested together and
+    // before the length is known (a slot's key index follows from the length afterwards), so
+    // the keys arrive after one memory round trip; slots past the ring read zero
+    constexpr int kChunks = D / 8;                              // 16-byte chunks per key
+    constexpr int kLoads = kMaxRing * kChunks / kThreads;       // per thread
+    const __amdgpu_buffer_rsrc_t ring_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.ring + (size_t)s * R * a.H * D), (short)0, R * a.H * D * 2, 0x00020000);
+    u32x4 kbuf[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+        const int i = tid + j * kThreads, slot = i / kChunks, c8 = (i % kChunks) * 8;
+        kbuf[j] = __builtin_amdgcn_raw_buffer_load_b128(
+            ring_rsrc, slot < R ? (uint32_t)(((slot * a.H + kv) * D + c8) * 2) : kNowhere, 0, 0);
+    }
     const int N = max(a.seq_len[s], 0);
     const int n = min(N, R);
     const int first = N - n;
-
-    // ---- ring keys (positions first .. N-1, slot p % R) and the group's queries, 8 fp16 a load
-    for (int i = tid; i < n * (D / 8); i += kThreads) {
-        const int k = i / (D / 8), c8 = (i - k * (D / 8)) * 8;
-        const uint4 v = *reinterpret_cast<const uint4*>(
-            a.ring + (((size_t)s * R + (first + k) % R) * a.H + kv) * D + c8);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        float* dst = kref + k * (D + 1) + c8;
+    // key index k = (slot - first) mod R holds position first + k
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            dst[2 * j] = f16_val((uint16_t)(w[j] & 0xffffu));
-            dst[2 * j + 1] = f16_val((uint16_t)(w[j] >> 16));
+    for (int j = 0; j < kLoads; ++j) {
+        const int i = tid + j * kThreads, slot = i / kChunks, c8 = (i % kChunks) * 8;
+        const int k = slot < R ? (slot - first % R + R) % R : R;
+        if (k < n) {
+            float* dst = kref + k * (D + 1) + c8;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dst[2 * e] = f16_val((uint16_t)(kbuf[j][e] & 0xffffu));
+                dst[2 * e + 1] = f16_val((uint16_t)(kbuf[j][e] >> 16));
+            }
         }
     }
     for (int i = tid; i < grp * (D / 8); i += kThreads) {
@@ -192,36 +211,46 @@ __global__ __launch_bounds__(kThreads) void canary_kernel(CanaryArgs a) {
         }
     }
 
-    // ---- the last workgroup averages all rows, in row order. Its coherent stores complete
-    // before the ticket; the winner reads the rows with coherent loads issued after it.
+    // ---- the last workgroup of this width averages the width's rows, in row order (each lane
+    // sums rows lane, lane + 64, ... in turn; then a fixed tree). Its coherent stores complete
+    // before the ticket; the winner reads the rows with coherent loads issued after it, a batch
+    // of kRowBatch per lane at a time. Each width has its own counter, on its own line.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    const unsigned total = gridDim.x * gridDim.y;
+    uint32_t* counter = a.counter + ti * kCtrStride;
     if (tid == 0)
-        last = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               total - 1;
+        last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               gridDim.x - 1;
     __syncthreads();
     if (!last) return;
     constexpr int kSc1 = 16;                                    // device-coherent load
     const __amdgpu_buffer_rsrc_t rows_rsrc =
         __builtin_amdgcn_make_buffer_rsrc(a.ws_rows, (short)0, 0x7fffffff, 0x00020000);
-    if (wave < 3) {
+    if (wave == 0) {
         const int rows = a.batch * a.Hq;
         float acc = 0.f;
-        for (int r = lane; r < rows; r += 64)
-            acc += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                 rows_rsrc, (r * 3 + wave) * 4, 0, kSc1));
+        for (int r0 = 0; r0 < rows; r0 += 64 * kRowBatch) {
+            float v[kRowBatch];
+#pragma unroll
+            for (int j = 0; j < kRowBatch; ++j) {
+                const int r = r0 + 64 * j + lane;
+                v[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                     rows_rsrc, r < rows ? (uint32_t)((r * 3 + ti) * 4) : kNowhere, 0, kSc1));
+            }
+#pragma unroll
+            for (int j = 0; j < kRowBatch; ++j) acc += v[j];
+        }
         acc = wave_sum(acc);
-        if (lane == 0) a.kl_out[wave] = acc / (float)rows;
+        if (lane == 0) a.kl_out[ti] = acc / (float)rows;
     }
     if (tid == 0)
-        __hip_atomic_store(a.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
 
 size_t canary_workspace_bytes(const kv_geometry& g, int batch) {
-    return 256 + (size_t)batch * g.num_q_heads * 3 * sizeof(float);
+    return 3 * kCtrStride * 4 + (size_t)batch * g.num_q_heads * 3 * sizeof(float);
 }
 
 namespace {
@@ -261,7 +290,7 @@ hipError_t launch_canary(const kv_geometry& g, const uint16_t* ring, const int32
     a.kl_out = kl_out;
     a.kl_rows = kl_rows;
     a.counter = static_cast<uint32_t*>(workspace);
-    a.ws_rows = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + 256);
+    a.ws_rows = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + 3 * kCtrStride * 4);
     a.H = g.num_kv_heads;
     a.Hq = g.num_q_heads;
     a.grp = g.num_q_heads / g.num_kv_heads;
