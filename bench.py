@@ -38,8 +38,8 @@ ATTN_SRC = [os.path.join(ROOT, "mixed_precision_quantized_kv_amd", "csrc", f)
 # (FETCH_SIZE, WRITE_SIZE) scaled by the same counters' reading for a plain copy kernel of known
 # size. It describes the kernel sources with this digest only; after any change to them
 # the bench reports traffic as null until the counters are taken again.
-ATTN_TRAFFIC = {"source_sha256": "2252ac65be0ec60bc01b3d22f14cf5ec57be3aabed6ea71d1bafe5b9a8c6b86c",
-                "bytes_per_launch": 45350864,
+ATTN_TRAFFIC = {"source_sha256": "701d6c67f8a3a374890af288c892136d183c777cea3b8340c4224a866f377b3f",
+                "bytes_per_launch": 45346997,
                 # the bench's algorithmic bytes per launch at the counter run's contexts
                 "algorithmic_bytes_per_launch": 41804027}
 

@@ -248,29 +248,6 @@ __device__ __forceinline__ float rows_max(float x) {
     x = fmaxf(x, __shfl_xor(x, 16, 64));
     return fmaxf(x, __shfl_xor(x, 32, 64));
 }
-// max / sum over all 64 lanes: within each row of 16 by DPP (quad swaps, then rotations by 4
-// and 8), across the four rows from one lane of each (readlane: no LDS round trip)
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float lane_value(float x, int l) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
-}
-__device__ __forceinline__ float wave_max_dpp(float x) {
-    x = fmaxf(x, dpp_mov<0xB1>(x));      // quad_perm [1,0,3,2]
-    x = fmaxf(x, dpp_mov<0x4E>(x));      // quad_perm [2,3,0,1]
-    x = fmaxf(x, dpp_mov<0x124>(x));     // row_ror:4
-    x = fmaxf(x, dpp_mov<0x128>(x));     // row_ror:8
-    return fmaxf(fmaxf(lane_value(x, 0), lane_value(x, 16)), fmaxf(lane_value(x, 32), lane_value(x, 48)));
-}
-__device__ __forceinline__ float wave_sum_dpp(float x) {
-    x += dpp_mov<0xB1>(x);
-    x += dpp_mov<0x4E>(x);
-    x += dpp_mov<0x124>(x);
-    x += dpp_mov<0x128>(x);
-    return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
-}
 __device__ __forceinline__ float rows_sum(float x) {
     x += __shfl_xor(x, 16, 64);
     return x + __shfl_xor(x, 32, 64);
@@ -1440,7 +1417,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
     for (int h2 = wave; h2 < grp; h2 += kWaves) {
         float M = -INFINITY;
         for (int k = lane; k < nsplit; k += 64) M = fmaxf(M, lds_ml[h2][k].x);
-        M = wave_max_dpp(M);
+        M = wave_max(M);
         float L = 0.f;
         for (int k = lane; k < nsplit; k += 64) {
             const float2 ml = lds_ml[h2][k];
@@ -1448,7 +1425,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
             lds_ml[h2][k].x = e;
             L += e * ml.y;
         }
-        L = wave_sum_dpp(L);
+        L = wave_sum(L);
         if (lane == 0) lds_L[h2] = L;
     }
     __syncthreads();

@@ -68,18 +68,29 @@ __device__ inline int quant_code(float x, float s, int bits) {
     return (int)q;
 }
 
-template <typename T>
-__device__ inline T wave_max(T v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
+// Max / sum over all 64 lanes of a wave, every lane active: within each row of 16 lanes by DPP
+// (quad swaps, then rotations by 4 and 8), then across the four rows from one lane of each
+// (readlane), with no LDS round trip. Every lane gets the same value, summed in one fixed order.
+template <int CTRL>
+__device__ __forceinline__ float row_dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
 }
-
-template <typename T>
-__device__ inline T wave_sum(T v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
+__device__ __forceinline__ float lane_of(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, row_dpp<0xB1>(x));      // quad_perm [1,0,3,2]
+    x = fmaxf(x, row_dpp<0x4E>(x));      // quad_perm [2,3,0,1]
+    x = fmaxf(x, row_dpp<0x124>(x));     // row_ror:4
+    x = fmaxf(x, row_dpp<0x128>(x));     // row_ror:8
+    return fmaxf(fmaxf(lane_of(x, 0), lane_of(x, 16)), fmaxf(lane_of(x, 32), lane_of(x, 48)));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+    x += row_dpp<0xB1>(x);
+    x += row_dpp<0x4E>(x);
+    x += row_dpp<0x124>(x);
+    x += row_dpp<0x128>(x);
+    return (lane_of(x, 0) + lane_of(x, 16)) + (lane_of(x, 32) + lane_of(x, 48));
 }
 
 }  // namespace kvq
