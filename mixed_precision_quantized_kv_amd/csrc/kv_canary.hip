@@ -31,7 +31,7 @@ namespace kvq {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;   // eight waves: one query head each for groups of up to 8
 constexpr int kWavesC = kThreads / 64;
 constexpr int kMaxRing = 128;   // largest ring the geometry check accepts
 constexpr int kCtrStride = 64;  // uint32 words between the widths' counters (256 bytes)
