@@ -95,6 +95,8 @@ def parse():
     ap.add_argument("--pages-per-split", type=int, default=0)
     ap.add_argument("--unfused", action="store_true",
                     help="write and attend with two launches per layer instead of kv_decode_step")
+    ap.add_argument("--fused", action="store_true",
+                    help="use kv_decode_step also for more than 16 new tokens per sequence")
     return ap.parse_args()
 
 
@@ -191,10 +193,9 @@ def run(args):
     dev = "cuda:0"
     w = synth.WORKLOADS[args.workload]
     L, B, nn = w.num_layers, w.batch, w.new_tokens
-    # the fused step writes at most 16 tokens per sequence; wider writes take the two-call step
     # the fused step takes up to 64 new tokens, but with more than 16 (over two pages, written
     # two at a time by the last split's workgroup) the separate write launch measures faster
-    unfused = args.unfused or nn > 16
+    unfused = args.unfused or (nn > 16 and not args.fused)
     steps_total = args.warmup + args.steps
     t0 = time.time()
     m = Model(w, steps_total, torch, kvq, synth, dev)
