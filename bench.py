@@ -3,16 +3,19 @@
 
 A step is one pass of the whole hot path over one synthetic decode token: for every layer,
 quantize-on-write of the new key/value (kv_quant_write) followed by decode attention over the
-paged mixed-precision cache (kv_decode_attn); on every 64th step the KL canary runs for every
-layer (kv_canary_kl). The write and the attention of a layer run as one launch
-(kv_decode_step; --unfused times the two separate calls). Inputs are resident in HBM before
-timing starts; each timed step is replayed from a HIP graph holding exactly the eager step's
-launches.
+paged mixed-precision cache (kv_decode_attn); once every 64 steps the KL canary fires for every
+layer (kv_canary_kl_layers, one launch). The write and the attention of a layer run as one
+launch (kv_decode_step; --unfused times the two separate calls). Inputs are resident in HBM
+before timing starts; each timed step is replayed from a HIP graph holding exactly the eager
+step's launches. The step time is the window of K steps divided by K plus one canary firing,
+timed in windows of its own, divided by 64 -- the same charge whatever K is.
 
     python bench.py [--gpus 1] [--steps 256] [--warmup 10] [--workload qwen14b_32k]
+                    [--also llama70b_128k]
 
 Prints one JSON line. `value` is the effective cache bytes the attention kernels must read per
-step divided by the wall time of the step (GB/s); steps/s is reported beside it.
+step divided by the step time (GB/s); steps/s is reported beside it. `also` holds the same
+figures for a second workload (by default the 70B shape at 128K context).
 """
 from __future__ import annotations
 
@@ -31,6 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "quantized decode-attn achieved HBM GB/s + decode steps/s, 14B-shape @32K"
 HBM_PEAK_GBS = 8000.0
 CANARY_EVERY = 64
+CANARY_FIRINGS_TIMED = 8
 ATTN_SRC = [os.path.join(ROOT, "mixed_precision_quantized_kv_amd", "csrc", f)
             for f in ("kv_attn.hip", "kvq_write_dev.hpp", "kvq_device.hpp")]
 
@@ -97,6 +101,9 @@ def parse():
                     help="write and attend with two launches per layer instead of kv_decode_step")
     ap.add_argument("--fused", action="store_true",
                     help="use kv_decode_step also for more than 16 new tokens per sequence")
+    ap.add_argument("--also", default="llama70b_128k",
+                    help="a second workload measured after the first and reported under 'also' "
+                         "('' to skip)")
     return ap.parse_args()
 
 
@@ -184,19 +191,14 @@ def prefill(m: Model, kvq, synth, dev):
     torch.cuda.synchronize()
 
 
-def run(args):
-    import torch
-
-    import mixed_precision_quantized_kv_amd as kvq
-    from mixed_precision_quantized_kv_amd import synth
-
-    dev = "cuda:0"
-    w = synth.WORKLOADS[args.workload]
+def measure(w, steps: int, warmup: int, pages_per_split: int, unfused_flag: bool, fused_flag: bool,
+            torch, kvq, synth, dev) -> dict:
+    """GPU timings of one workload: the steps window, the attention launches, the canary firing"""
     L, B, nn = w.num_layers, w.batch, w.new_tokens
     # the fused step takes up to 64 new tokens, but with more than 16 (over two pages, written
     # two at a time by the last split's workgroup) the separate write launch measures faster
-    unfused = args.unfused or (nn > 16 and not args.fused)
-    steps_total = args.warmup + args.steps
+    unfused = unfused_flag or (nn > 16 and not fused_flag)
+    steps_total = warmup + steps
     t0 = time.time()
     m = Model(w, steps_total, torch, kvq, synth, dev)
     prefill(m, kvq, synth, dev)
@@ -214,17 +216,17 @@ def run(args):
     # the split plan for the batch's lengths at the first timed step (the library's plan for
     # known lengths: one round for equal lengths, smaller balanced splits for a ragged batch; the
     # fused step's plan also keeps the last split, which writes, shorter)
-    if args.pages_per_split:
-        pps = args.pages_per_split
+    if pages_per_split:
+        pps = pages_per_split
     elif unfused:
-        pps = kvq.kv_decode_pages_per_split_for(m.g, (m.lens0 + args.warmup * nn).astype(np.int32))
+        pps = kvq.kv_decode_pages_per_split_for(m.g, (m.lens0 + warmup * nn).astype(np.int32))
     else:
         pps = kvq.kv_decode_step_pages_per_split_for(
-            m.g, (m.lens0 - 1 + args.warmup * nn).astype(np.int32), nn)
+            m.g, (m.lens0 - 1 + warmup * nn).astype(np.int32), nn)
     wsb = kvq.kv_decode_workspace_bytes(m.g, B, m.max_ctx, pps)
     ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
     out = torch.empty((B, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
-    cwsb = kvq.kv_canary_workspace_bytes(m.g, B)
+    cwsb = kvq.kv_canary_layers_workspace_bytes(m.g, L, B)
     cws = torch.zeros(cwsb, dtype=torch.uint8, device=dev)
     kl = torch.zeros((L, 3), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
@@ -252,19 +254,18 @@ def run(args):
                                    v_all[i, l], m.ring[l], m.max_ctx, q_all[i, l], scale, out, ws,
                                    wsb, pps, stream=sp_)
 
-    def canary_all(i, sp_):
-        for l in range(L):
-            kvq.kv_canary_kl(m.g, m.ring[l], ctx_all[i], B, q_all[i, l], scale, kl[l], None,
-                             cws, cwsb, stream=sp_)
+    def canary_all(i, sp_):                              # one firing: every layer, one launch
+        kvq.kv_canary_kl_layers(m.g, m.ring, ctx_all[i], B, [q_all[i, l] for l in range(L)], scale,
+                                kl, None, cws, cwsb, stream=sp_)
 
-    for i in range(args.warmup):                         # eager warm-up steps
+    for i in range(warmup):                              # eager warm-up steps
         writes_and_attention(i, sp)
         if i % CANARY_EVERY == 0:
             canary_all(i, sp)
     torch.cuda.synchronize()
 
     # Each timed step is replayed from a HIP graph captured once (one launch per step from the
-    # host instead of ~2L+1): a decode step is a chain of short kernels, and launching them one
+    # host instead of ~L+1): a decode step is a chain of short kernels, and launching them one
     # by one from Python would time the interpreter, not the GPU. A step's graph holds the same
     # launches, with the same arguments, as the eager step.
     def capture(fn, i):
@@ -273,54 +274,57 @@ def run(args):
             fn(i, torch.cuda.current_stream().cuda_stream)
         return g
 
-    steps_idx = [args.warmup + j for j in range(args.steps)]
+    steps_idx = [warmup + j for j in range(steps)]
+    n_fire = min(CANARY_FIRINGS_TIMED, steps)
     g_step = [capture(writes_and_attention, i) for i in steps_idx]
     g_attn = [capture(attention_only, i) for i in steps_idx]
-    g_canary = {j: capture(canary_all, steps_idx[j]) for j in range(0, args.steps, CANARY_EVERY)}
+    g_canary = [capture(canary_all, steps_idx[j]) for j in range(n_fire)]
     torch.cuda.synchronize()
 
-    # timed window: K steps, the canary firing on every 64th
+    # timed window: exactly K steps, writes and attention for every layer
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    for j in range(args.steps):
+    for j in range(steps):
         g_step[j].replay()
-        if j in g_canary:
-            g_canary[j].replay()
     t_end.record(stream)
     torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
+    ms_step_nocanary = t_start.elapsed_time(t_end) / steps
 
     # attention launch durations: events on the launch stream around each step's L attention
     # launches, replayed back to back (the caches already hold the step's tokens, and each
     # layer's attention reads only its own layer's cache); the per-launch time is the group's / L
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+           for _ in range(steps)]
     torch.cuda.synchronize()
-    for j in range(args.steps):
+    for j in range(steps):
         evs[j][0].record(stream)
         g_attn[j].replay()
         evs[j][1].record(stream)
     torch.cuda.synchronize()
     attn_group_ms = np.array([a.elapsed_time(b) for (a, b) in evs])          # [K], L launches each
 
-    # steps without the canary (for its overhead)
+    # canary firings, each in its own event window right after a step (as it fires in a run):
+    # the cost of one firing for all layers, charged to the step at the page's 1-in-64 rate
+    cevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n_fire)]
     torch.cuda.synchronize()
-    t_start.record(stream)
-    for j in range(args.steps):
+    for j in range(n_fire):
         g_step[j].replay()
-    t_end.record(stream)
+        cevs[j][0].record(stream)
+        g_canary[j].replay()
+        cevs[j][1].record(stream)
     torch.cuda.synchronize()
-    ms_step_nocanary = t_start.elapsed_time(t_end) / args.steps
+    canary_ms = float(np.mean([a.elapsed_time(b) for (a, b) in cevs]))
     del g_step, g_attn, g_canary
+    ms_step = ms_step_nocanary + canary_ms / CANARY_EVERY
 
     # algorithmic bytes
     lens = m.lens0.astype(np.int64)
     step_bytes = []
-    per_launch_bytes = np.zeros((args.steps, L))
-    for j in range(args.steps):
-        ctx = lens + (args.warmup + j) * nn
+    per_launch_bytes = np.zeros((steps, L))
+    for j in range(steps):
+        ctx = lens + (warmup + j) * nn
         for l, b in enumerate(m.bits):
             per_launch_bytes[j, l] = sum(attn_bytes(w, int(c), b) for c in ctx)
             if not unfused:
@@ -330,14 +334,36 @@ def run(args):
     avg_launch_bytes = float(per_launch_bytes.mean())
     avg_attn_ms = float(attn_group_ms.mean()) / L
     achieved = avg_launch_bytes / (avg_attn_ms * 1e-3) / 1e9
+    res = {"m": m, "unfused": unfused, "pps": pps, "setup_s": t_setup, "ms_step": ms_step,
+           "ms_step_nocanary": ms_step_nocanary, "canary_ms": canary_ms, "n_fire": n_fire,
+           "step_bytes": step_bytes, "avg_launch_bytes": avg_launch_bytes,
+           "avg_attn_ms": avg_attn_ms, "achieved": achieved}
+    return res
 
+
+def run(args):
+    import torch
+
+    import mixed_precision_quantized_kv_amd as kvq
+    from mixed_precision_quantized_kv_amd import synth
+
+    dev = "cuda:0"
+    w = synth.WORKLOADS[args.workload]
+    L, B = w.num_layers, w.batch
+    r = measure(w, args.steps, args.warmup, args.pages_per_split, args.unfused, args.fused,
+                torch, kvq, synth, dev)
+    m, unfused, pps = r["m"], r["unfused"], r["pps"]
+    ms_step, step_bytes, achieved = r["ms_step"], r["step_bytes"], r["achieved"]
     value = step_bytes / (ms_step * 1e-3) / 1e9
+    bits = list(m.bits)
+    del r["m"], m
+    torch.cuda.empty_cache()
     probes = hbm_probes(torch, dev)
     traffic = None
     if (ATTN_TRAFFIC["source_sha256"] == source_digest(ATTN_SRC) and not unfused
             and args.workload == "qwen14b_32k" and not args.pages_per_split):
         traffic = ATTN_TRAFFIC["bytes_per_launch"]      # taken on the fused kernel, default workload
-    tiers = {b: m.bits.count(b) for b in (2, 4, 8)}
+    tiers = {b: bits.count(b) for b in (2, 4, 8)}
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -354,78 +380,120 @@ def run(args):
         "data": "synthetic",
         "config": {
             "workload": w.name, "layers": L, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
-            "head_dim": w.head_dim, "batch": B, "context": int(m.lens0.max()),
+            "head_dim": w.head_dim, "batch": B, "context": int(synth.seq_lengths(w).max()),
             "page": 16, "ring": w.ring_size, "layer_bits": {f"int{b}": n for b, n in tiers.items()},
             "pages_per_split": pps, "canary_every": CANARY_EVERY,
         },
         "storage": "packed int2/int4/int8 codes + fp16 scales; f16 MFMA, f32 accumulate",
+        "step_time": "ms_per_step = the window of K steps (every layer's write and attention) / K "
+                     "+ one canary firing (every layer, one launch, own event window) / 64",
         "attn_bytes_per_step": int(step_bytes),
-        "attn_kernel_us": round(avg_attn_ms * 1e3, 3),
-        "canary_overhead": round(ms_step / ms_step_nocanary - 1.0, 5),
-        "ms_per_step_no_canary": round(ms_step_nocanary, 5),
+        "attn_kernel_us": round(r["avg_attn_ms"] * 1e3, 3),
+        "ms_per_step_no_canary": round(r["ms_step_nocanary"], 5),
+        "canary_ms_per_firing": round(r["canary_ms"], 5),
+        "canary_firings_timed": r["n_fire"],
+        "canary_overhead": round(r["canary_ms"] / CANARY_EVERY / r["ms_step_nocanary"], 5),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": f"decode_attn_kernel<{w.head_dim}> (unfused)" if unfused else
                       f"decode_attn_kernel<{w.head_dim}> fused with the write (kv_decode_step)",
-            "bytes_per_launch": int(avg_launch_bytes),
+            "bytes_per_launch": int(r["avg_launch_bytes"]),
             "traffic_over_algorithmic": (round(traffic / ATTN_TRAFFIC["algorithmic_bytes_per_launch"], 4)
                                          if traffic else None),
         },
         "hbm_probes": probes,
         "attn_source_sha256": source_digest(ATTN_SRC),
-        "setup_s": round(t_setup, 1),
+        "setup_s": round(r["setup_s"], 1),
     }
+    if args.also and args.workload != args.also:
+        wa = synth.WORKLOADS[args.also]
+        ra = measure(wa, min(args.steps, 64), min(args.warmup, 4), 0, False, False, torch, kvq,
+                     synth, dev)
+        del ra["m"]
+        torch.cuda.empty_cache()
+        ms_a = ra["ms_step"]
+        res["also"] = {
+            "workload": wa.name, "layers": wa.num_layers, "q_heads": wa.num_q_heads,
+            "kv_heads": wa.num_kv_heads, "batch": wa.batch,
+            "context": int(synth.seq_lengths(wa).max()), "pages_per_split": ra["pps"],
+            "steps": min(args.steps, 64), "value": round(ra["step_bytes"] / (ms_a * 1e-3) / 1e9, 2),
+            "unit": "GB/s", "ms_per_step": round(ms_a, 5), "steps_per_s": round(1000.0 / ms_a, 2),
+            "attn_kernel_us": round(ra["avg_attn_ms"] * 1e3, 3),
+            "canary_ms_per_firing": round(ra["canary_ms"], 5),
+            "roofline_frac": round(ra["achieved"] / HBM_PEAK_GBS, 4),
+        }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, m.bits, args.cpu_layers, args.cpu_reps, step_bytes)
+        res["cpu_baseline"] = cpu_baseline(w, bits, args.cpu_layers, args.cpu_reps, step_bytes)
     print(json.dumps(res), flush=True)
 
 
 def cpu_baseline(w, bits, n_layers: int, reps: int, step_bytes: float) -> dict:
-    """The oracle (plain C, fp64) on a bounded sample of the same decode step: for each sampled
-    layer, quantize-on-write of the new token plus decode attention at full context, repeated
-    `reps` times, and the canary once per layer (charged at its 1-in-64 rate); the per-step
-    time is scaled to all layers."""
+    """The oracle (plain C, fp64) on a bounded sample of the same decode step. All cores: for
+    each sampled layer, quantize-on-write of the new token plus decode attention at full context,
+    repeated `reps` times, scaled to all layers; the canary of every layer timed on its own and
+    charged at its 1-in-64 rate. One thread: one layer of each width once (write + attention) and
+    one canary, weighted by the workload's layer mix."""
     import oracle
     from mixed_precision_quantized_kv_amd import synth
 
     oracle.lib()
+    all_threads = oracle.num_threads()
     g = oracle.geom(w.num_q_heads, w.num_kv_heads, w.head_dim, 16, w.ring_size)
     N = int(synth.seq_lengths(w).max())
     layers = list(range(n_layers if n_layers > 0 else w.num_layers))
     B = w.batch
-    t_step_sum = 0.0
-    t_canary_sum = 0.0
     # one seeded draw of keys and values serves every sampled layer (the oracle's time does not
     # depend on the values); each layer keeps its own bit-width
     K, V = synth.keys_values(w, 0, N, synth.S_PREFILL_K, synth.S_PREFILL_V)
     scale = np.float32(1.0 / math.sqrt(w.head_dim))
     prepared = {}                   # one prefilled cache per bit-width, shared by its layers
-    for l in layers:
-        b = bits[l]
-        if b not in prepared:
-            tier = synth.TIER_OF_BITS[b]
-            pages = (N + 15) // 16
-            cap = [pages * B if t == tier else 1 for t in range(3)]
-            bt = synth.block_table([[tier] * pages] * B, pages, cap, synth.rng(w, l, synth.S_SHUFFLE))
-            pools = oracle.Pools(g, cap)
-            ring = np.zeros((B, w.ring_size, w.num_kv_heads, w.head_dim), dtype=np.uint16)
-            oracle.quant_write(g, pools, bt, np.zeros(B, np.int32), K[:, :N - 1], V[:, :N - 1], ring)
-            prepared[b] = (bt, pools, ring)
+    for b in sorted(set(bits[l] for l in layers) | set(bits)):
+        tier = synth.TIER_OF_BITS[b]
+        pages = (N + 15) // 16
+        cap = [pages * B if t == tier else 1 for t in range(3)]
+        bt = synth.block_table([[tier] * pages] * B, pages, cap, synth.rng(w, b, synth.S_SHUFFLE))
+        pools = oracle.Pools(g, cap)
+        ring = np.zeros((B, w.ring_size, w.num_kv_heads, w.head_dim), dtype=np.uint16)
+        oracle.quant_write(g, pools, bt, np.zeros(B, np.int32), K[:, :N - 1], V[:, :N - 1], ring)
+        prepared[b] = (bt, pools, ring)
+
+    def one_layer_step(b, q):
         bt, pools, ring = prepared[b]
-        q = synth.queries(w, l)
-        for _ in range(reps):
-            t0 = time.perf_counter()
-            oracle.quant_write(g, pools, bt, np.full(B, N - 1, np.int32), K[:, N - 1:], V[:, N - 1:], ring)
-            oracle.decode_attn(g, pools, bt, np.full(B, N, np.int32), q, scale)
-            t_step_sum += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.quant_write(g, pools, bt, np.full(B, N - 1, np.int32), K[:, N - 1:], V[:, N - 1:], ring)
+        oracle.decode_attn(g, pools, bt, np.full(B, N, np.int32), q, scale)
+        return time.perf_counter() - t0
+
+    def one_canary(b, q):
+        _, _, ring = prepared[b]
         t0 = time.perf_counter()
         oracle.canary_kl(g, ring, np.full(B, N, np.int32), q, scale)
-        t_canary_sum += time.perf_counter() - t0
-    t_layer = t_step_sum / (len(layers) * reps) + t_canary_sum / len(layers) / CANARY_EVERY
-    t_step = t_layer * w.num_layers
-    # the oracle's parallel loops run over (sequence, KV head) items
-    cores = min(oracle.num_threads(), B * w.num_kv_heads)
+        return time.perf_counter() - t0
+
+    oracle.set_num_threads(all_threads)
+    t_step_sum = 0.0
+    for l in layers:
+        q = synth.queries(w, l)
+        for _ in range(reps):
+            t_step_sum += one_layer_step(bits[l], q)
+    t_canary_firing = sum(one_canary(bits[l], synth.queries(w, l)) for l in range(w.num_layers))
+    t_step_nocanary = t_step_sum / (len(layers) * reps) * w.num_layers
+    t_step = t_step_nocanary + t_canary_firing / CANARY_EVERY
+
+    # one thread: a layer of each width, weighted by how many layers have that width
+    oracle.set_num_threads(1)
+    t1 = 0.0
+    t1_canary = 0.0
+    for b in sorted(set(bits)):
+        q = synth.queries(w, bits.index(b))
+        t1 += one_layer_step(b, q) * bits.count(b)
+        t1_canary += one_canary(b, q) * bits.count(b)
+    oracle.set_num_threads(all_threads)
+    t1_step = t1 + t1_canary / CANARY_EVERY
+
+    # the oracle's parallel loop runs over (sequence, KV head) items
+    cores = min(all_threads, B * w.num_kv_heads)
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -434,12 +502,19 @@ def cpu_baseline(w, bits, n_layers: int, reps: int, step_bytes: float) -> dict:
         pass
     return {"value": round(step_bytes / t_step / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle", "steps_per_s": round(1.0 / t_step, 5),
-            "host_cpus": os.cpu_count(), "cpu_model": model, "oracle_threads": oracle.num_threads(),
+            "s_per_step_no_canary": round(t_step_nocanary, 4),
+            "canary_s_per_firing": round(t_canary_firing, 4),
+            "one_thread": {"value": round(step_bytes / t1_step / 1e9, 4), "unit": "GB/s",
+                           "steps_per_s": round(1.0 / t1_step, 5),
+                           "canary_s_per_firing": round(t1_canary, 4),
+                           "sample": f"one layer of each width ({sorted(set(bits))}) once, "
+                                     f"weighted by the layer mix"},
+            "host_cpus": os.cpu_count(), "cpu_model": model, "oracle_threads": all_threads,
             "sample": f"{len(layers)} of {w.num_layers} layers, each {reps}x one decode step "
-                      f"(write of the new token + attention at context {N}, batch {B}) plus the "
-                      f"canary once (charged at 1/{CANARY_EVERY}); per-step time scaled to "
-                      f"{w.num_layers} layers",
-            "seconds_measured": round(t_step_sum + t_canary_sum, 2)}
+                      f"(write of the new token + attention at context {N}, batch {B}), scaled to "
+                      f"{w.num_layers} layers; the canary of all {w.num_layers} layers timed once, "
+                      f"charged at 1/{CANARY_EVERY}",
+            "seconds_measured": round(t_step_sum + t_canary_firing + t1 / max(1, len(set(bits))), 2)}
 
 
 def main():

@@ -235,10 +235,11 @@ kv_status kv_decode_step(const kv_geometry* g, const kv_layer_pools* pools, cons
  * sequence ends in the same split -- with the same split count but longer splits, so that the
  * last split, whose workgroup also writes the step's tokens (two pages at a time, each round
  * about the loop time of 30 to 50 pages), is 40 pages per round (at most half a split) shorter
- * than the others. kv_decode_step with
- * pages_per_split = 0 plans the same way from max_ctx_len; either plan fits the workspace of
- * kv_decode_workspace_bytes(g, batch, max_ctx_len, 0), since the split count is kept. Returns 0
- * on invalid arguments. */
+ * than the others. kv_decode_step with pages_per_split = 0 plans the same way from max_ctx_len.
+ * Size the workspace with the pages_per_split the call will pass:
+ * kv_decode_workspace_bytes(g, batch, max_ctx_len, pps) for this plan's pps, or with 0 for
+ * pages_per_split = 0 (for a ragged batch this plan can have more splits than the plan of 0).
+ * Returns 0 on invalid arguments. */
 int       kv_decode_step_pages_per_split_for(const kv_geometry* g, int batch, const int32_t* pos_host,
                                              int n_new);
 
@@ -258,6 +259,28 @@ size_t    kv_canary_workspace_bytes(const kv_geometry* g, int batch);
 kv_status kv_canary_kl(const kv_geometry* g, const uint16_t* ring, const int32_t* seq_len,
                        int batch, const uint16_t* q, float softmax_scale, float* kl_out,
                        float* kl_rows, void* workspace, size_t workspace_bytes, void* stream);
+/* One firing for every layer in one launch ([EchoKV] "Show the math": a firing yields one
+ * number per (layer, width), 3L numbers; at the page's rate of one firing per 64 steps the whole
+ * pipeline is meant to cost a small fraction of a step, so it runs as one grid of
+ * batch*H_kv*3*num_layers workgroups instead of num_layers launches). Layer l's readings are
+ * exactly those kv_canary_kl gives for rings[l] and q[l]; all layers share seq_len (every layer
+ * holds the same tokens).
+ *   num_layers  1 .. min(g->num_layers, KV_CANARY_MAX_LAYERS)
+ *   rings, q    HOST arrays [num_layers] of device pointers (each 16-byte aligned), read during
+ *               the call and not retained: rings[l] as the ring of kv_canary_kl, q[l] [batch][H_q][D]
+ *   kl_out      dev fp32 [num_layers][3];  kl_rows  dev fp32 [num_layers][batch][H_q][3] or NULL
+ *   workspace   dev, >= kv_canary_layers_workspace_bytes(g, num_layers, batch) bytes, zero-filled
+ *               before its first use; left ready for the next kv_canary_kl_layers call on the
+ *               same geometry, whatever its batch and layer count (its ticket counters, one
+ *               256-byte line per (layer, width) for min(g->num_layers, KV_CANARY_MAX_LAYERS)
+ *               layers, come first and do not move)
+ * Errors as for kv_canary_kl; a NULL or misaligned pointer of any layer is KV_EINVAL. */
+#define KV_CANARY_MAX_LAYERS 128
+size_t    kv_canary_layers_workspace_bytes(const kv_geometry* g, int num_layers, int batch);
+kv_status kv_canary_kl_layers(const kv_geometry* g, int num_layers, const uint16_t* const* rings,
+                              const int32_t* seq_len, int batch, const uint16_t* const* q,
+                              float softmax_scale, float* kl_out, float* kl_rows, void* workspace,
+                              size_t workspace_bytes, void* stream);
 /* The same divergence with the temporary copies built by the asymmetric quantizer ([EchoKV]
  * "Show the math" describes its canary quantizer as asymmetric per group, in the manner of KIVI),
  * over the same groups (each ring key's page, one group per channel): zero point m = the group

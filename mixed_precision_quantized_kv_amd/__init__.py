@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
             "kv_canary_workspace_bytes": (sz, [G, i32]),
             "kv_canary_kl": (i32, [G, P, P, i32, P, ctypes.c_float, P, P, P, sz, P]),
             "kv_canary_kl_asym": (i32, [G, P, P, i32, P, ctypes.c_float, P, P, P, sz, P]),
+            "kv_canary_layers_workspace_bytes": (sz, [G, i32, i32]),
+            "kv_canary_kl_layers": (i32, [G, i32, P, P, i32, P, ctypes.c_float, P, P, P, sz, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -347,3 +349,23 @@ def kv_canary_kl_asym(g: Geometry, ring, seq_len, batch: int, q, softmax_scale: 
     _check(lib().kv_canary_kl_asym(ctypes.byref(g), _addr(ring), _addr(seq_len), batch, _addr(q),
                                    softmax_scale, _addr(kl_out), _addr(kl_rows), _addr(workspace),
                                    workspace_bytes, _stream(stream)))
+
+
+def kv_canary_layers_workspace_bytes(g: Geometry, num_layers: int, batch: int) -> int:
+    return lib().kv_canary_layers_workspace_bytes(ctypes.byref(g), num_layers, batch)
+
+
+def kv_canary_kl_layers(g: Geometry, rings, seq_len, batch: int, qs, softmax_scale: float, kl_out,
+                        kl_rows, workspace, workspace_bytes=None, stream=None) -> None:
+    """rings, qs: sequences of per-layer device tensors (or addresses); their addresses are passed
+    as host arrays of device pointers"""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    n = len(rings)
+    if len(qs) != n:
+        raise ValueError("one q per ring")
+    ring_ptrs = (ctypes.c_void_p * max(n, 1))(*[_addr(r) for r in rings])
+    q_ptrs = (ctypes.c_void_p * max(n, 1))(*[_addr(q) for q in qs])
+    _check(lib().kv_canary_kl_layers(ctypes.byref(g), n, ring_ptrs, _addr(seq_len), batch, q_ptrs,
+                                     softmax_scale, _addr(kl_out), _addr(kl_rows), _addr(workspace),
+                                     workspace_bytes, _stream(stream)))

@@ -492,7 +492,14 @@ kv_status kv_decode_step(const kv_geometry* g, const kv_layer_pools* pools, cons
 
 size_t kv_canary_workspace_bytes(const kv_geometry* g, int batch) {
     if (check_geometry(g) != KV_OK || batch < 1) return 0;
-    return kvq::canary_workspace_bytes(*g, batch);
+    return kvq::canary_workspace_bytes(*g, 1, 1, batch);
+}
+
+size_t kv_canary_layers_workspace_bytes(const kv_geometry* g, int num_layers, int batch) {
+    if (check_geometry(g) != KV_OK || batch < 1 || num_layers < 1 ||
+        num_layers > std::min(g->num_layers, KV_CANARY_MAX_LAYERS))
+        return 0;
+    return kvq::canary_workspace_bytes(*g, kvq::canary_counter_layers(*g), num_layers, batch);
 }
 
 static kv_status canary(const kv_geometry* g, const uint16_t* ring, const int32_t* seq_len,
@@ -508,7 +515,7 @@ static kv_status canary(const kv_geometry* g, const uint16_t* ring, const int32_
         return fail(KV_EINVAL, "ring and q must be 16-byte aligned");
     if (reinterpret_cast<uintptr_t>(workspace) % 256)
         return fail(KV_EINVAL, "workspace must be 256-byte aligned");
-    const size_t need = kvq::canary_workspace_bytes(*g, batch);
+    const size_t need = kvq::canary_workspace_bytes(*g, 1, 1, batch);
     if (workspace_bytes < need)
         return fail(KV_EINVAL, "workspace %zu bytes, %zu needed", workspace_bytes, need);
     if (!(softmax_scale == softmax_scale)) return fail(KV_EINVAL, "softmax_scale is NaN");
@@ -523,6 +530,36 @@ kv_status kv_canary_kl(const kv_geometry* g, const uint16_t* ring, const int32_t
                        float* kl_rows, void* workspace, size_t workspace_bytes, void* stream) {
     return canary(g, ring, seq_len, batch, q, softmax_scale, false, kl_out, kl_rows, workspace,
                   workspace_bytes, stream, "kv_canary_kl");
+}
+
+kv_status kv_canary_kl_layers(const kv_geometry* g, int num_layers, const uint16_t* const* rings,
+                              const int32_t* seq_len, int batch, const uint16_t* const* q,
+                              float softmax_scale, float* kl_out, float* kl_rows, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    kv_status st = check_geometry(g);
+    if (st != KV_OK) return st;
+    if (num_layers < 1 || num_layers > std::min(g->num_layers, KV_CANARY_MAX_LAYERS))
+        return fail(KV_EINVAL, "num_layers %d: 1 .. min(geometry layers %d, %d)", num_layers,
+                    g->num_layers, KV_CANARY_MAX_LAYERS);
+    if (batch < 1 || batch > g->max_seqs) return fail(KV_EINVAL, "batch %d", batch);
+    if (!rings || !q) return fail(KV_EINVAL, "NULL host pointer array");
+    if (!seq_len || !kl_out || !workspace) return fail(KV_EINVAL, "NULL device pointer");
+    for (int l = 0; l < num_layers; ++l) {
+        if (!rings[l] || !q[l]) return fail(KV_EINVAL, "layer %d: NULL device pointer", l);
+        if (reinterpret_cast<uintptr_t>(rings[l]) % 16 || reinterpret_cast<uintptr_t>(q[l]) % 16)
+            return fail(KV_EINVAL, "layer %d: ring and q must be 16-byte aligned", l);
+    }
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+        return fail(KV_EINVAL, "workspace must be 256-byte aligned");
+    const size_t need =
+        kvq::canary_workspace_bytes(*g, kvq::canary_counter_layers(*g), num_layers, batch);
+    if (workspace_bytes < need)
+        return fail(KV_EINVAL, "workspace %zu bytes, %zu needed", workspace_bytes, need);
+    if (!(softmax_scale == softmax_scale)) return fail(KV_EINVAL, "softmax_scale is NaN");
+    return hip_status(kvq::launch_canary_layers(*g, num_layers, rings, seq_len, batch, q,
+                                                softmax_scale, kl_out, kl_rows, workspace,
+                                                static_cast<hipStream_t>(stream)),
+                      "kv_canary_kl_layers");
 }
 
 kv_status kv_canary_kl_asym(const kv_geometry* g, const uint16_t* ring, const int32_t* seq_len,

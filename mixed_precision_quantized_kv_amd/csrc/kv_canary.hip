@@ -38,16 +38,23 @@ constexpr int kCtrStride = 64;  // uint32 words between the widths' counters (25
 constexpr int kRowBatch = 16;   // row loads a lane has in flight in the final average
 constexpr uint32_t kNowhere = 0xffffff00u;   // a buffer offset past every range: reads zero
 
+struct CanaryLayer {
+    const uint16_t* ring;   // [batch][R][H][D]
+    const uint16_t* q;      // [batch][Hq][D]
+};
+
+// NL: room for that many layers in the argument block (1 for a single layer's call, the
+// multi-layer limit for a whole firing); layer l is blockIdx.z
+template <int NL>
 struct CanaryArgs {
-    const uint16_t* ring;
     const int32_t* seq_len;
-    const uint16_t* q;
-    float* kl_out;
-    float* kl_rows;       // optional
-    float* ws_rows;       // [batch][Hq][3]
-    uint32_t* counter;    // [3][kCtrStride]: one ticket counter per width, each in its own line
+    float* kl_out;        // [L][3]
+    float* kl_rows;       // optional, [L][batch][Hq][3]
+    float* ws_rows;       // [L][batch][Hq][3]
+    uint32_t* counter;    // [L][3][kCtrStride]: one ticket counter per (layer, width), each in its own line
     int H, Hq, grp, R, batch;
     float scale;
+    CanaryLayer layer[NL];
 };
 
 // logits of every query head of the group against n keys held in LDS rows of stride D + 1
@@ -77,8 +84,8 @@ __device__ inline uint16_t f64_to_f16_up(double x) {
     return b;
 }
 
-template <int D, bool ASYM>
-__global__ __launch_bounds__(kThreads) void canary_kernel(CanaryArgs a) {
+template <int D, bool ASYM, int NL>
+__global__ __launch_bounds__(kThreads) void canary_kernel(CanaryArgs<NL> a) {
     extern __shared__ float smem[];
     const int R = a.R;
     float* kref = smem;                          // [R][D + 1]; later the copy, in place
@@ -91,6 +98,10 @@ __global__ __launch_bounds__(kThreads) void canary_kernel(CanaryArgs a) {
 
     const int ti = blockIdx.y;                   // width 2, 4, 8
     const int bits = 2 << ti;
+    const int layer = NL == 1 ? 0 : (int)blockIdx.z;
+    const uint16_t* ring = a.layer[layer].ring;
+    const uint16_t* qv = a.layer[layer].q;
+    const size_t row0 = (size_t)layer * a.batch * a.Hq;   // this layer's first row
     const int s = blockIdx.x / a.H, kv = blockIdx.x % a.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int grp = a.grp;
@@ -101,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void canary_kernel(CanaryArgs a) {
     constexpr int kChunks = D / 8;                              // 16-byte chunks per key
     constexpr int kLoads = kMaxRing * kChunks / kThreads;       // per thread
     const __amdgpu_buffer_rsrc_t ring_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(a.ring + (size_t)s * R * a.H * D), (short)0, R * a.H * D * 2, 0x00020000);
+        const_cast<uint16_t*>(ring + (size_t)s * R * a.H * D), (short)0, R * a.H * D * 2, 0x00020000);
     u32x4 kbuf[kLoads];
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
@@ -127,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void canary_kernel(CanaryArgs a) {
         }
     }
     for (int i = tid; i < grp * (D / 8); i += kThreads) {
-        const uint4 v = *reinterpret_cast<const uint4*>(a.q + ((size_t)s * a.Hq + kv * grp) * D + 8 * i);
+        const uint4 v = *reinterpret_cast<const uint4*>(qv + ((size_t)s * a.Hq + kv * grp) * D + 8 * i);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -205,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void canary_kernel(CanaryArgs a) {
         acc = wave_sum(acc);
         const float kl = n > 0 ? fmaxf(acc - lse_l + lse_m, 0.f) : 0.f;
         if (lane == 0) {
-            const size_t row = ((size_t)s * a.Hq + kv * grp + hh) * 3 + ti;
+            const size_t row = (row0 + (size_t)s * a.Hq + kv * grp + hh) * 3 + ti;
             __hip_atomic_store(a.ws_rows + row, kl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (a.kl_rows) a.kl_rows[row] = kl;
         }
@@ -217,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void canary_kernel(CanaryArgs a) {
     // of kRowBatch per lane at a time. Each width has its own counter, on its own line.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    uint32_t* counter = a.counter + ti * kCtrStride;
+    uint32_t* counter = a.counter + (layer * 3 + ti) * kCtrStride;
     if (tid == 0)
         last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                gridDim.x - 1;
@@ -225,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void canary_kernel(CanaryArgs a) {
     if (!last) return;
     constexpr int kSc1 = 16;                                    // device-coherent load
     const __amdgpu_buffer_rsrc_t rows_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(a.ws_rows, (short)0, 0x7fffffff, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(a.ws_rows + row0 * 3, (short)0, 0x7fffffff, 0x00020000);
     if (wave == 0) {
         const int rows = a.batch * a.Hq;
         float acc = 0.f;
@@ -241,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void canary_kernel(CanaryArgs a) {
             for (int j = 0; j < kRowBatch; ++j) acc += v[j];
         }
         acc = wave_sum(acc);
-        if (lane == 0) a.kl_out[ti] = acc / (float)rows;
+        if (lane == 0) a.kl_out[layer * 3 + ti] = acc / (float)rows;
     }
     if (tid == 0)
         __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -249,8 +260,12 @@ __global__ __launch_bounds__(kThreads) void canary_kernel(CanaryArgs a) {
 
 }  // namespace
 
-size_t canary_workspace_bytes(const kv_geometry& g, int batch) {
-    return 3 * kCtrStride * 4 + (size_t)batch * g.num_q_heads * 3 * sizeof(float);
+// Workspace: the ticket counters of `counter_layers` layers (three lines each), then the rows of
+// the call. The counters stay at the same place whatever the call's batch and layer count, so a
+// workspace left at zero by one call is ready for the next.
+size_t canary_workspace_bytes(const kv_geometry& g, int counter_layers, int num_layers, int batch) {
+    return (size_t)counter_layers * 3 * kCtrStride * 4 +
+           (size_t)num_layers * batch * g.num_q_heads * 3 * sizeof(float);
 }
 
 namespace {
@@ -261,21 +276,38 @@ size_t canary_lds_bytes(int R, int D, bool asym) {
                             2 * kMaxGroup * (size_t)R);
 }
 
-template <int D, bool ASYM>
-hipError_t launch_one(const CanaryArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
+template <int D, bool ASYM, int NL>
+hipError_t launch_one(const CanaryArgs<NL>& a, dim3 grid, size_t lds, hipStream_t stream) {
     // the LDS footprint exceeds the 64 KiB default for rings of 64 keys at D = 128: raise the
     // limit to the largest footprint any supported ring needs, once per process and kernel (so
     // that launches stay plain stream work, e.g. under graph capture)
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
-        attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&canary_kernel<D, ASYM>),
+        attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&canary_kernel<D, ASYM, NL>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize,
                                    (int)canary_lds_bytes(kMaxRing, D, ASYM));
     });
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((canary_kernel<D, ASYM>), grid, dim3(kThreads), lds, stream, a);
+    hipLaunchKernelGGL((canary_kernel<D, ASYM, NL>), grid, dim3(kThreads), lds, stream, a);
     return hipGetLastError();
+}
+
+template <int NL>
+void fill_common(CanaryArgs<NL>& a, const kv_geometry& g, const int32_t* seq_len, int counter_layers,
+                 int batch, float softmax_scale, float* kl_out, float* kl_rows, void* workspace) {
+    a.seq_len = seq_len;
+    a.kl_out = kl_out;
+    a.kl_rows = kl_rows;
+    a.counter = static_cast<uint32_t*>(workspace);
+    a.ws_rows = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                         (size_t)counter_layers * 3 * kCtrStride * 4);
+    a.H = g.num_kv_heads;
+    a.Hq = g.num_q_heads;
+    a.grp = g.num_q_heads / g.num_kv_heads;
+    a.R = g.ring_size;
+    a.batch = batch;
+    a.scale = softmax_scale;
 }
 
 }  // namespace
@@ -283,20 +315,9 @@ hipError_t launch_one(const CanaryArgs& a, dim3 grid, size_t lds, hipStream_t st
 hipError_t launch_canary(const kv_geometry& g, const uint16_t* ring, const int32_t* seq_len,
                          int batch, const uint16_t* q, float softmax_scale, bool asymmetric,
                          float* kl_out, float* kl_rows, void* workspace, hipStream_t stream) {
-    CanaryArgs a;
-    a.ring = ring;
-    a.seq_len = seq_len;
-    a.q = q;
-    a.kl_out = kl_out;
-    a.kl_rows = kl_rows;
-    a.counter = static_cast<uint32_t*>(workspace);
-    a.ws_rows = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + 3 * kCtrStride * 4);
-    a.H = g.num_kv_heads;
-    a.Hq = g.num_q_heads;
-    a.grp = g.num_q_heads / g.num_kv_heads;
-    a.R = g.ring_size;
-    a.batch = batch;
-    a.scale = softmax_scale;
+    CanaryArgs<1> a;
+    fill_common(a, g, seq_len, 1, batch, softmax_scale, kl_out, kl_rows, workspace);
+    a.layer[0] = CanaryLayer{ring, q};
     const int D = g.head_dim;
     const size_t lds = canary_lds_bytes(a.R, D, asymmetric);
     dim3 grid((unsigned)(batch * g.num_kv_heads), 3u);
@@ -305,6 +326,22 @@ hipError_t launch_canary(const kv_geometry& g, const uint16_t* ring, const int32
                           : launch_one<128, false>(a, grid, lds, stream);
     return asymmetric ? launch_one<64, true>(a, grid, lds, stream)
                       : launch_one<64, false>(a, grid, lds, stream);
+}
+
+hipError_t launch_canary_layers(const kv_geometry& g, int num_layers,
+                                const uint16_t* const* rings, const int32_t* seq_len, int batch,
+                                const uint16_t* const* q, float softmax_scale, float* kl_out,
+                                float* kl_rows, void* workspace, hipStream_t stream) {
+    CanaryArgs<kMaxCanaryLayers> a;
+    fill_common(a, g, seq_len, canary_counter_layers(g), batch, softmax_scale, kl_out, kl_rows,
+                workspace);
+    for (int l = 0; l < kMaxCanaryLayers; ++l)
+        a.layer[l] = l < num_layers ? CanaryLayer{rings[l], q[l]} : CanaryLayer{nullptr, nullptr};
+    const int D = g.head_dim;
+    const size_t lds = canary_lds_bytes(a.R, D, false);
+    dim3 grid((unsigned)(batch * g.num_kv_heads), 3u, (unsigned)num_layers);
+    if (D == 128) return launch_one<128, false>(a, grid, lds, stream);
+    return launch_one<64, false>(a, grid, lds, stream);
 }
 
 }  // namespace kvq

@@ -23,7 +23,8 @@ hipError_t launch_decode_attn(const kv_geometry& g, PoolPtrs pools, const uint32
                               const uint16_t* q, float softmax_scale, float* out,
                               void* workspace, hipStream_t stream);
 
-// write of n_new <= 16 tokens per sequence fused into the decode attention over pos + n_new
+// write of n_new <= 64 tokens per sequence (at most five pages) fused into the decode attention
+// over pos + n_new
 hipError_t launch_decode_step(const kv_geometry& g, PoolPtrs pools, const uint32_t* bt,
                               const int32_t* pos, int batch, int n_new, const uint16_t* k_new,
                               const uint16_t* v_new, uint16_t* ring, int splits,
@@ -37,6 +38,17 @@ size_t decode_workspace_bytes(const kv_geometry& g, int batch, int splits);
 hipError_t launch_canary(const kv_geometry& g, const uint16_t* ring, const int32_t* seq_len,
                          int batch, const uint16_t* q, float softmax_scale, bool asymmetric,
                          float* kl_out, float* kl_rows, void* workspace, hipStream_t stream);
-size_t canary_workspace_bytes(const kv_geometry& g, int batch);
+// every layer's canary in one grid: rings[l], q[l] (host arrays of device pointers, copied
+// into the launch), l < num_layers <= kMaxCanaryLayers
+constexpr int kMaxCanaryLayers = KV_CANARY_MAX_LAYERS;
+hipError_t launch_canary_layers(const kv_geometry& g, int num_layers,
+                                const uint16_t* const* rings, const int32_t* seq_len, int batch,
+                                const uint16_t* const* q, float softmax_scale, float* kl_out,
+                                float* kl_rows, void* workspace, hipStream_t stream);
+size_t canary_workspace_bytes(const kv_geometry& g, int counter_layers, int num_layers, int batch);
+// the multi-layer call keeps a ticket line per (layer, width) for every layer it may be given
+inline int canary_counter_layers(const kv_geometry& g) {
+    return g.num_layers < kMaxCanaryLayers ? g.num_layers : kMaxCanaryLayers;
+}
 
 }  // namespace kvq

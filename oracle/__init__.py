@@ -73,6 +73,7 @@ def lib():
             "orc_cache_bytes_per_token": (d, [P, i, P]),
             "orc_ring_bytes": (d, [P, i]),
             "orc_num_threads": (i, []),
+            "orc_set_num_threads": (None, [i]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -258,3 +259,7 @@ def ring_bytes(g: Geom, num_layers: int) -> float:
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    lib().orc_set_num_threads(int(n))

@@ -527,3 +527,12 @@ int orc_num_threads(void) {
     return 1;
 #endif
 }
+
+/* threads of the parallel attention loop (a timing knob of the CPU baseline; no effect on results) */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

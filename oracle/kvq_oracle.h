@@ -126,6 +126,7 @@ double orc_cache_bytes_per_token(const orc_geom* g, int num_layers, const int* b
 double orc_ring_bytes(const orc_geom* g, int num_layers);
 
 int orc_num_threads(void);
+void orc_set_num_threads(int n);   /* threads of the parallel loops; results do not depend on it */
 
 #ifdef __cplusplus
 }

@@ -97,6 +97,30 @@ class LayerPair:
         ring_ok = np.array_equal(f16_bits(self.ring), self.oring)
         return bad, ring_ok
 
+    def step(self, k_new: np.ndarray, v_new: np.ndarray, q_u16, pages_per_split=0, scale=None):
+        """kv_decode_step on the GPU (write of the new tokens, then attention over them, one
+        launch), the same write on the oracle side; returns the attention rows and the workspace"""
+        B, n = self.batch, k_new.shape[1]
+        pos = self.len.copy()
+        max_ctx = int((pos + n).max())
+        scale = np.float32(1.0 / math.sqrt(self.d)) if scale is None else np.float32(scale)
+        wsb = kvq.kv_decode_workspace_bytes(self.g, B, max_ctx, pages_per_split)
+        ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+        out = torch.empty((B, self.hq, self.d), dtype=torch.float32, device=DEV)
+        kvq.kv_decode_step(self.g, self.pools, self.bt_dev, to_dev_i32(pos), B, n, to_dev_f16(k_new),
+                           to_dev_f16(v_new), self.ring, max_ctx, to_dev_f16(q_u16), float(scale),
+                           out, ws, wsb, pages_per_split)
+        torch.cuda.synchronize()
+        oracle.quant_write(self.og, self.opools, self.bt, pos, k_new, v_new, self.oring)
+        self.len += n
+        return out.cpu().numpy().astype(np.float64), ws
+
+    def tickets_zero(self, ws: torch.Tensor) -> bool:
+        """the split-ticket counters at the head of an attention workspace -- one 256-byte line
+        per (sequence slot, KV head) of the geometry, plus one line -- are all back at zero"""
+        n = self.g.max_seqs * self.g.num_kv_heads * 256 + 256
+        return not ws[:n].any()
+
     def attn(self, q_u16, ctx=None, scale=None, pages_per_split=0):
         ctx = self.len.copy() if ctx is None else np.asarray(ctx, dtype=np.int32)
         scale = np.float32(1.0 / math.sqrt(self.d)) if scale is None else np.float32(scale)

@@ -109,6 +109,30 @@ def test_kernel_calls_reject_bad_arguments_without_launching():
     kvq.kv_quant_write(g, pools, 0, 0, 1, 0, 0, 0, 0, stream=0)   # n_new == 0: a no-op
 
 
+def test_canary_layers_validation_and_workspace():
+    """kv_canary_kl_layers: every layer's pointers are checked before anything is launched"""
+    g = geom(num_layers=3)
+    rows = 2 * 8 * 3 * 4                                          # batch 2 x 8 q heads x 3 widths
+    assert kvq.kv_canary_workspace_bytes(g, 2) == 3 * 256 + rows
+    # ticket lines for all three layers of the geometry, then the call's rows
+    assert kvq.kv_canary_layers_workspace_bytes(g, 1, 2) == 3 * 3 * 256 + rows
+    assert kvq.kv_canary_layers_workspace_bytes(g, 3, 2) == 3 * 3 * 256 + 3 * rows
+    assert kvq.kv_canary_layers_workspace_bytes(g, 4, 2) == 0      # beyond the geometry's layers
+    assert kvq.kv_canary_layers_workspace_bytes(g, 0, 2) == 0
+    need = kvq.kv_canary_layers_workspace_bytes(g, 3, 2)
+    ok = [256, 512, 768]
+    for rings, qs, n, wsb in (
+            (ok, ok, 4, need),                  # more layers than the geometry has
+            (ok[:2], ok[:2], 0, need),          # no layers
+            ([256, 0, 768], ok, 3, need),       # a NULL ring
+            (ok, [256, 520, 768], 3, need),     # a misaligned q
+            (ok, ok, 3, need - 1)):             # workspace too small
+        with pytest.raises(kvq.KVError) as e:
+            kvq.kv_canary_kl_layers(g, (rings * 2)[:n], 256, 2, (qs * 2)[:n], 0.1, 256, None, 256,
+                                    wsb, stream=0)
+        assert e.value.status == kvq.KV_EINVAL
+
+
 def test_split_plan():
     g = geom(head_dim=128, num_q_heads=40, num_kv_heads=8, max_seqs=1, max_pages_per_seq=2100)
     pps = kvq.kv_decode_pages_per_split(g, 1, 32768)

@@ -1,18 +1,21 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the benchmark times.
 
 For each full-size workload the test takes one layer of every bit-width the workload draws, builds
-the whole cache of that layer at full context on both sides (prefill of N - 1 tokens, then the
-decode token), and compares every written block and the ring bit-exactly, every attention row
-(library split plan) against the oracle's fp64 rows, and the canary. The batched workload also
+the whole cache of that layer at full context on both sides (prefill of N - 1 tokens), writes the
+decode token and attends with the launch the benchmark times (kv_decode_step at the fused step's
+split plan), and compares every written block and the ring bit-exactly, every attention row
+against the oracle's fp64 rows, the fused launch against the two separate calls bit for bit, the
+rows of the library's other split plans, and the canary. The batched workload also
 switches the layer's tier mid-run and writes 64 tokens per sequence per step.
 """
 import numpy as np
 import pytest
+import torch
 
 import mixed_precision_quantized_kv_amd as kvq
 from mixed_precision_quantized_kv_amd import synth
 
-from gpu_cases import LayerPair, rowwise_rel_err
+from gpu_cases import LayerPair, rowwise_rel_err, to_dev_f16, to_dev_i32
 
 pytestmark = pytest.mark.gpu
 
@@ -63,13 +66,40 @@ def test_full_context_layer(name, layer, bits):
                   seed=w.config_id * 100 + layer)
     K, V = synth.keys_values(w, layer, N, synth.S_PREFILL_K, synth.S_PREFILL_V)
     L.write(K[:, :N - 1], V[:, :N - 1])                 # prefill in one call per layer
-    L.write(K[:, N - 1:], V[:, N - 1:])                 # the decode step's own token
+    k1, v1 = K[:, N - 1:].copy(), V[:, N - 1:].copy()
     del K, V
+    q = synth.queries(w, layer)
+    # The decode step's own token through the launch the benchmark times: kv_decode_step at the
+    # fused step's plan (write, then attention over N tokens, in one launch).
+    pre_pools = [t.clone() for t in L.pools_t]
+    pre_ring = L.ring.clone()
+    pps = kvq.kv_decode_step_pages_per_split_for(L.g, L.len, 1)
+    got, ws = L.step(k1, v1, q, pages_per_split=pps)
     bad, ring_ok = L.compare_bytes()
-    print(f"  blocks compared {len(L.used_blocks())}, mismatching {len(bad)}", flush=True)
+    print(f"  fused step (pages per split {pps}): blocks compared {len(L.used_blocks())}, "
+          f"mismatching {len(bad)}", flush=True)
     assert not bad, bad[:5]
     assert ring_ok
-    check_attention_and_canary(L, synth.queries(w, layer))
+    assert L.tickets_zero(ws)
+    err = rowwise_rel_err(got, L.oracle_attn(q))
+    print(f"  fused step attention rows {err.size}: max rel err {err.max():.3e}", flush=True)
+    assert err.max() <= ATTN_TOL, (err.max(), np.unravel_index(np.argmax(err), err.shape))
+    # the same step as two launches from the same state: identical bytes, ring and rows
+    fused_pools = [t.clone() for t in L.pools_t]
+    fused_ring = L.ring.clone()
+    for t, p in zip(L.pools_t, pre_pools):
+        t.copy_(p)
+    L.ring.copy_(pre_ring)
+    del pre_pools, pre_ring
+    pos = to_dev_i32(L.len - 1)
+    kvq.kv_quant_write(L.g, L.pools, L.bt_dev, pos, B, 1, to_dev_f16(k1), to_dev_f16(v1), L.ring)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(L.pools_t, fused_pools))
+    assert torch.equal(L.ring, fused_ring)
+    del fused_pools, fused_ring
+    sep, _ = L.attn(q, pages_per_split=pps)
+    assert np.array_equal(sep, got), "fused step differs from the two separate calls"
+    check_attention_and_canary(L, q)
 
 
 def switching_layer(w):

@@ -1,8 +1,6 @@
 """The fused decode step (kv_decode_step: the write of the step's tokens and the attention over
 them in one launch) against the two separate calls, bit for bit: the same pool bytes, the same
 ring, the same attention rows; and against the oracle."""
-import math
-
 import numpy as np
 import pytest
 import torch
@@ -28,24 +26,6 @@ def make_pair(hq, hkv, d, lens, tiers, max_pages, seed):
             A.write(K, V, rows=[s])
             B.write(K, V, rows=[s])
     return A, B, g
-
-
-def fused_step(L, k_new, v_new, q, pps):
-    """B side: one kv_decode_step; keeps the oracle in step through its own write"""
-    B, n = L.batch, k_new.shape[1]
-    pos = L.len.copy()
-    max_ctx = int((pos + n).max())
-    scale = float(np.float32(1.0 / math.sqrt(L.d)))
-    wsb = kvq.kv_decode_workspace_bytes(L.g, B, max_ctx, pps)
-    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
-    out = torch.empty((B, L.hq, L.d), dtype=torch.float32, device="cuda")
-    kvq.kv_decode_step(L.g, L.pools, L.bt_dev, to_dev_i32(pos), B, n, to_dev_f16(k_new),
-                       to_dev_f16(v_new), L.ring, max_ctx, to_dev_f16(q), scale, out, ws, wsb, pps)
-    torch.cuda.synchronize()
-    import oracle
-    oracle.quant_write(L.og, L.opools, L.bt, pos, k_new, v_new, L.oring)
-    L.len += n
-    return out.cpu().numpy().astype(np.float64), ws
 
 
 @pytest.mark.parametrize("case", ["tiny_token_by_token", "ragged_mixed_n3", "ragged_mixed_n16",
@@ -82,13 +62,13 @@ def test_fused_equals_separate(case):
             assert sep_pps != kvq.kv_decode_pages_per_split_for(B.g, B.len + nn)
         A.write(k_new, v_new)
         ref_sep, _ = A.attn(q, pages_per_split=sep_pps)
-        got, ws = fused_step(B, k_new, v_new, q, pps)
+        got, ws = B.step(k_new, v_new, q, pps)   # B side: one kv_decode_step
         torch.cuda.synchronize()
         for a, b in zip(A.pools_t, B.pools_t):
             assert torch.equal(a, b), f"step {step}: pool bytes differ"
         assert torch.equal(A.ring, B.ring), f"step {step}: ring differs"
         assert np.array_equal(got, ref_sep), f"step {step}: attention differs"
-        assert not ws[:256].any()
+        assert B.tickets_zero(ws)
     bad, ring_ok = B.compare_bytes()
     assert not bad and ring_ok, bad[:5]
     err = rowwise_rel_err(got, B.oracle_attn(q))
