@@ -229,6 +229,21 @@ kv_status kv_decode_step(const kv_geometry* g, const kv_layer_pools* pools, cons
                          const uint16_t* v_new, uint16_t* ring, int max_ctx_len, const uint16_t* q,
                          float softmax_scale, float* out, void* workspace,
                          size_t workspace_bytes, int pages_per_split, void* stream);
+/* kv_decode_step for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same write and attention, same
+ * bytes, ring and outputs, with the workspace taken from a fixed device array inside the
+ * library (16 MiB per GPU, held until the process ends) instead of an argument. The call
+ * allocates nothing. Limits: batch * H_kv <= 4096, and the split partials
+ * (batch*H_kv*splits*(H_q/H_kv)*(D+2)*4 bytes, about) within 15 MiB -- larger calls return
+ * KV_EINVAL with the sizes in kv_last_error(). Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (two streams, two threads) race and must not be issued. The
+ * first call on a device also launches a small kernel that clears the array's counters.
+ * Arguments and other errors as for kv_decode_step, without workspace and workspace_bytes. */
+kv_status kv_decode_step_noalloc(const kv_geometry* g, const kv_layer_pools* pools,
+                                 const uint32_t* bt, const int32_t* pos, int batch, int n_new,
+                                 const uint16_t* k_new, const uint16_t* v_new, uint16_t* ring,
+                                 int max_ctx_len, const uint16_t* q, float softmax_scale,
+                                 float* out, int pages_per_split, void* stream);
 /* The split plan for a fused step whose positions are known on the host (pos_host int32
  * [batch], each >= 0; not retained; n_new as for kv_decode_step): the plan of
  * kv_decode_pages_per_split_for for the lengths pos + n_new, then -- when n_new > 0 and every

@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
             "kv_canary_kl": (i32, [G, P, P, i32, P, ctypes.c_float, P, P, P, sz, P]),
             "kv_canary_kl_asym": (i32, [G, P, P, i32, P, ctypes.c_float, P, P, P, sz, P]),
             "kv_canary_layers_workspace_bytes": (sz, [G, i32, i32]),
+            "kv_decode_step_noalloc": (i32, [G, ctypes.POINTER(LayerPools), P, P, i32, i32, P, P,
+                                             P, i32, P, ctypes.c_float, P, i32, P]),
             "kv_canary_kl_layers": (i32, [G, i32, P, P, i32, P, ctypes.c_float, P, P, P, sz, P]),
         }
         for name, (res, args) in sigs.items():
@@ -369,3 +371,12 @@ def kv_canary_kl_layers(g: Geometry, rings, seq_len, batch: int, qs, softmax_sca
     _check(lib().kv_canary_kl_layers(ctypes.byref(g), n, ring_ptrs, _addr(seq_len), batch, q_ptrs,
                                      softmax_scale, _addr(kl_out), _addr(kl_rows), _addr(workspace),
                                      workspace_bytes, _stream(stream)))
+
+
+def kv_decode_step_noalloc(g: Geometry, pools: LayerPools, bt, pos, batch: int, n_new: int, k_new,
+                           v_new, ring, max_ctx_len: int, q, softmax_scale: float, out,
+                           pages_per_split: int = 0, stream=None) -> None:
+    _check(lib().kv_decode_step_noalloc(ctypes.byref(g), ctypes.byref(pools), _addr(bt), _addr(pos),
+                                        batch, n_new, _addr(k_new), _addr(v_new), _addr(ring),
+                                        max_ctx_len, _addr(q), softmax_scale, _addr(out),
+                                        pages_per_split, _stream(stream)))

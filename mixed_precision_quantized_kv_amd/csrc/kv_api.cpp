@@ -490,6 +490,44 @@ kv_status kv_decode_step(const kv_geometry* g, const kv_layer_pools* pools, cons
                       "kv_decode_step");
 }
 
+kv_status kv_decode_step_noalloc(const kv_geometry* g, const kv_layer_pools* pools,
+                                 const uint32_t* bt, const int32_t* pos, int batch, int n_new,
+                                 const uint16_t* k_new, const uint16_t* v_new, uint16_t* ring,
+                                 int max_ctx_len, const uint16_t* q, float softmax_scale,
+                                 float* out, int pages_per_split, void* stream) {
+    kv_status st = check_geometry(g);
+    if (st != KV_OK) return st;
+    if ((st = check_pools(g, pools)) != KV_OK) return st;
+    if (n_new < 0 || n_new > kMaxFusedNew)
+        return fail(KV_EINVAL, "n_new %d: the fused step writes 0..%d tokens", n_new, kMaxFusedNew);
+    int pps, splits;
+    if ((st = decode_plan(g, batch, max_ctx_len, pages_per_split, &pps, &splits, n_new)) != KV_OK)
+        return st;
+    if (!bt || !pos || !q || !out) return fail(KV_EINVAL, "NULL device pointer");
+    if (n_new > 0 && (!k_new || !v_new || !ring)) return fail(KV_EINVAL, "NULL device pointer");
+    if (reinterpret_cast<uintptr_t>(q) % 4 || reinterpret_cast<uintptr_t>(out) % 16)
+        return fail(KV_EINVAL, "q must be 4-byte and out 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(k_new) % 16 || reinterpret_cast<uintptr_t>(v_new) % 16 ||
+        reinterpret_cast<uintptr_t>(ring) % 16)
+        return fail(KV_EINVAL, "k_new, v_new and ring must be 16-byte aligned");
+    if ((int64_t)batch * g->num_kv_heads > kvq::kStaticMaxGroups)
+        return fail(KV_EINVAL,
+                    "batch %d x %d KV heads: the static scratch holds counters for %d groups",
+                    batch, g->num_kv_heads, kvq::kStaticMaxGroups);
+    const size_t need = kvq::static_scratch_partial_bytes(*g, batch, splits);
+    const size_t room = kvq::kStaticScratchBytes - kvq::kStaticCounterBytes;
+    if (need > room)
+        return fail(KV_EINVAL,
+                    "the split partials need %zu bytes (%d splits); the static scratch holds %zu",
+                    need, splits, room);
+    if (!(softmax_scale == softmax_scale)) return fail(KV_EINVAL, "softmax_scale is NaN");
+    return hip_status(kvq::launch_decode_step_static(*g, pool_ptrs(pools), bt, pos, batch, n_new,
+                                                     k_new, v_new, ring, splits, pps, q,
+                                                     softmax_scale, out,
+                                                     static_cast<hipStream_t>(stream)),
+                      "kv_decode_step_noalloc");
+}
+
 size_t kv_canary_workspace_bytes(const kv_geometry* g, int batch) {
     if (check_geometry(g) != KV_OK || batch < 1) return 0;
     return kvq::canary_workspace_bytes(*g, 1, 1, batch);

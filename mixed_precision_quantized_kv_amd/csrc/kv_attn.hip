@@ -31,6 +31,8 @@
 #include "kvq_launch.hpp"
 #include "kvq_write_dev.hpp"
 
+#include <mutex>
+
 namespace kvq {
 namespace {
 
@@ -1533,13 +1535,11 @@ hipError_t launch_decode_attn(const kv_geometry& g, PoolPtrs pools, const uint32
     return launch<false>(g, a, splits, stream);
 }
 
-hipError_t launch_decode_step(const kv_geometry& g, PoolPtrs pools, const uint32_t* bt,
-                              const int32_t* pos, int batch, int n_new, const uint16_t* k_new,
-                              const uint16_t* v_new, uint16_t* ring, int splits,
-                              int pages_per_split, const uint16_t* q, float softmax_scale,
-                              float* out, void* workspace, hipStream_t stream) {
-    AttnArgs a = attn_args(g, pools, bt, batch, splits, pages_per_split, q, softmax_scale, out,
-                           workspace);
+namespace {
+
+void set_write_args(AttnArgs& a, const kv_geometry& g, PoolPtrs pools, const uint32_t* bt,
+                    const int32_t* pos, int n_new, const uint16_t* k_new, const uint16_t* v_new,
+                    uint16_t* ring) {
     a.pos = pos;
     a.n_new = n_new;
     a.wr.pools = pools;
@@ -1552,6 +1552,100 @@ hipError_t launch_decode_step(const kv_geometry& g, PoolPtrs pools, const uint32
     a.wr.n_new = n_new;
     a.wr.H = g.num_kv_heads;
     a.wr.R = g.ring_size;
+}
+
+}  // namespace
+
+hipError_t launch_decode_step(const kv_geometry& g, PoolPtrs pools, const uint32_t* bt,
+                              const int32_t* pos, int batch, int n_new, const uint16_t* k_new,
+                              const uint16_t* v_new, uint16_t* ring, int splits,
+                              int pages_per_split, const uint16_t* q, float softmax_scale,
+                              float* out, void* workspace, hipStream_t stream) {
+    AttnArgs a = attn_args(g, pools, bt, batch, splits, pages_per_split, q, softmax_scale, out,
+                           workspace);
+    set_write_args(a, g, pools, bt, pos, n_new, k_new, v_new, ring);
+    return launch<true>(g, a, splits, stream);
+}
+
+// ---------------------------------------------------------------- the fixed device scratch
+// For callers that cannot allocate device memory (code under graph capture, tight serving
+// loops): the fused step's workspace -- ticket counters, split maxima and sums, split partial
+// outputs -- lives in one file-scope device array of kStaticScratchBytes, one copy per GPU,
+// held until the process ends. The counters sit at a fixed place (one 256-byte line for each
+// of kStaticMaxGroups (sequence, KV head) groups, whatever the geometry), so the zeros one call
+// leaves there serve the next call of any geometry; the partials follow and are written before
+// they are read. Calls that overlap on one GPU share the array and race.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+static_assert((size_t)kStaticMaxGroups * kCounterStride * 4 == kStaticCounterBytes,
+              "one counter line per group");
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices];     // device address of `scratch` on each GPU
+bool g_scratch_cleared[kMaxDevices];
+
+__global__ void clear_words(uint32_t* p, uint32_t n) {
+    for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+// The scratch array's address on the current device, looked up once per device with that
+// device current (the array's name is a host-side stand-in, never a device address). The first
+// call on a device also clears the counters with a fill kernel on the caller's stream: device
+// arrays without an initializer start at zero when the code object is loaded, and the clear
+// keeps that true even if this first call is captured into a graph rather than run.
+hipError_t static_scratch(hipStream_t stream, uint8_t** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+    }
+    if (!g_scratch_cleared[dev]) {
+        hipLaunchKernelGGL(clear_words, dim3(256), dim3(256), 0, stream,
+                           reinterpret_cast<uint32_t*>(g_scratch_ptr[dev]),
+                           (uint32_t)(kStaticCounterBytes / 4));
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        g_scratch_cleared[dev] = true;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+size_t static_scratch_partial_bytes(const kv_geometry& g, int batch, int splits) {
+    const size_t groups = (size_t)batch * g.num_kv_heads;
+    const size_t grp = (size_t)(g.num_q_heads / g.num_kv_heads);
+    return ((groups * splits * grp * 2 * sizeof(float) + 255) / 256) * 256 +
+           groups * splits * grp * g.head_dim * sizeof(float);
+}
+
+hipError_t launch_decode_step_static(const kv_geometry& g, PoolPtrs pools, const uint32_t* bt,
+                                     const int32_t* pos, int batch, int n_new,
+                                     const uint16_t* k_new, const uint16_t* v_new, uint16_t* ring,
+                                     int splits, int pages_per_split, const uint16_t* q,
+                                     float softmax_scale, float* out, hipStream_t stream) {
+    uint8_t* ws = nullptr;
+    const hipError_t e = static_scratch(stream, &ws);
+    if (e != hipSuccess) return e;
+    AttnArgs a = attn_args(g, pools, bt, batch, splits, pages_per_split, q, softmax_scale, out, ws);
+    const size_t groups = (size_t)a.groups;
+    a.counters = reinterpret_cast<uint32_t*>(ws);
+    a.ws_ml = reinterpret_cast<float*>(ws + kStaticCounterBytes);
+    a.ws_o = reinterpret_cast<float*>(
+        ws + kStaticCounterBytes +
+        ((groups * splits * a.grp * 2 * sizeof(float) + 255) / 256) * 256);
+    set_write_args(a, g, pools, bt, pos, n_new, k_new, v_new, ring);
     return launch<true>(g, a, splits, stream);
 }
 

@@ -34,6 +34,18 @@ hipError_t launch_decode_step(const kv_geometry& g, PoolPtrs pools, const uint32
 // workspace layout of the decode attention (bytes)
 size_t decode_workspace_bytes(const kv_geometry& g, int batch, int splits);
 
+// the fused step with its workspace in a fixed file-scope device array (one per GPU): ticket
+// counters for kStaticMaxGroups (sequence, KV head) groups first, then the split partials
+constexpr int kStaticMaxGroups = 4096;
+constexpr size_t kStaticCounterBytes = (size_t)kStaticMaxGroups * 256;      // 1 MiB
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;                    // 16 MiB
+size_t static_scratch_partial_bytes(const kv_geometry& g, int batch, int splits);
+hipError_t launch_decode_step_static(const kv_geometry& g, PoolPtrs pools, const uint32_t* bt,
+                                     const int32_t* pos, int batch, int n_new,
+                                     const uint16_t* k_new, const uint16_t* v_new, uint16_t* ring,
+                                     int splits, int pages_per_split, const uint16_t* q,
+                                     float softmax_scale, float* out, hipStream_t stream);
+
 // asymmetric: build the temporary copies with the min / max (zero point) quantizer
 hipError_t launch_canary(const kv_geometry& g, const uint16_t* ring, const int32_t* seq_len,
                          int batch, const uint16_t* q, float softmax_scale, bool asymmetric,
