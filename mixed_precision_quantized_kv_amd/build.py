@@ -26,17 +26,11 @@ FLAGS = ["-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-fno-fast-math", "-ffp-contract=fast", "-fhip-fp32-correctly-rounded-divide-sqrt",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
-# Per-source additions. The attention kernel is built without LLVM's load/store vectorizer:
-# with it, INT8 pages read wrong once a wave refills its page buffers inside the page loop
-# (bisected with -opt-bisect-limit to that pass on this kernel; the IR it emits looks sound,
-# so the fault is further down the backend). Without it the backend still forms the same
-# 16-byte global loads, and the kernel runs at the same speed.
-# The controller keeps its averages bit-identical to a plain binary64 evaluation, so it is built
+# Per-source additions. The controller keeps its averages bit-identical to a plain binary64 evaluation, so it is built
 # without floating-point contraction.
 # The attention kernel's first twelve argument dwords (block table, lengths, q, shape) are preloaded into
 # SGPRs at wave launch (gfx950 kernel-argument preloading).
-EXTRA = {"kv_attn.hip": ["-mllvm", "-amdgpu-load-store-vectorizer=0",
-                         "-mllvm", "-amdgpu-kernarg-preload-count=12"],
+EXTRA = {"kv_attn.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=12"],
          "kv_controller.cpp": ["-ffp-contract=off"]}
 
 

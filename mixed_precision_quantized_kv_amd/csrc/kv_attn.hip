@@ -140,12 +140,12 @@ __device__ __forceinline__ void load_page(const PageSrc& a, int kv, int page, bo
     const uint8_t* kp = sec + t * (D * lb / 8) + G * ch;
     const uint8_t* vp = sec + code_bytes + 2 * D + (G * D + t * (D / 16)) * lb / 2;
     const int second = lb == 8 ? 16 : 0;
-    const uint4 k0 = *reinterpret_cast<const uint4*>(kp);
-    const uint4 k1 = *reinterpret_cast<const uint4*>(kp + second);
-    const uint4 v0 = *reinterpret_cast<const uint4*>(vp);
-    const uint4 v1 = *reinterpret_cast<const uint4*>(vp + second);
-    r.ks = *reinterpret_cast<const uint32_t*>(sec + code_bytes + 4 * (lane & (D / 2 - 1)));
-    const uint2 vs = *reinterpret_cast<const uint2*>(sec + 2 * code_bytes + 2 * D + 8 * G);
+    const uint4 k0 = *reinterpret_cast<const ma_uint4*>(kp);
+    const uint4 k1 = *reinterpret_cast<const ma_uint4*>(kp + second);
+    const uint4 v0 = *reinterpret_cast<const ma_uint4*>(vp);
+    const uint4 v1 = *reinterpret_cast<const ma_uint4*>(vp + second);
+    r.ks = *reinterpret_cast<const ma_u32*>(sec + code_bytes + 4 * (lane & (D / 2 - 1)));
+    const uint2 vs = *reinterpret_cast<const ma_uint2*>(sec + 2 * code_bytes + 2 * D + 8 * G);
     r.k[0] = k0.x; r.k[1] = k0.y; r.k[2] = k0.z; r.k[3] = k0.w;
     r.k[4] = k1.x; r.k[5] = k1.y; r.k[6] = k1.z; r.k[7] = k1.w;
     r.v[0] = v0.x; r.v[1] = v0.y; r.v[2] = v0.z; r.v[3] = v0.w;
@@ -179,24 +179,24 @@ __device__ __forceinline__ void load_page_t(const uint8_t* base, uint32_t idx, i
     const uint8_t* kp = sec + t * (D * BITS / 8) + G * ch;
     const uint8_t* vp = sec + code_bytes + 2 * D + (G * D + t * (D / 16)) * BITS / 2;
     if constexpr (ch == 4) {
-        r.k[0] = *reinterpret_cast<const uint32_t*>(kp);
-        r.v[0] = *reinterpret_cast<const uint32_t*>(vp);
+        r.k[0] = *reinterpret_cast<const ma_u32*>(kp);
+        r.v[0] = *reinterpret_cast<const ma_u32*>(vp);
     } else if constexpr (ch == 8) {
-        const uint2 k0 = *reinterpret_cast<const uint2*>(kp);
-        const uint2 v0 = *reinterpret_cast<const uint2*>(vp);
+        const uint2 k0 = *reinterpret_cast<const ma_uint2*>(kp);
+        const uint2 v0 = *reinterpret_cast<const ma_uint2*>(vp);
         r.k[0] = k0.x; r.k[1] = k0.y;
         r.v[0] = v0.x; r.v[1] = v0.y;
     } else {
 #pragma unroll
         for (int h = 0; h < ch / 16; ++h) {
-            const uint4 k0 = *reinterpret_cast<const uint4*>(kp + 16 * h);
-            const uint4 v0 = *reinterpret_cast<const uint4*>(vp + 16 * h);
+            const uint4 k0 = *reinterpret_cast<const ma_uint4*>(kp + 16 * h);
+            const uint4 v0 = *reinterpret_cast<const ma_uint4*>(vp + 16 * h);
             r.k[4 * h] = k0.x; r.k[4 * h + 1] = k0.y; r.k[4 * h + 2] = k0.z; r.k[4 * h + 3] = k0.w;
             r.v[4 * h] = v0.x; r.v[4 * h + 1] = v0.y; r.v[4 * h + 2] = v0.z; r.v[4 * h + 3] = v0.w;
         }
     }
-    r.ks = *reinterpret_cast<const uint32_t*>(sec + code_bytes + 4 * (lane & (D / 2 - 1)));
-    const uint2 vs = *reinterpret_cast<const uint2*>(sec + 2 * code_bytes + 2 * D + 8 * G);
+    r.ks = *reinterpret_cast<const ma_u32*>(sec + code_bytes + 4 * (lane & (D / 2 - 1)));
+    const uint2 vs = *reinterpret_cast<const ma_uint2*>(sec + 2 * code_bytes + 2 * D + 8 * G);
     r.vs[0] = vs.x; r.vs[1] = vs.y;
     r.bits = present ? BITS : 0;
     r.ntok = ntok;
@@ -275,7 +275,7 @@ __device__ __forceinline__ float4v page_logits(const PageRaw& r, int bits, const
     uint32_t ks[D / 8];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) {
-        const uint4 v = *reinterpret_cast<const uint4*>(lds_ks + G * (D / 8) + 4 * i);
+        const uint4 v = *reinterpret_cast<const ma_uint4*>(lds_ks + G * (D / 8) + 4 * i);
         ks[4 * i] = v.x; ks[4 * i + 1] = v.y; ks[4 * i + 2] = v.z; ks[4 * i + 3] = v.w;
     }
     uint32_t kf[D / 8];
@@ -432,8 +432,8 @@ __device__ __forceinline__ void process_pair_half(const PageRaw& A, const PageRa
         uint32_t ksa[D / 8], ksb[D / 8];
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) {
-            const uint4 va = *reinterpret_cast<const uint4*>(lds_ks + G * (D / 8) + 4 * i);
-            const uint4 vb = *reinterpret_cast<const uint4*>(lds_ks + 64 + G * (D / 8) + 4 * i);
+            const uint4 va = *reinterpret_cast<const ma_uint4*>(lds_ks + G * (D / 8) + 4 * i);
+            const uint4 vb = *reinterpret_cast<const ma_uint4*>(lds_ks + 64 + G * (D / 8) + 4 * i);
             ksa[4 * i] = va.x; ksa[4 * i + 1] = va.y; ksa[4 * i + 2] = va.z; ksa[4 * i + 3] = va.w;
             ksb[4 * i] = vb.x; ksb[4 * i + 1] = vb.y; ksb[4 * i + 2] = vb.z; ksb[4 * i + 3] = vb.w;
         }
@@ -464,7 +464,7 @@ __device__ __forceinline__ void process_pair_half(const PageRaw& A, const PageRa
         const uint32_t* src = lds_ks + (side ? 64 : 0) + G * (D / 8);
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) {
-            const uint4 v = *reinterpret_cast<const uint4*>(src + 4 * i);
+            const uint4 v = *reinterpret_cast<const ma_uint4*>(src + 4 * i);
             ks[4 * i] = v.x; ks[4 * i + 1] = v.y; ks[4 * i + 2] = v.z; ks[4 * i + 3] = v.w;
         }
         uint32_t qh[D / 8], ql[D / 8];
@@ -566,8 +566,8 @@ struct PageF16 {
 template <int D>
 __device__ __forceinline__ void load_page_f16(const uint8_t* sec, int lane, PageF16<D>& r) {
     const int t = lane & 15, G = lane >> 4;
-    const uint4* kp = reinterpret_cast<const uint4*>(sec + t * 2 * D + G * (D / 2));
-    const uint4* vp = reinterpret_cast<const uint4*>(sec + 2 * kPage * D + (G * D + t * (D / 16)) * 8);
+    const ma_uint4* kp = reinterpret_cast<const ma_uint4*>(sec + t * 2 * D + G * (D / 2));
+    const ma_uint4* vp = reinterpret_cast<const ma_uint4*>(sec + 2 * kPage * D + (G * D + t * (D / 16)) * 8);
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) {
         const uint4 kk = kp[i], vv = vp[i];
@@ -824,14 +824,14 @@ struct FastPair {
 template <int KW>
 __device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* w) {
     if constexpr (KW == 1) {
-        w[0] = *reinterpret_cast<const uint32_t*>(p);
+        w[0] = *reinterpret_cast<const ma_u32*>(p);
     } else if constexpr (KW == 2) {
-        const uint2 x = *reinterpret_cast<const uint2*>(p);
+        const uint2 x = *reinterpret_cast<const ma_uint2*>(p);
         w[0] = x.x; w[1] = x.y;
     } else {
 #pragma unroll
         for (int h = 0; h < KW / 4; ++h) {
-            const uint4 x = *reinterpret_cast<const uint4*>(p + 16 * h);
+            const uint4 x = *reinterpret_cast<const ma_uint4*>(p + 16 * h);
             w[4 * h] = x.x; w[4 * h + 1] = x.y; w[4 * h + 2] = x.z; w[4 * h + 3] = x.w;
         }
     }
@@ -972,7 +972,7 @@ __device__ __forceinline__ void read_kscales(const uint32_t* ks_lds, int slot, i
         __builtin_assume_aligned(ks_lds + slot * kKsSlot<D> + G * kKsQuarter<D>, 16));
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(src + 4 * i);
+        const u32x4 v = *reinterpret_cast<const ma_u32x4*>(src + 4 * i);
         ks[4 * i] = v[0]; ks[4 * i + 1] = v[1]; ks[4 * i + 2] = v[2]; ks[4 * i + 3] = v[3];
     }
 }
@@ -1181,6 +1181,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
                                                                   int pps, int Hq, int grp,
                                                                   AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t lds_ks[kWaves][2][64];
+    // the K scales of the uniform-width loop's page pairs, staged per wave (stage_kscale)
+    __shared__ __attribute__((aligned(16))) uint32_t lds_ksr[kWaves][2 * kKsSlot<D>];
     // per-wave partials, one padded row per head: channel c of head h sits at h*kORow + c +
     // 4*(c/32), so the float4 writes of a wave's 64 lanes (16 heads x 4 channel quarters) spread
     // over all LDS banks instead of landing on the same four
@@ -1211,7 +1213,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
     const int hq = HALF ? (h & 7) : h;                 // the query head of this lane's column
     uint32_t qf[D / 8];
     {
-        const uint32_t* qp = reinterpret_cast<const uint32_t*>(
+        const ma_u32* qp = reinterpret_cast<const ma_u32*>(
             qv + ((size_t)s * Hq + kv * grp + min(hq, grp - 1)) * D + G * (D / 4));
 #pragma unroll
         for (int i = 0; i < D / 8; ++i) qf[i] = hq < grp ? qp[i] : 0u;
@@ -1277,7 +1279,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
             tier0 = (int)((uint32_t)__builtin_amdgcn_readfirstlane((int)hv) >> 30);
             uniform = __builtin_amdgcn_ballot_w64((int)(hv >> 30) != tier0) == 0;
         }
-        uint32_t* ks_round = reinterpret_cast<uint32_t*>(&lds_o[wave][0]);  // free until the merge
+        uint32_t* ks_round = &lds_ksr[wave][0];
         if (HALF && uniform && tier0 == 0)
             wave_chunk_fast<D, 2, kDepth2>(a.pools.base[0], hv, a.H, kv, cb, npg, ctx, lane, qf,
                                            ks_round, a.scale_log2, st);
@@ -1332,7 +1334,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
         for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int k4 = 0; k4 < D / 64; ++k4)
-                *reinterpret_cast<float4v*>(&lds_o[wave][h * kORow + G * (D / 4) + r * (D / 16) + 4 * k4 +
+                *reinterpret_cast<ma_f32x4*>(&lds_o[wave][h * kORow + G * (D / 4) + r * (D / 16) + 4 * k4 +
                                                          4 * ((G * (D / 4) + r * (D / 16)) / 32)]) =
                     float4v{st.o[4 * k4][r], st.o[4 * k4 + 1][r], st.o[4 * k4 + 2][r], st.o[4 * k4 + 3][r]};
     }
@@ -1359,12 +1361,12 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
         for (int w = 0; w < kWaves; ++w) {
             const float mw = lds_m[w][hh];
             const float e = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-            acc += e * *reinterpret_cast<const float4v*>(&lds_o[w][hh * kORow + 4 * c4 + 4 * (c4 / 8)]);
+            acc += e * *reinterpret_cast<const ma_f32x4*>(&lds_o[w][hh * kORow + 4 * c4 + 4 * (c4 / 8)]);
             L += e * lds_l[w][hh];
         }
         if (single) {
             const float inv = L > 0.f ? 1.f / L : 0.f;
-            *reinterpret_cast<float4v*>(a.out + ((size_t)s * a.Hq + kv * grp + hh) * D + 4 * c4) = acc * inv;
+            *reinterpret_cast<ma_f32x4*>(a.out + ((size_t)s * a.Hq + kv * grp + hh) * D + 4 * c4) = acc * inv;
         } else {
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), o_rsrc,
                                                    (int)((split * grp + hh) * D + 4 * c4) * 4, 0, kSc1);
@@ -1444,7 +1446,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
         for (int i = 0; i < kBatch; ++i)
             if (kb + i < k1) acc += lds_ml[hh][kb + i].x * buf[i];
     }
-    float4v* part_acc = reinterpret_cast<float4v*>(&lds_o[0][0]);   // [parts][slots]
+    float4v* part_acc = reinterpret_cast<ma_f32x4*>(&lds_o[0][0]);   // [parts][slots]
     if (has_job) part_acc[pidx * nslot + slot] = acc;
     __syncthreads();
     if (tid < nslot) {
@@ -1452,7 +1454,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
         for (int pi = 1; pi < parts; ++pi) sum += part_acc[pi * nslot + tid];
         const float L = lds_L[tid / (D / 4)];
         const float inv = L > 0.f ? 1.f / L : 0.f;
-        *reinterpret_cast<float4v*>(a.out + ((size_t)s * a.Hq + kv * grp) * D + tid * 4) = sum * inv;
+        *reinterpret_cast<ma_f32x4*>(a.out + ((size_t)s * a.Hq + kv * grp) * D + tid * 4) = sum * inv;
     }
     if (tid == 0)
         __hip_atomic_store(&a.counters[group * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void canary_kernel(CanaryArgs<NL> a) {
         }
     }
     for (int i = tid; i < grp * (D / 8); i += kThreads) {
-        const uint4 v = *reinterpret_cast<const uint4*>(qv + ((size_t)s * a.Hq + kv * grp) * D + 8 * i);
+        const uint4 v = *reinterpret_cast<const ma_uint4*>(qv + ((size_t)s * a.Hq + kv * grp) * D + 8 * i);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {

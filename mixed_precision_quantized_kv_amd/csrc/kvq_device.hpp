@@ -9,6 +9,17 @@
 
 namespace kvq {
 
+// Typeless views of device memory: the pools, rings, workspaces and LDS buffers are raw bytes
+// read and written as words of several widths (and the kernels reuse LDS for more than one
+// purpose), so every access through a reinterpreted pointer uses a may_alias type and no
+// type-based alias assumption can reorder two accesses to the same bytes.
+typedef uint4 __attribute__((may_alias)) ma_uint4;
+typedef uint2 __attribute__((may_alias)) ma_uint2;
+typedef uint32_t __attribute__((may_alias)) ma_u32;
+typedef uint16_t __attribute__((may_alias)) ma_u16;
+typedef uint32_t __attribute__((ext_vector_type(4), may_alias)) ma_u32x4;
+typedef float __attribute__((ext_vector_type(4), may_alias)) ma_f32x4;
+
 constexpr int kPage = 16;
 constexpr int kMaxGroup = 16;   // query heads per KV head handled by one MFMA tile
 

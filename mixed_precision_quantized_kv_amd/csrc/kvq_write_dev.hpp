@@ -36,7 +36,7 @@ struct WriteArgs {
 template <int CPT>
 __device__ __forceinline__ void load_f16(const uint16_t* p, float* out) {
     if constexpr (CPT == 8) {
-        const uint4 v = *reinterpret_cast<const uint4*>(p);
+        const uint4 v = *reinterpret_cast<const ma_uint4*>(p);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -44,7 +44,7 @@ __device__ __forceinline__ void load_f16(const uint16_t* p, float* out) {
             out[2 * i + 1] = f16_val((uint16_t)(w[i] >> 16));
         }
     } else {
-        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        const uint2 v = *reinterpret_cast<const ma_uint2*>(p);
         const uint32_t w[2] = {v.x, v.y};
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -122,7 +122,7 @@ __device__ __forceinline__ void write_page(const WriteArgs& a, int s, int kv, in
     const bool quad_old = 4 * quad < told;      // the quad holds tokens cached before the call
     const bool quad_new = 4 * quad + 3 >= told && 4 * quad < nk;
     const bool quad_store = active && (quad_new || !quad_old);   // entirely-old quads: untouched
-    uint32_t* vwords = reinterpret_cast<uint32_t*>(sec + L.vcode_off);
+    ma_u32* vwords = reinterpret_cast<ma_u32*>(sec + L.vcode_off);
     const int wbase = ((quad * D + c0) * 4) / (32 / bits);  // first V word of this (quad, group)
     uint32_t vold[2] = {0u, 0u};                // at most 8 words / 4 lanes
     if (quad_store && quad_old && !fp16) {
@@ -157,11 +157,11 @@ __device__ __forceinline__ void write_page(const WriteArgs& a, int s, int kv, in
                 kb[i] = present ? f16_bits((_Float16)kf[i]) : (uint16_t)0;
                 vb[i] = is_new ? f16_bits((_Float16)vf[i]) : (uint16_t)0;
             }
-            uint16_t* krow = reinterpret_cast<uint16_t*>(sec) + (size_t)t * D + c0;
+            ma_u16* krow = reinterpret_cast<ma_u16*>(sec) + (size_t)t * D + c0;
 #pragma unroll
             for (int i = 0; i < CPT; i += 2)
-                reinterpret_cast<uint32_t*>(krow)[i / 2] = kb[i] | ((uint32_t)kb[i + 1] << 16);
-            uint16_t* vvals = reinterpret_cast<uint16_t*>(sec + L.vcode_off);
+                reinterpret_cast<ma_u32*>(krow)[i / 2] = kb[i] | ((uint32_t)kb[i + 1] << 16);
+            ma_u16* vvals = reinterpret_cast<ma_u16*>(sec + L.vcode_off);
 #pragma unroll
             for (int i = 0; i < CPT; ++i) vvals[((size_t)(quad * D + c0 + i)) * 4 + r] = vb[i];
         }
@@ -180,7 +180,7 @@ __device__ __forceinline__ void write_page(const WriteArgs& a, int s, int kv, in
 
     // ---- K codes: row t holds D codes, 32/b per word; this thread's CPT codes fill CPT*b bits
     {
-        uint32_t* row = reinterpret_cast<uint32_t*>(sec + (size_t)t * (D * bits / 8));
+        ma_u32* row = reinterpret_cast<ma_u32*>(sec + (size_t)t * (D * bits / 8));
         const int per_word = 32 / bits;
         if (CPT * bits >= 32) {                 // whole words: INT4/INT8 (D=128), INT8 (D=64)
             const int nw = CPT * bits / 32;
@@ -204,16 +204,16 @@ __device__ __forceinline__ void write_page(const WriteArgs& a, int s, int kv, in
     }
     // K scales (one slot row writes them)
     if (t == 0) {
-        uint16_t* dst = reinterpret_cast<uint16_t*>(sec + L.kscale_off) + c0;
+        ma_u16* dst = reinterpret_cast<ma_u16*>(sec + L.kscale_off) + c0;
         if constexpr (CPT == 8) {
             uint4 v;
             v.x = ks[0] | ((uint32_t)ks[1] << 16); v.y = ks[2] | ((uint32_t)ks[3] << 16);
             v.z = ks[4] | ((uint32_t)ks[5] << 16); v.w = ks[6] | ((uint32_t)ks[7] << 16);
-            *reinterpret_cast<uint4*>(dst) = v;
+            *reinterpret_cast<ma_uint4*>(dst) = v;
         } else {
             uint2 v;
             v.x = ks[0] | ((uint32_t)ks[1] << 16); v.y = ks[2] | ((uint32_t)ks[3] << 16);
-            *reinterpret_cast<uint2*>(dst) = v;
+            *reinterpret_cast<ma_uint2*>(dst) = v;
         }
     }
 
@@ -265,7 +265,7 @@ __device__ __forceinline__ void write_page(const WriteArgs& a, int s, int kv, in
     }
     // V scales: new tokens get theirs, empty slots zero; earlier tokens keep theirs
     if (g == 0 && t >= told)
-        reinterpret_cast<uint16_t*>(sec + L.vscale_off)[t] = vs;
+        reinterpret_cast<ma_u16*>(sec + L.vscale_off)[t] = vs;
 }
 
 // The ring update for sequence s, KV head kv: the newest min(n_new, R) keys into their slots.
@@ -284,9 +284,9 @@ __device__ __forceinline__ void write_ring(const WriteArgs& a, int s, int kv, in
         const uint16_t* src = a.k_new + (((size_t)s * a.n_new + (pp - p0)) * a.H + kv) * D + cc;
         uint16_t* dst = ring_s + ((size_t)(pp % a.R) * a.H + kv) * D + cc;
         if constexpr (CPT == 8)
-            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+            *reinterpret_cast<ma_uint4*>(dst) = *reinterpret_cast<const ma_uint4*>(src);
         else
-            *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+            *reinterpret_cast<ma_uint2*>(dst) = *reinterpret_cast<const ma_uint2*>(src);
     }
 }
 
