@@ -978,7 +978,8 @@ __device__ __forceinline__ void read_kscales(const uint32_t* ks_lds, int slot, i
 }
 
 // S^T of one pair for this lane's side (tokens 4G..4G+3 of its page, head h % 8), log2 units
-template <int D, int BITS>
+// SINGLE: page B is absent (a chunk's odd last page): its keys are neither decoded nor multiplied
+template <int D, int BITS, bool SINGLE = false>
 __device__ __forceinline__ float4v pair_logits(const FastPair<D, BITS>& P, const uint32_t* qf,
                                                const uint32_t* ks_lds, int lane, bool side,
                                                float scale_log2) {
@@ -986,7 +987,7 @@ __device__ __forceinline__ float4v pair_logits(const FastPair<D, BITS>& P, const
     float4v acca = {0.f, 0.f, 0.f, 0.f}, accb = {0.f, 0.f, 0.f, 0.f};
     uint32_t kfa[D / 8], kfb[D / 8];
     unpack_k_fast<D, BITS>(P.ka, kfa);
-    unpack_k_fast<D, BITS>(P.kb, kfb);
+    if constexpr (!SINGLE) unpack_k_fast<D, BITS>(P.kb, kfb);
     if constexpr (BITS == 2) {
         // codes -1, 0, 1: code * scale is exact in fp16, so the scales fold into the keys
         uint32_t ksa[D / 8], ksb[D / 8];
@@ -995,15 +996,17 @@ __device__ __forceinline__ float4v pair_logits(const FastPair<D, BITS>& P, const
 #pragma unroll
         for (int i = 0; i < D / 8; ++i) {
             kfa[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, kfa[i]) * __builtin_bit_cast(half2v, ksa[i]));
-            kfb[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, kfb[i]) * __builtin_bit_cast(half2v, ksb[i]));
+            if constexpr (!SINGLE)
+                kfb[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, kfb[i]) * __builtin_bit_cast(half2v, ksb[i]));
         }
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) {
             const half8 qq = make_half8(qf[4 * i], qf[4 * i + 1], qf[4 * i + 2], qf[4 * i + 3]);
             acca = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                 make_half8(kfa[4 * i], kfa[4 * i + 1], kfa[4 * i + 2], kfa[4 * i + 3]), qq, acca, 0, 0, 0);
-            accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                make_half8(kfb[4 * i], kfb[4 * i + 1], kfb[4 * i + 2], kfb[4 * i + 3]), qq, accb, 0, 0, 0);
+            if constexpr (!SINGLE)
+                accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    make_half8(kfb[4 * i], kfb[4 * i + 1], kfb[4 * i + 2], kfb[4 * i + 3]), qq, accb, 0, 0, 0);
         }
     } else {
         // q * Kscale of this lane's side page as fp16 hi + lo, against both pages' keys
@@ -1023,11 +1026,13 @@ __device__ __forceinline__ float4v pair_logits(const FastPair<D, BITS>& P, const
             const half8 hq = make_half8(qh[4 * i], qh[4 * i + 1], qh[4 * i + 2], qh[4 * i + 3]);
             const half8 lq = make_half8(ql[4 * i], ql[4 * i + 1], ql[4 * i + 2], ql[4 * i + 3]);
             const half8 ka = make_half8(kfa[4 * i], kfa[4 * i + 1], kfa[4 * i + 2], kfa[4 * i + 3]);
-            const half8 kb = make_half8(kfb[4 * i], kfb[4 * i + 1], kfb[4 * i + 2], kfb[4 * i + 3]);
             acca = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, hq, acca, 0, 0, 0);
             acca = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, lq, acca, 0, 0, 0);
-            accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, hq, accb, 0, 0, 0);
-            accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, lq, accb, 0, 0, 0);
+            if constexpr (!SINGLE) {
+                const half8 kb = make_half8(kfb[4 * i], kfb[4 * i + 1], kfb[4 * i + 2], kfb[4 * i + 3]);
+                accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, hq, accb, 0, 0, 0);
+                accb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, lq, accb, 0, 0, 0);
+            }
         }
     }
     return (side ? accb : acca) * scale_log2;
@@ -1067,8 +1072,8 @@ __device__ __forceinline__ float max2(float a, float b, float pinf) {
     return __builtin_amdgcn_fmed3f(a, b, pinf);
 }
 
-// one page pair: QK, the running maxima, then PV
-template <int D, int BITS>
+// one page pair: QK, the running maxima, then PV (SINGLE: page B is absent)
+template <int D, int BITS, bool SINGLE = false>
 __device__ __forceinline__ void round_fast(const FastPair<D, BITS>& P, const uint32_t* qf,
                                            uint32_t* ks_lds, int lane, int bp16, int bp32, float pinf,
                                            float scale_log2, WaveState<D>& st) {
@@ -1082,7 +1087,7 @@ __device__ __forceinline__ void round_fast(const FastPair<D, BITS>& P, const uin
     stage_kscale<D>(ks_lds, 0, lane, P.ksa);
     stage_kscale<D>(ks_lds, 1, lane, P.ksb);
     __builtin_amdgcn_wave_barrier();
-    float4v lg = pair_logits<D, BITS>(P, qf, ks_lds, lane, side, scale_log2);
+    float4v lg = pair_logits<D, BITS, SINGLE>(P, qf, ks_lds, lane, side, scale_log2);
     if (partial) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -1115,7 +1120,12 @@ __device__ __forceinline__ void round_fast(const FastPair<D, BITS>& P, const uin
     // in the same positions)
     uint32_t va[D / 8], vb[D / 8];
     unpack_k_fast<D, BITS>(P.va, va);
-    unpack_k_fast<D, BITS>(P.vb, vb);
+    if constexpr (SINGLE) {
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) vb[i] = 0u;
+    } else {
+        unpack_k_fast<D, BITS>(P.vb, vb);
+    }
 #pragma unroll
     for (int k = 0; k < D / 16; ++k)
         st.o[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
@@ -1157,11 +1167,17 @@ __device__ __forceinline__ void wave_chunk_fast(const uint8_t* base, uint32_t hv
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    // the last nq % DEPTH pairs: the rotation has already loaded them into b[0 ..]
+    // the last nq % DEPTH pairs: the rotation has already loaded them into b[0 ..]; the last
+    // of a chunk with an odd page count holds one page only and skips the absent page's work
 #pragma unroll
-    for (int i = 0; i < DEPTH - 1; ++i)
-        if (i < nq - nfull * DEPTH)
-            round_fast<D, BITS>(b[i], qf, ks_lds, lane, bp16, bp32, pinf, scale_log2, st);
+    for (int i = 0; i < DEPTH - 1; ++i) {
+        if (i < nq - nfull * DEPTH) {
+            if ((npg & 1) && i == nq - nfull * DEPTH - 1)
+                round_fast<D, BITS, true>(b[i], qf, ks_lds, lane, bp16, bp32, pinf, scale_log2, st);
+            else
+                round_fast<D, BITS>(b[i], qf, ks_lds, lane, bp16, bp32, pinf, scale_log2, st);
+        }
+    }
 }
 
 // HALF: the group has at most 8 query heads (see process_pair_half). FUSED: the kernel first
@@ -1446,7 +1462,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
         for (int i = 0; i < kBatch; ++i)
             if (kb + i < k1) acc += lds_ml[hh][kb + i].x * buf[i];
     }
-    float4v* part_acc = reinterpret_cast<ma_f32x4*>(&lds_o[0][0]);   // [parts][slots]
+    ma_f32x4* part_acc = reinterpret_cast<ma_f32x4*>(&lds_o[0][0]);   // [parts][slots]
     if (has_job) part_acc[pidx * nslot + slot] = acc;
     __syncthreads();
     if (tid < nslot) {
