@@ -42,8 +42,8 @@ ATTN_SRC = [os.path.join(ROOT, "mixed_precision_quantized_kv_amd", "csrc", f)
 # (FETCH_SIZE, WRITE_SIZE) scaled by the same counters' reading for a plain copy kernel of known
 # size. It describes the kernel sources with this digest only; after any change to them
 # the bench reports traffic as null until the counters are taken again.
-ATTN_TRAFFIC = {"source_sha256": "701d6c67f8a3a374890af288c892136d183c777cea3b8340c4224a866f377b3f",
-                "bytes_per_launch": 45355460,
+ATTN_TRAFFIC = {"source_sha256": "b2002cf902dc18fcbfc50c4110fc678ce82c4e522fa806371c07f56281d4cfc6",
+                "bytes_per_launch": 45360672,
                 # the bench's algorithmic bytes per launch at the counter run's contexts
                 "algorithmic_bytes_per_launch": 41804027}
 
