@@ -67,7 +67,7 @@ struct AttnArgs {
     const uint16_t* q;
     float* out;
     uint32_t* counters;   // [groups][kCounterStride]: one counter per group, each in its own line
-    float* ws_ml;         // [groups][splits][group][2] (max, sum) in log2 units
+    float* ws_ml;         // [groups][group][splits][2] (max, sum) in log2 units
     float* ws_o;          // [groups][splits][group][D]
     int max_pages;
     int H;                // KV heads
@@ -1206,8 +1206,6 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
     __shared__ __attribute__((aligned(16))) float lds_o[kWaves][kMaxGroup * kORow];
     __shared__ float lds_m[kWaves][kMaxGroup];
     __shared__ float lds_l[kWaves][kMaxGroup];
-    __shared__ float2 lds_ml[kMaxGroup][kMaxSplits]; // (max, sum) of every split in the final merge
-    __shared__ float lds_L[kMaxGroup];
     __shared__ int lds_last;
 
     const int split = blockIdx.x / groups, group = blockIdx.x % groups;
@@ -1388,7 +1386,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
                                                    (int)((split * grp + hh) * D + 4 * c4) * 4, 0, kSc1);
             if (c4 == 0)
                 __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, float2v{M, L}), ml_rsrc,
-                                                      (split * grp + hh) * 8, 0, kSc1);
+                                                      (hh * a.splits + split) * 8, 0, kSc1);
         }
     }
     if (single) return;
@@ -1404,73 +1402,78 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
     __syncthreads();
     if (!lds_last) return;
 
-    // Output slot `slot` (four channels of one head) is summed over the splits by `parts`
-    // threads, each over a contiguous run of at most kBatch splits per round. Every thread
-    // issues its first round of partial loads together with the (max, sum) pairs, so the merge
-    // costs one memory round trip in the common case; loads past a thread's range take an
-    // offset outside the workspace and read zero without touching memory. The split weights
-    // are formed once per head from the pairs staged in LDS, and the splits are always
-    // combined in index order.
+    // One wave per head. The wave first requests the head's (max, sum) pairs (lane k: splits
+    // k, k+64, ...; contiguous per head) and then its first kBatch partials per lane -- lane
+    // (c4, part) sums four channels over a contiguous run of the splits -- so both arrive in one
+    // memory round trip. The split weights e_k = 2^(m_k - M) are formed once, at the lane that
+    // holds the pair, and pass to the other lanes through the wave's own LDS row; the parts
+    // combine by lane exchanges. No workgroup barrier is taken. Loads past a lane's run
+    // re-read its last split and get weight zero.
     constexpr int kBatch = 16;
-    constexpr uint32_t kNowhere = 0xffffff00u;           // past num_records for every dword
-    const int parts = max(1, min(nsplit, (kWaves * 64) / nslot));
-    const int per_part = (nsplit + parts - 1) / parts;
-    const bool has_job = tid < nslot * parts;
-    const int job = has_job ? tid : 0;
-    const int slot = job % nslot, pidx = job / nslot;
-    const int hh = slot / (D / 4);
-    const int k0 = pidx * per_part;                      // this job's splits: [k0, k1)
-    const int k1 = min(nsplit, k0 + per_part);
-    float4v buf[kBatch];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i)
-        buf[i] = __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(
-            o_rsrc, k0 + i < k1 ? (uint32_t)(((k0 + i) * grp * D + slot * 4) * 4) : kNowhere, 0, kSc1));
-    const int npair = nsplit * grp;
-    for (int i = tid; i < npair; i += kWaves * 64) {
-        const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(ml_rsrc, i * 8, 0, kSc1));
-        lds_ml[i % grp][i / grp] = float2{__builtin_bit_cast(float, v.x), __builtin_bit_cast(float, v.y)};
-    }
-    __syncthreads();
-    // split weights, one wave per head, one lane per split: M = max_k m_k, e_k = 2^(m_k - M),
-    // L = sum_k e_k * l_k; the weights go back to LDS for the accumulation
+    constexpr int kParts = 256 / D;                      // lanes per output slot
+    float* e_row = &lds_o[wave][0];                      // kMaxSplits weights of this wave's head
+    const int c4 = lane % (D / 4), part = lane / (D / 4);
+    const int per_part = (nsplit + kParts - 1) / kParts;
+    const int k0 = min(nsplit, part * per_part), k1 = min(nsplit, k0 + per_part);
+    const uint32_t stride = (uint32_t)(grp * D * 4);     // bytes from one split's partial to the next
     for (int h2 = wave; h2 < grp; h2 += kWaves) {
-        float M = -INFINITY;
-        for (int k = lane; k < nsplit; k += 64) M = fmaxf(M, lds_ml[h2][k].x);
-        M = wave_max(M);
-        float L = 0.f;
-        for (int k = lane; k < nsplit; k += 64) {
-            const float2 ml = lds_ml[h2][k];
-            const float e = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
-            lds_ml[h2][k].x = e;
-            L += e * ml.y;
-        }
-        L = wave_sum(L);
-        if (lane == 0) lds_L[h2] = L;
-    }
-    __syncthreads();
-    float4v acc = {0.f, 0.f, 0.f, 0.f};
+        float2v ml[kMaxSplits / 64];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i)
-        if (k0 + i < k1) acc += lds_ml[hh][k0 + i].x * buf[i];
-    for (int kb = k0 + kBatch; kb < k1; kb += kBatch) {         // long split lists only
+        for (int r = 0; r < kMaxSplits / 64; ++r)
+            if (64 * r < nsplit)                         // uniform
+                ml[r] = __builtin_bit_cast(float2v, __builtin_amdgcn_raw_buffer_load_b64(
+                    ml_rsrc, (uint32_t)((h2 * a.splits + min(64 * r + lane, nsplit - 1)) * 8), 0, kSc1));
+        // the offsets in VGPRs: as scalars, the offsets of a batch would each take a register
+        // (a part without splits reads split nsplit-1, in range, and gives it weight zero)
+        uint32_t off = (uint32_t)((min(k0, nsplit - 1) * grp + h2) * D * 4 + c4 * 16);
+        uint32_t last = k1 > k0 ? off + (uint32_t)(k1 - 1 - k0) * stride : off;
+        asm("" : "+v"(off), "+v"(last));
+        float4v buf[kBatch];
 #pragma unroll
         for (int i = 0; i < kBatch; ++i)
             buf[i] = __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(
-                o_rsrc, kb + i < k1 ? (uint32_t)(((kb + i) * grp * D + slot * 4) * 4) : kNowhere, 0, kSc1));
+                o_rsrc, min(off + (uint32_t)i * stride, last), 0, kSc1));
+        float M = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < kMaxSplits / 64; ++r)
+            if (64 * r < nsplit) M = fmaxf(M, ml[r][0]);
+        M = wave_max(M);
+        float L = 0.f;
+#pragma unroll
+        for (int r = 0; r < kMaxSplits / 64; ++r)
+            if (64 * r < nsplit) {
+                const int k = 64 * r + lane;
+                const float e = k >= nsplit || ml[r][0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[r][0] - M);
+                L += e * ml[r][1];
+                if (k < nsplit) e_row[k] = e;
+            }
+        L = wave_sum(L);
+        __builtin_amdgcn_wave_barrier();                 // the wave's LDS accesses stay in order
+        float4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < kBatch; ++i)
-            if (kb + i < k1) acc += lds_ml[hh][kb + i].x * buf[i];
-    }
-    ma_f32x4* part_acc = reinterpret_cast<ma_f32x4*>(&lds_o[0][0]);   // [parts][slots]
-    if (has_job) part_acc[pidx * nslot + slot] = acc;
-    __syncthreads();
-    if (tid < nslot) {
-        float4v sum = part_acc[tid];
-        for (int pi = 1; pi < parts; ++pi) sum += part_acc[pi * nslot + tid];
-        const float L = lds_L[tid / (D / 4)];
-        const float inv = L > 0.f ? 1.f / L : 0.f;
-        *reinterpret_cast<ma_f32x4*>(a.out + ((size_t)s * a.Hq + kv * grp) * D + tid * 4) = sum * inv;
+            if (k0 + i < k1) acc += e_row[k0 + i] * buf[i];
+        for (int kb = k0 + kBatch; kb < k1; kb += kBatch) {            // long split lists only
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i)
+                buf[i] = __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(
+                    o_rsrc, min(off + (uint32_t)(kb - k0 + i) * stride, last), 0, kSc1));
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i)
+                if (kb + i < k1) acc += e_row[kb + i] * buf[i];
+        }
+        __builtin_amdgcn_wave_barrier();                 // e_row is rewritten for the next head
+#pragma unroll
+        for (int w = 64 / kParts; w < 64; w *= 2)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x = acc[r];
+                acc[r] = x + __shfl_xor(x, w, 64);
+            }
+        if (part == 0) {
+            const float inv = L > 0.f ? 1.f / L : 0.f;
+            *reinterpret_cast<ma_f32x4*>(a.out + ((size_t)s * a.Hq + kv * grp + h2) * D + c4 * 4) = acc * inv;
+        }
     }
     if (tid == 0)
         __hip_atomic_store(&a.counters[group * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
