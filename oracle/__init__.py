@@ -34,7 +34,7 @@ def build(verbose: bool = False) -> str:
 class Geom(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int), ("num_kv_heads", ctypes.c_int),
                 ("head_dim", ctypes.c_int), ("page_size", ctypes.c_int),
-                ("ring_size", ctypes.c_int)]
+                ("ring_size", ctypes.c_int), ("asymmetric", ctypes.c_int)]
 
 
 _lib = None
@@ -63,6 +63,8 @@ def lib():
             "orc_v_code": (i, [P, P, i, i, i]),
             "orc_k_scale": (d, [P, P, i, i]),
             "orc_v_scale": (d, [P, P, i, i]),
+            "orc_k_zero": (d, [P, P, i, i]),
+            "orc_v_zero": (d, [P, P, i, i]),
             "orc_quant_write": (i, [P, P, P, i, P, i, i, P, P, P]),
             "orc_dequant_kv": (i, [P, P, P, i, i, P, P]),
             "orc_decode_attn": (i, [P, P, P, i, P, i, P, f, P]),
@@ -88,8 +90,11 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
-def geom(num_q_heads, num_kv_heads, head_dim, page_size=16, ring_size=64) -> Geom:
-    return Geom(num_q_heads, num_kv_heads, head_dim, page_size, ring_size)
+def geom(num_q_heads, num_kv_heads, head_dim, page_size=16, ring_size=64,
+         asymmetric=False) -> Geom:
+    """asymmetric: the cache's INT tiers hold zero point + scale per group (the asymmetric
+    storage format); the default is the symmetric format"""
+    return Geom(num_q_heads, num_kv_heads, head_dim, page_size, ring_size, int(bool(asymmetric)))
 
 
 class Pools:
@@ -175,6 +180,14 @@ def k_scale(g, sec: np.ndarray, bits, c):
 
 def v_scale(g, sec: np.ndarray, bits, t):
     return lib().orc_v_scale(ctypes.byref(g), _ptr(sec), bits, t)
+
+
+def k_zero(g, sec: np.ndarray, bits, c):
+    return lib().orc_k_zero(ctypes.byref(g), _ptr(sec), bits, c)
+
+
+def v_zero(g, sec: np.ndarray, bits, t):
+    return lib().orc_v_zero(ctypes.byref(g), _ptr(sec), bits, t)
 
 
 # ---- the three path operations ----

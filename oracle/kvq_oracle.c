@@ -129,15 +129,13 @@ void orc_quantize_group_asym(const uint16_t* x, int n, ptrdiff_t stride, int bit
 
 static int field_bit(int k, int bits) { return 16 * (k % 2) + bits * (k / 2); }
 
-void orc_pack(const int* q, int n, int bits, uint8_t* out) {
+/* fields u[i] (already unsigned) into words */
+static void pack_fields(const int* u, int n, int bits, uint8_t* out) {
     const int per_word = 32 / bits;
-    const int offset = 1 << (bits - 1);
     for (int w = 0; w < n / per_word; ++w) {
         uint32_t word = 0;
-        for (int k = 0; k < per_word; ++k) {
-            uint32_t u = (uint32_t)(q[w * per_word + k] + offset);
-            word |= u << field_bit(k, bits);
-        }
+        for (int k = 0; k < per_word; ++k)
+            word |= (uint32_t)u[w * per_word + k] << field_bit(k, bits);
         out[4 * w + 0] = (uint8_t)(word & 0xff);
         out[4 * w + 1] = (uint8_t)((word >> 8) & 0xff);
         out[4 * w + 2] = (uint8_t)((word >> 16) & 0xff);
@@ -145,13 +143,24 @@ void orc_pack(const int* q, int n, int bits, uint8_t* out) {
     }
 }
 
-static int unpack_one(const uint8_t* in, int i, int bits) {
+/* symmetric codes q in [-qmax, qmax] are stored as the fields q + 2^(b-1) */
+void orc_pack(const int* q, int n, int bits, uint8_t* out) {
+    int* u = malloc(sizeof(int) * (size_t)(n > 0 ? n : 1));
+    for (int i = 0; i < n; ++i) u[i] = q[i] + (1 << (bits - 1));
+    pack_fields(u, n, bits, out);
+    free(u);
+}
+
+static int field_of(const uint8_t* in, int i, int bits) {
     const int per_word = 32 / bits;
     const int w = i / per_word, k = i % per_word;
     uint32_t word = (uint32_t)in[4 * w] | ((uint32_t)in[4 * w + 1] << 8) |
                     ((uint32_t)in[4 * w + 2] << 16) | ((uint32_t)in[4 * w + 3] << 24);
-    uint32_t u = (word >> field_bit(k, bits)) & ((1u << bits) - 1u);
-    return (int)u - (1 << (bits - 1));
+    return (int)((word >> field_bit(k, bits)) & ((1u << bits) - 1u));
+}
+
+static int unpack_one(const uint8_t* in, int i, int bits) {
+    return field_of(in, i, bits) - (1 << (bits - 1));
 }
 
 void orc_unpack(const uint8_t* in, int n, int bits, int* q) {
@@ -168,20 +177,30 @@ int orc_bits_of_tier(int tier) {
 static size_t code_bytes(const orc_geom* g, int bits) {
     return (size_t)g->page_size * g->head_dim * bits / 8;
 }
+/* bytes of the per-channel K parameters and of the per-token V parameters of a section: a
+   scale each, and for the asymmetric format a zero point each before the scales */
+static size_t kparam_bytes(const orc_geom* g) { return (g->asymmetric ? 4u : 2u) * (size_t)g->head_dim; }
+static size_t vparam_bytes(const orc_geom* g) { return (g->asymmetric ? 4u : 2u) * (size_t)g->page_size; }
 size_t orc_section_bytes(const orc_geom* g, int bits) {
     if (bits == 16) return 2 * code_bytes(g, bits);       /* FP16 keys and values, no scales */
-    return 2 * code_bytes(g, bits) + 2 * (size_t)g->head_dim + 2 * (size_t)g->page_size;
+    return 2 * code_bytes(g, bits) + kparam_bytes(g) + vparam_bytes(g);
 }
 size_t orc_block_bytes(const orc_geom* g, int bits) {
     return (size_t)g->num_kv_heads * orc_section_bytes(g, bits);
 }
-static size_t off_kscale(const orc_geom* g, int bits) { return code_bytes(g, bits); }
+static size_t off_kzero(const orc_geom* g, int bits) { return code_bytes(g, bits); }  /* asymmetric */
+static size_t off_kscale(const orc_geom* g, int bits) {
+    return code_bytes(g, bits) + (g->asymmetric ? 2 * (size_t)g->head_dim : 0);
+}
 static size_t off_vcodes(const orc_geom* g, int bits) {
     if (bits == 16) return code_bytes(g, bits);
-    return code_bytes(g, bits) + 2 * (size_t)g->head_dim;
+    return code_bytes(g, bits) + kparam_bytes(g);
+}
+static size_t off_vzero(const orc_geom* g, int bits) {                               /* asymmetric */
+    return 2 * code_bytes(g, bits) + kparam_bytes(g);
 }
 static size_t off_vscale(const orc_geom* g, int bits) {
-    return 2 * code_bytes(g, bits) + 2 * (size_t)g->head_dim;
+    return 2 * code_bytes(g, bits) + kparam_bytes(g) + (g->asymmetric ? 2 * (size_t)g->page_size : 0);
 }
 static int k_index(const orc_geom* g, int t, int c) { return t * g->head_dim + c; }
 static int v_index(const orc_geom* g, int t, int c) { return ((t / 4) * g->head_dim + c) * 4 + t % 4; }
@@ -189,11 +208,19 @@ static int v_index(const orc_geom* g, int t, int c) { return ((t / 4) * g->head_
 static uint16_t rd16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
 static void wr16(uint8_t* p, uint16_t v) { p[0] = (uint8_t)(v & 0xff); p[1] = (uint8_t)(v >> 8); }
 
+/* the code of an element: q for the symmetric format, the field u itself for the asymmetric */
 int orc_k_code(const orc_geom* g, const uint8_t* sec, int bits, int t, int c) {
-    return unpack_one(sec, k_index(g, t, c), bits);
+    return g->asymmetric ? field_of(sec, k_index(g, t, c), bits) : unpack_one(sec, k_index(g, t, c), bits);
 }
 int orc_v_code(const orc_geom* g, const uint8_t* sec, int bits, int t, int c) {
-    return unpack_one(sec + off_vcodes(g, bits), v_index(g, t, c), bits);
+    const uint8_t* v = sec + off_vcodes(g, bits);
+    return g->asymmetric ? field_of(v, v_index(g, t, c), bits) : unpack_one(v, v_index(g, t, c), bits);
+}
+double orc_k_zero(const orc_geom* g, const uint8_t* sec, int bits, int c) {
+    return g->asymmetric ? orc_f16_to_f64(rd16(sec + off_kzero(g, bits) + 2 * (size_t)c)) : 0.0;
+}
+double orc_v_zero(const orc_geom* g, const uint8_t* sec, int bits, int t) {
+    return g->asymmetric ? orc_f16_to_f64(rd16(sec + off_vzero(g, bits) + 2 * (size_t)t)) : 0.0;
 }
 double orc_k_scale(const orc_geom* g, const uint8_t* sec, int bits, int c) {
     return orc_f16_to_f64(rd16(sec + off_kscale(g, bits) + 2 * (size_t)c));
@@ -232,7 +259,9 @@ int orc_quant_write(const orc_geom* g, uint8_t* const pools[4], const uint32_t* 
     int* kq = malloc(sizeof(int) * (size_t)P * D);
     int* vq = malloc(sizeof(int) * (size_t)P * D);
     uint16_t* vs = malloc(sizeof(uint16_t) * (size_t)P);
+    uint16_t* vz = malloc(sizeof(uint16_t) * (size_t)P);
     int* codes = malloc(sizeof(int) * (size_t)(P > D ? P : D));
+    const int asym = g->asymmetric != 0;
     for (int s = 0; s < batch && status == 0; ++s) {
         const int p0 = pos[s], end = p0 + n_new;
         const uint16_t* kn = k_new + (size_t)s * n_new * H * D;
@@ -266,34 +295,48 @@ int orc_quant_write(const orc_geom* g, uint8_t* const pools[4], const uint32_t* 
                         keys[(p - lo) * D + c] =
                             p < p0 ? rg[((size_t)(p % R) * H + kv) * D + c]
                                    : kn[((size_t)(p - p0) * H + kv) * D + c];
-                /* K: one scale per channel over the present tokens; zero code elsewhere */
+                /* K: one scale (and, asymmetric, one zero point) per channel over the present
+                   tokens; the zero code elsewhere */
                 for (int i = 0; i < P * D; ++i) kq[i] = 0;
                 for (int c = 0; c < D; ++c) {
-                    uint16_t sc;
-                    orc_quantize_group(keys + c, hi - lo, D, bits, &sc, codes);
+                    uint16_t sc, zp;
+                    if (asym) {
+                        orc_quantize_group_asym(keys + c, hi - lo, D, bits, &sc, &zp, codes);
+                        wr16(sec + off_kzero(g, bits) + 2 * (size_t)c, zp);
+                    } else {
+                        orc_quantize_group(keys + c, hi - lo, D, bits, &sc, codes);
+                    }
                     for (int t = 0; t < hi - lo; ++t) kq[k_index(g, t, c)] = codes[t];
                     wr16(sec + off_kscale(g, bits) + 2 * (size_t)c, sc);
                 }
-                orc_pack(kq, P * D, bits, sec);
-                /* V: tokens cached before keep their codes, new tokens are quantized, empty
-                   slots get the zero code and scale 0 */
+                if (asym) pack_fields(kq, P * D, bits, sec);
+                else orc_pack(kq, P * D, bits, sec);
+                /* V: tokens cached before keep their codes (and scale, zero point), new tokens
+                   are quantized, empty slots get the zero code, scale 0 and zero point 0 */
                 for (int t = 0; t < P; ++t) {
                     const int p = lo + t;
+                    vz[t] = 0;
                     if (p < p0) {
                         for (int c = 0; c < D; ++c)
                             vq[v_index(g, t, c)] = orc_v_code(g, sec, bits, t, c);
                         vs[t] = rd16(sec + off_vscale(g, bits) + 2 * (size_t)t);
+                        if (asym) vz[t] = rd16(sec + off_vzero(g, bits) + 2 * (size_t)t);
                     } else if (p < hi) {
-                        orc_quantize_group(vn + ((size_t)(p - p0) * H + kv) * D, D, 1, bits,
-                                           &vs[t], codes);
+                        const uint16_t* x = vn + ((size_t)(p - p0) * H + kv) * D;
+                        if (asym) orc_quantize_group_asym(x, D, 1, bits, &vs[t], &vz[t], codes);
+                        else orc_quantize_group(x, D, 1, bits, &vs[t], codes);
                         for (int c = 0; c < D; ++c) vq[v_index(g, t, c)] = codes[c];
                     } else {
                         for (int c = 0; c < D; ++c) vq[v_index(g, t, c)] = 0;
                         vs[t] = 0;
                     }
                 }
-                orc_pack(vq, P * D, bits, sec + off_vcodes(g, bits));
-                for (int t = 0; t < P; ++t) wr16(sec + off_vscale(g, bits) + 2 * (size_t)t, vs[t]);
+                if (asym) pack_fields(vq, P * D, bits, sec + off_vcodes(g, bits));
+                else orc_pack(vq, P * D, bits, sec + off_vcodes(g, bits));
+                for (int t = 0; t < P; ++t) {
+                    wr16(sec + off_vscale(g, bits) + 2 * (size_t)t, vs[t]);
+                    if (asym) wr16(sec + off_vzero(g, bits) + 2 * (size_t)t, vz[t]);
+                }
             }
             if (status) break;
         }
@@ -302,12 +345,14 @@ int orc_quant_write(const orc_geom* g, uint8_t* const pools[4], const uint32_t* 
             memcpy(rg + (size_t)(p % R) * H * D, kn + (size_t)(p - p0) * H * D,
                    sizeof(uint16_t) * (size_t)H * D);
     }
-    free(keys); free(kq); free(vq); free(vs); free(codes);
+    free(keys); free(kq); free(vq); free(vs); free(vz); free(codes);
     return status;
 }
 
 /* ------------------------------------------------------------------------------------------ */
-/* Dequantized cache: K^_t[c] = code * s_K(page(t), c),  V^_t[c] = code * s_V(t); exact doubles. */
+/* Dequantized cache: K^_t[c] = code * s_K(page(t), c),  V^_t[c] = code * s_V(t); for the       */
+/* asymmetric format K^_t[c] = z_K(page(t), c) + u * s_K(page(t), c), V^_t[c] = z_V(t) + u * s_V(t). */
+/* Exact doubles.                                                                               */
 
 int orc_dequant_kv(const orc_geom* g, uint8_t* const pools[4], const uint32_t* bt_row, int n,
                    int kv, double* K, double* V) {
@@ -325,10 +370,11 @@ int orc_dequant_kv(const orc_geom* g, uint8_t* const pools[4], const uint32_t* b
             }
             continue;
         }
-        const double sv = orc_v_scale(g, sec, bits, slot);
+        const double sv = orc_v_scale(g, sec, bits, slot), zv = orc_v_zero(g, sec, bits, slot);
         for (int c = 0; c < D; ++c) {
-            K[(size_t)t * D + c] = orc_k_code(g, sec, bits, slot, c) * orc_k_scale(g, sec, bits, c);
-            V[(size_t)t * D + c] = orc_v_code(g, sec, bits, slot, c) * sv;
+            K[(size_t)t * D + c] = orc_k_zero(g, sec, bits, c) +
+                                   orc_k_code(g, sec, bits, slot, c) * orc_k_scale(g, sec, bits, c);
+            V[(size_t)t * D + c] = zv + orc_v_code(g, sec, bits, slot, c) * sv;
         }
     }
     return 0;

@@ -40,6 +40,13 @@
  *   tier 3 <-> b = 16, plain FP16 (EchoKV, "How EchoKV works": a layer's initial state before
  *   the canary first fires): a section is 4*P*D bytes, the keys at index t*D + c then the values
  *   at index ((t/4)*D + c)*4 + t%4, fp16 each, no scales; empty slots are +0.
+ * Asymmetric format (geometry flag `asymmetric`; EchoKV, "Future work": per-token KIVI INT2/4/8
+ *   storage in the paged cache): the same groups (K per page and channel, V per token) with
+ *   the asymmetric quantizer below; a section is S_b = P*D*b/4 + 4*D + 4*P bytes:
+ *     K codes, K zero points (D fp16), K scales (D fp16), V codes, V zero points (P fp16),
+ *     V scales (P fp16);
+ *   the field of a code is the code u in [0, 2^b - 1] itself, and an element is z + u * s.
+ *   Empty token slots carry u = 0 and a zero scale and zero point.
  */
 #ifndef KVQ_ORACLE_H
 #define KVQ_ORACLE_H
@@ -56,6 +63,7 @@ typedef struct {
     int head_dim;      /* D */
     int page_size;     /* P */
     int ring_size;     /* R, a multiple of P */
+    int asymmetric;    /* 0: symmetric codes; 1: the asymmetric format (zero point + scale) */
 } orc_geom;
 
 /* ---- fp16 ---- */
@@ -86,6 +94,8 @@ int    orc_k_code(const orc_geom* g, const uint8_t* sec, int bits, int t, int c)
 int    orc_v_code(const orc_geom* g, const uint8_t* sec, int bits, int t, int c);
 double orc_k_scale(const orc_geom* g, const uint8_t* sec, int bits, int c);
 double orc_v_scale(const orc_geom* g, const uint8_t* sec, int bits, int t);
+double orc_k_zero(const orc_geom* g, const uint8_t* sec, int bits, int c);   /* 0 if symmetric */
+double orc_v_zero(const orc_geom* g, const uint8_t* sec, int bits, int t);   /* 0 if symmetric */
 
 /* ---- quantize-on-write: one layer, `batch` sequences, n_new tokens each ----
  * pools[tier]: host copies of the four tier pools (INT2, INT4, INT8, FP16); bt: [batch][max_pages] handles;
@@ -95,7 +105,8 @@ int orc_quant_write(const orc_geom* g, uint8_t* const pools[4], const uint32_t* 
                     const int32_t* pos, int batch, int n_new,
                     const uint16_t* k_new, const uint16_t* v_new, uint16_t* ring);
 
-/* ---- dequantized cache of one (sequence, kv head): K, V as [n][D] doubles ---- */
+/* ---- dequantized cache of one (sequence, kv head): K, V as [n][D] doubles (for the
+ * asymmetric format, zero point + code * scale) ---- */
 int orc_dequant_kv(const orc_geom* g, uint8_t* const pools[4], const uint32_t* bt_row, int n,
                    int kv, double* K, double* V);
 
