@@ -40,6 +40,15 @@
  *   Quantizer over a group with absolute maximum a: scale s = smallest fp16 >= a/qmax_b
  *   (0 if a == 0), code = round-half-even(x/s); both decided in IEEE binary32, which equals the
  *   exact rational result for fp16 inputs ([Kaizen] "symmetric uniform quantization").
+ * Asymmetric format (kv_geometry.asymmetric = 1; [EchoKV] "Future work": per-token KIVI
+ *   INT2/4/8 storage in the paged cache, with the KIVI-style quantizer of "Show the math"):
+ *   the same groups; a section of S_b = P*D*b/4 + 4*D + 4*P bytes holds K codes, K zero points
+ *   (D fp16), K scales (D fp16), V codes, V zero points (P fp16), V scales (P fp16). A group
+ *   with minimum m and maximum M gets the zero point m (+0 for a zero minimum), the scale
+ *   s = smallest fp16 >= (M - m)/(2^b - 1) (0 if M == m) and codes u = round-half-even((x - m)/s)
+ *   in [0, 2^b - 1], decided in IEEE binary64 (exact for fp16 inputs); the field of a code is u
+ *   itself and an element is m + u*s. Empty token slots carry u = 0, zero point 0, scale 0.
+ *   The FP16 tier and the block handles are the same in both formats.
  */
 #ifndef KV_QUANT_H
 #define KV_QUANT_H
@@ -51,7 +60,7 @@
 extern "C" {
 #endif
 
-#define KV_ABI_VERSION 2
+#define KV_ABI_VERSION 3
 #define KV_NUM_TIERS 4          /* INT2, INT4, INT8, FP16 */
 #define KV_NO_BLOCK 0xFFFFFFFFu
 
@@ -72,6 +81,8 @@ typedef struct {
     int32_t ring_size;          /* R: FP16 key ring per sequence, a multiple of P, P..128 */
     int32_t max_seqs;           /* rows of a block table / ring */
     int32_t max_pages_per_seq;  /* columns of a block table */
+    int32_t asymmetric;         /* 0: symmetric codes (the format above); 1: the asymmetric
+                                   format below, for every INT tier of every layer */
 } kv_geometry;
 
 /* the tier pools of one layer: base[t] holds capacity[t] blocks of kv_block_bytes(g, b_t),

@@ -31,7 +31,7 @@ class KVError(RuntimeError):
 class Geometry(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_layers", "num_q_heads", "num_kv_heads", "head_dim", "page_size", "ring_size",
-        "max_seqs", "max_pages_per_seq")]
+        "max_seqs", "max_pages_per_seq", "asymmetric")]
 
 
 class LayerPools(ctypes.Structure):
@@ -133,9 +133,11 @@ def _stream(stream):
 
 
 def geometry(num_layers, num_q_heads, num_kv_heads, head_dim, max_seqs, max_pages_per_seq,
-             page_size=16, ring_size=64) -> Geometry:
+             page_size=16, ring_size=64, asymmetric=False) -> Geometry:
+    """asymmetric: the INT tiers hold a zero point and a scale per group (the asymmetric
+    storage format of the header); the default is the symmetric format"""
     return Geometry(num_layers, num_q_heads, num_kv_heads, head_dim, page_size, ring_size,
-                    max_seqs, max_pages_per_seq)
+                    max_seqs, max_pages_per_seq, int(bool(asymmetric)))
 
 
 def layer_pools(bases, capacities) -> LayerPools:

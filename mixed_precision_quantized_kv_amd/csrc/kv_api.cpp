@@ -78,6 +78,8 @@ kv_status check_geometry(const kv_geometry* g) {
         return fail(KV_EUNSUPPORTED, "GQA group %d exceeds 16", g->num_q_heads / g->num_kv_heads);
     if ((int64_t)g->max_pages_per_seq * g->page_size > (int64_t)1 << 30)
         return fail(KV_EINVAL, "max_pages_per_seq too large");
+    if (g->asymmetric != 0 && g->asymmetric != 1)
+        return fail(KV_EINVAL, "asymmetric must be 0 or 1, not %d", g->asymmetric);
     return ok();
 }
 
@@ -181,7 +183,7 @@ uint32_t kv_handle(int bits, uint32_t index) {
 
 size_t kv_block_bytes(const kv_geometry* g, int bits) {
     if (check_geometry(g) != KV_OK || tier_of_bits(bits) < 0) return 0;
-    return (size_t)g->num_kv_heads * kvq::section_layout(g->head_dim, bits).bytes;
+    return (size_t)g->num_kv_heads * kvq::section_layout(g->head_dim, bits, g->asymmetric != 0).bytes;
 }
 
 size_t kv_ring_bytes(const kv_geometry* g) {

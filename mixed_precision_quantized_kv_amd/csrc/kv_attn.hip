@@ -89,6 +89,8 @@ struct PageRaw {
     uint32_t v[8];   // this lane's V code chunk (token quad lane/16, channels of lane%16)
     uint32_t ks;     // two K scales (channels 2*lane, 2*lane+1)
     uint32_t vs[2];  // four V scales (tokens 4*(lane/16) .. +3)
+    uint32_t kz;     // asymmetric format: the two K zero points of the same channels
+    uint32_t vz[2];  // asymmetric format: the four V zero points of the same tokens
     int bits;        // 0 = no page
     int ntok;        // valid tokens in the page
 };
@@ -121,7 +123,7 @@ __device__ __forceinline__ const uint8_t* tier_base(const PageSrc& a, int tier) 
 // page's loads while the next pairs' loads stay in flight. `page` must be a valid page index
 // even when `present` is false. An FP16 page (bits 16) is read later, by its own path: here its
 // lane loads use INT2 offsets, which stay inside its (larger) section, and are not used.
-template <int D>
+template <int D, bool ASYM = false>
 __device__ __forceinline__ void load_page(const PageSrc& a, int kv, int page, bool present,
                                           int ctx, int lane, PageRaw& r) {
     const uint32_t handle = ((const_u32_ptr)a.bt_row)[page];
@@ -131,21 +133,27 @@ __device__ __forceinline__ void load_page(const PageSrc& a, int kv, int page, bo
     r.bits = present ? bits : 0;
     r.ntok = present ? min(kPage, ctx - page * kPage) : 0;
     const bool f16 = tier == kFp16Tier;
-    const uint32_t sec_bytes = f16 ? 4u * kPage * D : kPage * D * bits / 4 + 2 * D + 2 * kPage;
+    constexpr uint32_t kpar = (ASYM ? 4 : 2) * D, vpar = (ASYM ? 4 : 2) * kPage;   // group parameters
+    const uint32_t sec_bytes = f16 ? 4u * kPage * D : kPage * D * bits / 4 + kpar + vpar;
     const uint8_t* sec = tier_base(a, tier) + ((size_t)idx * a.H + kv) * sec_bytes;
     const int lb = f16 ? 2 : bits;                  // the layout the lane offsets follow
     const uint32_t code_bytes = kPage * D * lb / 8;
     const int t = lane & 15, G = lane >> 4;
     const int ch = D * lb / 32;                     // bytes of one lane chunk
     const uint8_t* kp = sec + t * (D * lb / 8) + G * ch;
-    const uint8_t* vp = sec + code_bytes + 2 * D + (G * D + t * (D / 16)) * lb / 2;
+    const uint8_t* vp = sec + code_bytes + kpar + (G * D + t * (D / 16)) * lb / 2;
     const int second = lb == 8 ? 16 : 0;
     const uint4 k0 = *reinterpret_cast<const ma_uint4*>(kp);
     const uint4 k1 = *reinterpret_cast<const ma_uint4*>(kp + second);
     const uint4 v0 = *reinterpret_cast<const ma_uint4*>(vp);
     const uint4 v1 = *reinterpret_cast<const ma_uint4*>(vp + second);
-    r.ks = *reinterpret_cast<const ma_u32*>(sec + code_bytes + 4 * (lane & (D / 2 - 1)));
-    const uint2 vs = *reinterpret_cast<const ma_uint2*>(sec + 2 * code_bytes + 2 * D + 8 * G);
+    r.ks = *reinterpret_cast<const ma_u32*>(sec + code_bytes + (kpar - 2 * D) + 4 * (lane & (D / 2 - 1)));
+    const uint2 vs = *reinterpret_cast<const ma_uint2*>(sec + 2 * code_bytes + kpar + (vpar - 2 * kPage) + 8 * G);
+    if constexpr (ASYM) {
+        r.kz = *reinterpret_cast<const ma_u32*>(sec + code_bytes + 4 * (lane & (D / 2 - 1)));
+        const uint2 vz = *reinterpret_cast<const ma_uint2*>(sec + 2 * code_bytes + kpar + 8 * G);
+        r.vz[0] = vz.x; r.vz[1] = vz.y;
+    }
     r.k[0] = k0.x; r.k[1] = k0.y; r.k[2] = k0.z; r.k[3] = k0.w;
     r.k[4] = k1.x; r.k[5] = k1.y; r.k[6] = k1.z; r.k[7] = k1.w;
     r.v[0] = v0.x; r.v[1] = v0.y; r.v[2] = v0.z; r.v[3] = v0.w;
@@ -155,29 +163,30 @@ __device__ __forceinline__ void load_page(const PageSrc& a, int kv, int page, bo
 
 // page pair `pair` of the split [pbeg, pend); pairs past the end reload the last pair (their
 // data is never used) so that every iteration issues the same loads
-template <int D>
+template <int D, bool ASYM>
 __device__ __forceinline__ void load_pair(const PageSrc& a, int kv, int pbeg, int pend,
                                           int pair, int npairs, int ctx, int lane, PageRaw& x,
                                           PageRaw& y) {
     const int pc = min(pair, npairs - 1);
     const int pa = pbeg + 2 * pc;
     const bool has_b = pa + 1 < pend;
-    load_page<D>(a, kv, pa, true, ctx, lane, x);
-    load_page<D>(a, kv, has_b ? pa + 1 : pa, has_b, ctx, lane, y);
+    load_page<D, ASYM>(a, kv, pa, true, ctx, lane, x);
+    load_page<D, ASYM>(a, kv, has_b ? pa + 1 : pa, has_b, ctx, lane, y);
 }
 
 // Loads of one page whose width is known at compile time: exactly the bytes this lane needs
 // (K and V chunks of D*b/32 bytes each, one K-scale dword, one V-scale pair).
-template <int D, int BITS>
+template <int D, int BITS, bool ASYM = false>
 __device__ __forceinline__ void load_page_t(const uint8_t* base, uint32_t idx, int H, int kv,
                                             bool present, int ntok, int lane, PageRaw& r) {
+    constexpr uint32_t kpar = (ASYM ? 4 : 2) * D, vpar = (ASYM ? 4 : 2) * kPage;   // group parameters
     constexpr uint32_t code_bytes = kPage * D * BITS / 8;
-    constexpr uint32_t sec_bytes = 2 * code_bytes + 2 * D + 2 * kPage;
+    constexpr uint32_t sec_bytes = 2 * code_bytes + kpar + vpar;
     constexpr int ch = D * BITS / 32;              // bytes of one lane chunk: 4, 8, 16 or 32
     const uint8_t* sec = base + ((size_t)idx * H + kv) * sec_bytes;
     const int t = lane & 15, G = lane >> 4;
     const uint8_t* kp = sec + t * (D * BITS / 8) + G * ch;
-    const uint8_t* vp = sec + code_bytes + 2 * D + (G * D + t * (D / 16)) * BITS / 2;
+    const uint8_t* vp = sec + code_bytes + kpar + (G * D + t * (D / 16)) * BITS / 2;
     if constexpr (ch == 4) {
         r.k[0] = *reinterpret_cast<const ma_u32*>(kp);
         r.v[0] = *reinterpret_cast<const ma_u32*>(vp);
@@ -195,9 +204,14 @@ __device__ __forceinline__ void load_page_t(const uint8_t* base, uint32_t idx, i
             r.v[4 * h] = v0.x; r.v[4 * h + 1] = v0.y; r.v[4 * h + 2] = v0.z; r.v[4 * h + 3] = v0.w;
         }
     }
-    r.ks = *reinterpret_cast<const ma_u32*>(sec + code_bytes + 4 * (lane & (D / 2 - 1)));
-    const uint2 vs = *reinterpret_cast<const ma_uint2*>(sec + 2 * code_bytes + 2 * D + 8 * G);
+    r.ks = *reinterpret_cast<const ma_u32*>(sec + code_bytes + (kpar - 2 * D) + 4 * (lane & (D / 2 - 1)));
+    const uint2 vs = *reinterpret_cast<const ma_uint2*>(sec + 2 * code_bytes + kpar + (vpar - 2 * kPage) + 8 * G);
     r.vs[0] = vs.x; r.vs[1] = vs.y;
+    if constexpr (ASYM) {
+        r.kz = *reinterpret_cast<const ma_u32*>(sec + code_bytes + 4 * (lane & (D / 2 - 1)));
+        const uint2 vz = *reinterpret_cast<const ma_uint2*>(sec + 2 * code_bytes + kpar + 8 * G);
+        r.vz[0] = vz.x; r.vz[1] = vz.y;
+    }
     r.bits = present ? BITS : 0;
     r.ntok = ntok;
 }
@@ -209,8 +223,8 @@ __device__ __forceinline__ uint32_t hsub(uint32_t u, float bias) {
 
 // K chunk (D*b/32 bytes) -> D/8 dwords of fp16 pairs holding the signed codes, in code order.
 // Bytes of a masked word are spread into fp16 pairs 0x64uu (= 1024 + u) by v_perm_b32, then the
-// offset 1024 + 2^(b-1) is subtracted exactly.
-template <int D>
+// offset 1024 + 2^(b-1) is subtracted exactly (ASYM: 1024, leaving the unsigned code u).
+template <int D, bool ASYM = false>
 __device__ __forceinline__ void unpack_k(const uint32_t* w, int bits, uint32_t* out) {
     const uint32_t hi = 0x64646464u;
     if (bits == 2) {
@@ -219,8 +233,8 @@ __device__ __forceinline__ void unpack_k(const uint32_t* w, int bits, uint32_t* 
 #pragma unroll
             for (int j = 0; j < 4; ++j) {   // codes 2j, 2j+1 (bytes 0, 2) and 2j+8, 2j+9 (1, 3)
                 const uint32_t m = (w[i] >> (2 * j)) & 0x03030303u;
-                out[i * 8 + j] = hsub(__builtin_amdgcn_perm(hi, m, 0x04020400u), 1026.0f);
-                out[i * 8 + 4 + j] = hsub(__builtin_amdgcn_perm(hi, m, 0x04030401u), 1026.0f);
+                out[i * 8 + j] = hsub(__builtin_amdgcn_perm(hi, m, 0x04020400u), ASYM ? 1024.0f : 1026.0f);
+                out[i * 8 + 4 + j] = hsub(__builtin_amdgcn_perm(hi, m, 0x04030401u), ASYM ? 1024.0f : 1026.0f);
             }
     } else if (bits == 4) {
 #pragma unroll
@@ -228,14 +242,14 @@ __device__ __forceinline__ void unpack_k(const uint32_t* w, int bits, uint32_t* 
 #pragma unroll
             for (int j = 0; j < 2; ++j) {   // codes 2j, 2j+1 (bytes 0, 2) and 2j+4, 2j+5 (1, 3)
                 const uint32_t m = (w[i] >> (4 * j)) & 0x0F0F0F0Fu;
-                out[i * 4 + j] = hsub(__builtin_amdgcn_perm(hi, m, 0x04020400u), 1032.0f);
-                out[i * 4 + 2 + j] = hsub(__builtin_amdgcn_perm(hi, m, 0x04030401u), 1032.0f);
+                out[i * 4 + j] = hsub(__builtin_amdgcn_perm(hi, m, 0x04020400u), ASYM ? 1024.0f : 1032.0f);
+                out[i * 4 + 2 + j] = hsub(__builtin_amdgcn_perm(hi, m, 0x04030401u), ASYM ? 1024.0f : 1032.0f);
             }
     } else {
 #pragma unroll
         for (int i = 0; i < D / 16; ++i) {
-            out[2 * i] = hsub(__builtin_amdgcn_perm(hi, w[i], 0x04020400u), 1152.0f);
-            out[2 * i + 1] = hsub(__builtin_amdgcn_perm(hi, w[i], 0x04030401u), 1152.0f);
+            out[2 * i] = hsub(__builtin_amdgcn_perm(hi, w[i], 0x04020400u), ASYM ? 1024.0f : 1152.0f);
+            out[2 * i + 1] = hsub(__builtin_amdgcn_perm(hi, w[i], 0x04030401u), ASYM ? 1024.0f : 1152.0f);
         }
     }
 }
@@ -260,10 +274,48 @@ struct WaveState {
     float4v o[D / 16];   // o^T tile per channel chunk: lane (h, G) element r -> channel G*D/4 + r*D/16 + k
     float m;             // running max (log2 units) of head lane%16
     float l;             // this lane's share of the running sum of p
+    float z;             // asymmetric format: this lane's share of the sum of p * (V zero point)
 };
 
-// QK for one page: S^T for tokens 4G..4G+3 of head lane%16, in log2 units, masked
+// the D/4 K parameters (scales or zero points) of this lane's channel quarter, staged in LDS
+// one dword a lane (lane i: channels 2i, 2i+1)
 template <int D>
+__device__ __forceinline__ void read_quarter(const uint32_t* lds, int G, uint32_t* out) {
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+        const uint4 v = *reinterpret_cast<const ma_uint4*>(lds + G * (D / 8) + 4 * i);
+        out[4 * i] = v.x; out[4 * i + 1] = v.y; out[4 * i + 2] = v.z; out[4 * i + 3] = v.w;
+    }
+}
+
+// asymmetric format: the zero-point part of the logits, sum_c z_c q_c for every token row of the
+// tile (the zero points stand in every row of the A operand; fp16 times fp16 is exact in fp32)
+template <int D>
+__device__ __forceinline__ float4v zero_point_logits(const uint32_t* kz, const uint32_t* qf) {
+    float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            make_half8(kz[4 * i], kz[4 * i + 1], kz[4 * i + 2], kz[4 * i + 3]),
+            make_half8(qf[4 * i], qf[4 * i + 1], qf[4 * i + 2], qf[4 * i + 3]), acc, 0, 0, 0);
+    return acc;
+}
+
+// asymmetric format: p_i * (V zero point of token 4G+i) summed over this lane's four tokens
+__device__ __forceinline__ float zero_point_mass(const float* p, uint32_t vz0, uint32_t vz1, int ntok, int G) {
+    const half2v z01 = __builtin_bit_cast(half2v, vz0);
+    const half2v z23 = __builtin_bit_cast(half2v, vz1);
+    const float z[4] = {(float)z01[0], (float)z01[1], (float)z23[0], (float)z23[1]};
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (4 * G + i < ntok) acc += p[i] * z[i];
+    return acc;
+}
+
+// QK for one page: S^T for tokens 4G..4G+3 of head lane%16, in log2 units, masked. ASYM: the
+// logit of an element m + u*s is the zero-point part plus the code part.
+template <int D, bool ASYM = false>
 __device__ __forceinline__ float4v page_logits(const PageRaw& r, int bits, const uint32_t* qf,
                                                uint32_t* lds_ks, int lane, float scale_log2) {
     const int G = lane >> 4;
@@ -271,17 +323,19 @@ __device__ __forceinline__ float4v page_logits(const PageRaw& r, int bits, const
     // (one wave writes and reads its own slot; LDS serves a wave's requests in order, and the
     // wave barrier keeps the compiler from hoisting the reads above the write)
     lds_ks[lane] = r.ks;
+    if constexpr (ASYM) lds_ks[128 + lane] = r.kz;
     __builtin_amdgcn_wave_barrier();
     uint32_t ks[D / 8];
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-        const uint4 v = *reinterpret_cast<const ma_uint4*>(lds_ks + G * (D / 8) + 4 * i);
-        ks[4 * i] = v.x; ks[4 * i + 1] = v.y; ks[4 * i + 2] = v.z; ks[4 * i + 3] = v.w;
-    }
+    read_quarter<D>(lds_ks, G, ks);
     uint32_t kf[D / 8];
-    unpack_k<D>(r.k, bits, kf);
+    unpack_k<D, ASYM>(r.k, bits, kf);
     float4v acc = {0.f, 0.f, 0.f, 0.f};
-    if (bits == 2) {
+    if constexpr (ASYM) {
+        uint32_t kz[D / 8];
+        read_quarter<D>(lds_ks + 128, G, kz);
+        acc = zero_point_logits<D>(kz, qf);
+    }
+    if (!ASYM && bits == 2) {
         // INT2 codes are -1, 0, 1: code * scale is exact in fp16, so the scales fold into the
         // keys and every MFMA product is exact
 #pragma unroll
@@ -349,16 +403,16 @@ __device__ __forceinline__ void page_weights(uint32_t vs0, uint32_t vs1, int nto
 
 // One page pair: QK, online softmax and PV. BITS is the width of both pages when the caller
 // knows it at compile time, 0 when each page carries its own; page B may be absent (bits 0).
-template <int D, int BITS>
+template <int D, int BITS, bool ASYM = false>
 __device__ __forceinline__ void process_pair(const PageRaw& A, const PageRaw& B, const uint32_t* qf,
                                              uint32_t* lds_ks, int lane, float scale_log2,
                                              WaveState<D>& st) {
     const int G = lane >> 4;
     const int bits_a = BITS ? BITS : A.bits;
     const int bits_b = BITS ? BITS : B.bits;
-    const float4v la = page_logits<D>(A, bits_a, qf, lds_ks, lane, scale_log2);
+    const float4v la = page_logits<D, ASYM>(A, bits_a, qf, lds_ks, lane, scale_log2);
     float4v lb = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    if (B.bits) lb = page_logits<D>(B, bits_b, qf, lds_ks + 64, lane, scale_log2);
+    if (B.bits) lb = page_logits<D, ASYM>(B, bits_b, qf, lds_ks + 64, lane, scale_log2);
 
     // online softmax over the pair's 32 tokens, per head (lanes h, h+16, h+32, h+48)
     float mx = fmaxf(fmaxf(fmaxf(la[0], la[1]), fmaxf(la[2], la[3])),
@@ -368,6 +422,7 @@ __device__ __forceinline__ void process_pair(const PageRaw& A, const PageRaw& B,
     if (__builtin_amdgcn_ballot_w64(m_new != st.m)) {
         const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);   // 0 on the first pair
         st.l *= alpha;
+        if constexpr (ASYM) st.z *= alpha;
 #pragma unroll
         for (int k = 0; k < D / 16; ++k) st.o[k] *= alpha;
         st.m = m_new;
@@ -379,6 +434,10 @@ __device__ __forceinline__ void process_pair(const PageRaw& A, const PageRaw& B,
         pb[i] = __builtin_amdgcn_exp2f(lb[i] - m_new);
     }
     st.l += ((pa[0] + pa[1]) + (pa[2] + pa[3])) + ((pb[0] + pb[1]) + (pb[2] + pb[3]));
+    if constexpr (ASYM) {
+        st.z += zero_point_mass(pa, A.vz[0], A.vz[1], A.ntok, G);
+        if (B.bits) st.z += zero_point_mass(pb, B.vz[0], B.vz[1], B.ntok, G);
+    }
 
     uint32_t wh[4], wl[4];
     page_weights(A.vs[0], A.vs[1], A.ntok, pa, G, wh, wl);
@@ -391,9 +450,9 @@ __device__ __forceinline__ void process_pair(const PageRaw& A, const PageRaw& B,
     const half8 pl = make_half8(wl[0], wl[1], wl[2], wl[3]);
 
     uint32_t va[D / 8], vb[D / 8];
-    unpack_k<D>(A.v, bits_a, va);
+    unpack_k<D, ASYM>(A.v, bits_a, va);
     if (B.bits) {
-        unpack_k<D>(B.v, bits_b, vb);
+        unpack_k<D, ASYM>(B.v, bits_b, vb);
     } else {
 #pragma unroll
         for (int i = 0; i < D / 8; ++i) vb[i] = 0u;
@@ -413,7 +472,7 @@ __device__ __forceinline__ void process_pair(const PageRaw& A, const PageRaw& B,
 // h - 8. The scaled query q * Kscale is then computed once for both pages (each lane with its
 // own page's scales), each lane keeps four logits and four weights instead of eight, and the PV
 // product accumulates page B's share in columns 8..15, folded into 0..7 at the end.
-template <int D, int BITS>
+template <int D, int BITS, bool ASYM = false>
 __device__ __forceinline__ void process_pair_half(const PageRaw& A, const PageRaw& B,
                                                   const uint32_t* qf, uint32_t* lds_ks, int lane,
                                                   float scale_log2, WaveState<D>& st) {
@@ -425,9 +484,13 @@ __device__ __forceinline__ void process_pair_half(const PageRaw& A, const PageRa
     const int ntok = side ? B.ntok : A.ntok;
     lds_ks[lane] = A.ks;
     lds_ks[64 + lane] = B.ks;
+    if constexpr (ASYM) {
+        lds_ks[128 + lane] = A.kz;
+        lds_ks[192 + lane] = B.kz;
+    }
     __builtin_amdgcn_wave_barrier();
     float4v acc;
-    if (bits_a == 2 && bits_b == 2) {
+    if (!ASYM && bits_a == 2 && bits_b == 2) {
         // INT2: the scales fold exactly into each page's keys, q is used as is
         uint32_t ksa[D / 8], ksb[D / 8];
 #pragma unroll
@@ -477,9 +540,18 @@ __device__ __forceinline__ void process_pair_half(const PageRaw& A, const PageRa
             ql[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q2, s2, -hi));
         }
         uint32_t kfa[D / 8], kfb[D / 8];
-        unpack_k<D>(A.k, bits_a, kfa);
-        if (has_b) unpack_k<D>(B.k, bits_b, kfb);
+        unpack_k<D, ASYM>(A.k, bits_a, kfa);
+        if (has_b) unpack_k<D, ASYM>(B.k, bits_b, kfb);
         float4v acca = {0.f, 0.f, 0.f, 0.f}, accb = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (ASYM) {                     // the zero-point parts, page by page
+            uint32_t kz[D / 8];
+            read_quarter<D>(lds_ks + 128, G, kz);
+            acca = zero_point_logits<D>(kz, qf);
+            if (has_b) {
+                read_quarter<D>(lds_ks + 192, G, kz);
+                accb = zero_point_logits<D>(kz, qf);
+            }
+        }
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) {
             const half8 hq = make_half8(qh[4 * i], qh[4 * i + 1], qh[4 * i + 2], qh[4 * i + 3]);
@@ -510,6 +582,7 @@ __device__ __forceinline__ void process_pair_half(const PageRaw& A, const PageRa
     if (__builtin_amdgcn_ballot_w64(m_new != st.m)) {
         const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);   // 0 on the first pair
         st.l *= alpha;
+        if constexpr (ASYM) st.z *= alpha;
 #pragma unroll
         for (int k = 0; k < D / 16; ++k) st.o[k] *= alpha;
         st.m = m_new;
@@ -518,6 +591,8 @@ __device__ __forceinline__ void process_pair_half(const PageRaw& A, const PageRa
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(lg[i] - m_new);
     st.l += (p[0] + p[1]) + (p[2] + p[3]);
+    if constexpr (ASYM)
+        st.z += zero_point_mass(p, side ? B.vz[0] : A.vz[0], side ? B.vz[1] : A.vz[1], ntok, G);
 
     uint32_t wh[2], wl[2];
     page_weights(side ? B.vs[0] : A.vs[0], side ? B.vs[1] : A.vs[1], ntok, p, G, wh, wl);
@@ -526,9 +601,9 @@ __device__ __forceinline__ void process_pair_half(const PageRaw& A, const PageRa
     const half8 pl = make_half8(side ? z : wl[0], side ? z : wl[1], side ? wl[0] : z, side ? wl[1] : z);
 
     uint32_t va[D / 8], vb[D / 8];
-    unpack_k<D>(A.v, bits_a, va);
+    unpack_k<D, ASYM>(A.v, bits_a, va);
     if (has_b) {
-        unpack_k<D>(B.v, bits_b, vb);
+        unpack_k<D, ASYM>(B.v, bits_b, vb);
     } else {
 #pragma unroll
         for (int i = 0; i < D / 8; ++i) vb[i] = 0u;
@@ -542,14 +617,14 @@ __device__ __forceinline__ void process_pair_half(const PageRaw& A, const PageRa
 }
 
 // one pair through the layout the kernel was instantiated for
-template <int D, int BITS, bool HALF>
+template <int D, int BITS, bool HALF, bool ASYM = false>
 __device__ __forceinline__ void run_pair(const PageRaw& A, const PageRaw& B, const uint32_t* qf,
                                          uint32_t* lds_ks, int lane, float scale_log2,
                                          WaveState<D>& st) {
     if constexpr (HALF)
-        process_pair_half<D, BITS>(A, B, qf, lds_ks, lane, scale_log2, st);
+        process_pair_half<D, BITS, ASYM>(A, B, qf, lds_ks, lane, scale_log2, st);
     else
-        process_pair<D, BITS>(A, B, qf, lds_ks, lane, scale_log2, st);
+        process_pair<D, BITS, ASYM>(A, B, qf, lds_ks, lane, scale_log2, st);
 }
 
 
@@ -691,13 +766,13 @@ __device__ __forceinline__ void wave_chunk_f16(const uint8_t* base, uint32_t hv,
 
 // one pair of the general loop: pairs with an FP16 page go page by page, each FP16 page read
 // here from its section (its PageRaw holds only its width and token count)
-template <int D, bool HALF>
+template <int D, bool HALF, bool ASYM>
 __device__ __forceinline__ void run_pair_any(const PageSrc& src, int kv, int page, const PageRaw& A,
                                              const PageRaw& B, const uint32_t* qf,
                                              uint32_t* lds_ks, int lane, float scale_log2,
                                              WaveState<D>& st) {
     if (A.bits != 16 && B.bits != 16) {
-        run_pair<D, 0, HALF>(A, B, qf, lds_ks, lane, scale_log2, st);
+        run_pair<D, 0, HALF, ASYM>(A, B, qf, lds_ks, lane, scale_log2, st);
         return;
     }
     PageRaw none = A;
@@ -713,12 +788,12 @@ __device__ __forceinline__ void run_pair_any(const PageSrc& src, int kv, int pag
             load_page_f16<D>(sec, lane, F);
             process_pair_f16<D, HALF>(F, F, false, X.ntok, 0, qf, lane, scale_log2, st);
         } else if (X.bits) {
-            run_pair<D, 0, HALF>(X, none, qf, lds_ks, lane, scale_log2, st);
+            run_pair<D, 0, HALF, ASYM>(X, none, qf, lds_ks, lane, scale_log2, st);
         }
     }
 }
 
-template <int D, int BITS>
+template <int D, int BITS, bool ASYM>
 __device__ __forceinline__ void load_pair_t(const uint8_t* base, uint32_t hv, int H, int kv, int cb,
                                             int npg, int q, int nq, int ctx, int lane, PageRaw& x,
                                             PageRaw& y) {
@@ -727,15 +802,15 @@ __device__ __forceinline__ void load_pair_t(const uint8_t* base, uint32_t hv, in
     const uint32_t ia = (uint32_t)__builtin_amdgcn_readlane((int)hv, pa) & 0x3fffffffu;
     const uint32_t ib = (uint32_t)__builtin_amdgcn_readlane((int)hv, has_b ? pa + 1 : pa) & 0x3fffffffu;
     const int page = cb + pa;
-    load_page_t<D, BITS>(base, ia, H, kv, true, min(kPage, ctx - page * kPage), lane, x);
-    load_page_t<D, BITS>(base, ib, H, kv, has_b, has_b ? min(kPage, ctx - (page + 1) * kPage) : 0,
-                         lane, y);
+    load_page_t<D, BITS, ASYM>(base, ia, H, kv, true, min(kPage, ctx - page * kPage), lane, x);
+    load_page_t<D, BITS, ASYM>(base, ib, H, kv, has_b, has_b ? min(kPage, ctx - (page + 1) * kPage) : 0,
+                               lane, y);
 }
 
 // A wave's chunk of pages, all of one width, with DEPTH page pairs in flight: while pair q is
 // processed, pairs q+1 .. q+DEPTH-1 are loading. The rotation over the DEPTH buffers is unrolled,
 // so every buffer index is a constant. No per-page branching and no block-table reads in the loop.
-template <int D, int BITS, int DEPTH, bool HALF>
+template <int D, int BITS, int DEPTH, bool HALF, bool ASYM = false>
 __device__ __forceinline__ void wave_chunk_uniform(const uint8_t* base, uint32_t hv, int H, int kv,
                                                    int cb, int npg, int ctx, int lane,
                                                    const uint32_t* qf, uint32_t* ks_slot,
@@ -744,7 +819,7 @@ __device__ __forceinline__ void wave_chunk_uniform(const uint8_t* base, uint32_t
     PageRaw buf[DEPTH][2];
 #pragma unroll
     for (int d = 0; d < DEPTH - 1; ++d)
-        load_pair_t<D, BITS>(base, hv, H, kv, cb, npg, d, nq, ctx, lane, buf[d][0], buf[d][1]);
+        load_pair_t<D, BITS, ASYM>(base, hv, H, kv, cb, npg, d, nq, ctx, lane, buf[d][0], buf[d][1]);
     // whole rotations in a loop with one exit and unconditional loads (see wave_chunk_fast),
     // then the last nq % DEPTH pairs, already loaded
     const int nfull = nq / DEPTH;
@@ -752,37 +827,37 @@ __device__ __forceinline__ void wave_chunk_uniform(const uint8_t* base, uint32_t
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
             const int nxt = (d + DEPTH - 1) % DEPTH;
-            load_pair_t<D, BITS>(base, hv, H, kv, cb, npg, r + d + DEPTH - 1, nq, ctx, lane,
-                                 buf[nxt][0], buf[nxt][1]);
-            run_pair<D, BITS, HALF>(buf[d][0], buf[d][1], qf, ks_slot, lane, scale_log2, st);
+            load_pair_t<D, BITS, ASYM>(base, hv, H, kv, cb, npg, r + d + DEPTH - 1, nq, ctx, lane,
+                                       buf[nxt][0], buf[nxt][1]);
+            run_pair<D, BITS, HALF, ASYM>(buf[d][0], buf[d][1], qf, ks_slot, lane, scale_log2, st);
         }
     }
 #pragma unroll
     for (int d = 0; d < DEPTH - 1; ++d)
         if (d < nq - nfull * DEPTH)
-            run_pair<D, BITS, HALF>(buf[d][0], buf[d][1], qf, ks_slot, lane, scale_log2, st);
+            run_pair<D, BITS, HALF, ASYM>(buf[d][0], buf[d][1], qf, ks_slot, lane, scale_log2, st);
 }
 
 // The same for a chunk whose pages may differ in width: handles from the block table, the
 // width-independent loads of load_page and per-page width branches.
-template <int D, bool HALF>
+template <int D, bool HALF, bool ASYM = false>
 __device__ __forceinline__ void wave_chunk_mixed(const PageSrc& src, int kv, int cb, int npg,
                                                  int ctx, int lane, const uint32_t* qf,
                                                  uint32_t* ks_slot, float scale_log2,
                                                  WaveState<D>& st) {
     const int nq = (npg + 1) / 2;
     PageRaw a0, a1, b0, b1;
-    load_pair<D>(src, kv, cb, cb + npg, 0, nq, ctx, lane, a0, a1);
+    load_pair<D, ASYM>(src, kv, cb, cb + npg, 0, nq, ctx, lane, a0, a1);
     // two pairs per trip, one exit, unconditional loads (see wave_chunk_fast); an odd last
     // pair is already in a0, a1
     for (int q = 0; q + 1 < nq; q += 2) {
-        load_pair<D>(src, kv, cb, cb + npg, q + 1, nq, ctx, lane, b0, b1);
-        run_pair_any<D, HALF>(src, kv, cb + 2 * q, a0, a1, qf, ks_slot, lane, scale_log2, st);
-        load_pair<D>(src, kv, cb, cb + npg, q + 2, nq, ctx, lane, a0, a1);
-        run_pair_any<D, HALF>(src, kv, cb + 2 * (q + 1), b0, b1, qf, ks_slot, lane, scale_log2, st);
+        load_pair<D, ASYM>(src, kv, cb, cb + npg, q + 1, nq, ctx, lane, b0, b1);
+        run_pair_any<D, HALF, ASYM>(src, kv, cb + 2 * q, a0, a1, qf, ks_slot, lane, scale_log2, st);
+        load_pair<D, ASYM>(src, kv, cb, cb + npg, q + 2, nq, ctx, lane, a0, a1);
+        run_pair_any<D, HALF, ASYM>(src, kv, cb + 2 * (q + 1), b0, b1, qf, ks_slot, lane, scale_log2, st);
     }
     if (nq & 1)
-        run_pair_any<D, HALF>(src, kv, cb + 2 * (nq - 1), a0, a1, qf, ks_slot, lane, scale_log2, st);
+        run_pair_any<D, HALF, ASYM>(src, kv, cb + 2 * (nq - 1), a0, a1, qf, ks_slot, lane, scale_log2, st);
 }
 
 // ---------------------------------------------------------------- uniform-width fast path
@@ -1185,7 +1260,7 @@ __device__ __forceinline__ void wave_chunk_fast(const uint8_t* base, uint32_t hv
 // whose split holds a touched page quantizes it (256 threads a page, two pages at a time) and,
 // for the first page, updates the ring, then makes its writes visible to its own loads and
 // attends over pos + n_new tokens. No other workgroup reads those pages, so one launch does both steps.
-template <int D, bool HALF, bool FUSED>
+template <int D, bool HALF, bool FUSED, bool ASYM>
 // The block table, the lengths (ctx_len, or pos for the fused step), q and the shape integers
 // that address them come first as plain arguments: the build preloads the first twelve
 // kernel-argument dwords into SGPRs at wave launch, so the first loads need not wait for the
@@ -1196,7 +1271,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
                                                                   int groups, int H, int max_pages,
                                                                   int pps, int Hq, int grp,
                                                                   AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint32_t lds_ks[kWaves][2][64];
+    // the K scales of a pair's pages (ASYM: then their zero points), staged per wave
+    __shared__ __attribute__((aligned(16))) uint32_t lds_ks[kWaves][ASYM ? 4 : 2][64];
     // the K scales of the uniform-width loop's page pairs, staged per wave (stage_kscale)
     __shared__ __attribute__((aligned(16))) uint32_t lds_ksr[kWaves][2 * kKsSlot<D>];
     // per-wave partials, one padded row per head: channel c of head h sits at h*kORow + c +
@@ -1246,7 +1322,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
     const int pend = min(pbeg + a.pps, npages);
 
     if constexpr (FUSED) {
-        __shared__ float chan_max[2][4][D];
+        __shared__ float chan_max[2][ASYM ? 8 : 4][D];
         const int p0 = ctx - a.n_new;
         const int first_page = p0 / kPage, last_page = (ctx - 1) / kPage;
         // the touched pages this split holds, two at a time (256 threads a page)
@@ -1254,8 +1330,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
         if (a.n_new > 0 && lo_page <= hi_page) {         // uniform over the workgroup
             const int half = tid >> 8;                   // threads 0..255: even page, 256..511: odd
             for (int pg = lo_page; pg <= hi_page; pg += 2) {
-                write_page<D>(a.wr, s, kv, p0, pg + half - first_page, tid & 255,
-                              pg + half <= hi_page, chan_max[half]);
+                write_page<D, ASYM>(a.wr, s, kv, p0, pg + half - first_page, tid & 255,
+                                    pg + half <= hi_page, chan_max[half]);
                 __syncthreads();                         // chan_max is reused; ring reads done
             }
             if (lo_page == first_page)                   // the first page's split: the ring
@@ -1272,6 +1348,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
     WaveState<D> st;
     st.m = -INFINITY;
     st.l = 0.f;
+    st.z = 0.f;
 #pragma unroll
     for (int k = 0; k < D / 16; ++k) st.o[k] = float4v{0.f, 0.f, 0.f, 0.f};
 
@@ -1294,23 +1371,24 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
             uniform = __builtin_amdgcn_ballot_w64((int)(hv >> 30) != tier0) == 0;
         }
         uint32_t* ks_round = &lds_ksr[wave][0];
-        if (HALF && uniform && tier0 == 0)
+        // the asymmetric format takes the general loops (constexpr: no fast path is compiled)
+        if (!ASYM && HALF && uniform && tier0 == 0)
             wave_chunk_fast<D, 2, kDepth2>(a.pools.base[0], hv, a.H, kv, cb, npg, ctx, lane, qf,
                                            ks_round, a.scale_log2, st);
-        else if (HALF && uniform && tier0 == 1)
+        else if (!ASYM && HALF && uniform && tier0 == 1)
             wave_chunk_fast<D, 4, kDepth4>(a.pools.base[1], hv, a.H, kv, cb, npg, ctx, lane, qf,
                                            ks_round, a.scale_log2, st);
-        else if (HALF && uniform && tier0 == 2)
+        else if (!ASYM && HALF && uniform && tier0 == 2)
             wave_chunk_fast<D, 8, kDepth8>(a.pools.base[2], hv, a.H, kv, cb, npg, ctx, lane, qf,
                                            ks_round, a.scale_log2, st);
         else if (uniform && tier0 == 0)
-            wave_chunk_uniform<D, 2, 2, HALF>(a.pools.base[0], hv, a.H, kv, cb, npg, ctx, lane, qf, ks_slot,
+            wave_chunk_uniform<D, 2, 2, HALF, ASYM>(a.pools.base[0], hv, a.H, kv, cb, npg, ctx, lane, qf, ks_slot,
                                      a.scale_log2, st);
         else if (uniform && tier0 == 1)
-            wave_chunk_uniform<D, 4, 2, HALF>(a.pools.base[1], hv, a.H, kv, cb, npg, ctx, lane, qf, ks_slot,
+            wave_chunk_uniform<D, 4, 2, HALF, ASYM>(a.pools.base[1], hv, a.H, kv, cb, npg, ctx, lane, qf, ks_slot,
                                      a.scale_log2, st);
         else if (uniform && tier0 == 2)
-            wave_chunk_uniform<D, 8, 2, HALF>(a.pools.base[2], hv, a.H, kv, cb, npg, ctx, lane, qf, ks_slot,
+            wave_chunk_uniform<D, 8, 2, HALF, ASYM>(a.pools.base[2], hv, a.H, kv, cb, npg, ctx, lane, qf, ks_slot,
                                      a.scale_log2, st);
         else if (uniform && tier0 == kFp16Tier)
             wave_chunk_f16<D, HALF>(a.pools.base[3], hv, a.H, kv, cb, npg, ctx, lane, qf,
@@ -1318,7 +1396,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
         else {
             const PageSrc src = {a.pools.base[0], a.pools.base[1], a.pools.base[2],
                                  a.pools.base[3], bt_row, a.H};
-            wave_chunk_mixed<D, HALF>(src, kv, cb, npg, ctx, lane, qf, ks_slot, a.scale_log2, st);
+            wave_chunk_mixed<D, HALF, ASYM>(src, kv, cb, npg, ctx, lane, qf, ks_slot, a.scale_log2, st);
         }
     }
 
@@ -1337,6 +1415,15 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
             }
     }
     lsum = rows_sum(lsum);
+    if constexpr (ASYM) {
+        // the zero-point part of the values, sum_t p_t m_t, is the same for every channel of a
+        // head: folded and summed like l, then added to the head's accumulators
+        float zsum = st.z;
+        if constexpr (HALF) zsum += __builtin_bit_cast(float, dpp_ror8(__builtin_bit_cast(uint32_t, zsum)));
+        zsum = rows_sum(zsum);
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k) st.o[k] += zsum;
+    }
     if (h < grp) {
         if (G == 0) {
             lds_m[wave][h] = st.m;
@@ -1526,20 +1613,29 @@ AttnArgs attn_args(const kv_geometry& g, PoolPtrs pools, const uint32_t* bt, int
     return a;
 }
 
+template <int D, bool HALF, bool FUSED, bool ASYM>
+void launch_one(const AttnArgs& a, dim3 grid, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_attn_kernel<D, HALF, FUSED, ASYM>), grid, dim3(kWaves * 64), 0, stream,
+                       a.bt, FUSED ? a.pos : a.ctx_len, a.q, a.groups, a.H, a.max_pages, a.pps, a.Hq,
+                       a.grp, a);
+}
+
+template <int D, bool FUSED, bool ASYM>
+void launch_d(const AttnArgs& a, dim3 grid, hipStream_t stream) {
+    if (a.grp <= 8) launch_one<D, true, FUSED, ASYM>(a, grid, stream);
+    else launch_one<D, false, FUSED, ASYM>(a, grid, stream);
+}
+
 template <bool FUSED>
 hipError_t launch(const kv_geometry& g, const AttnArgs& a, int splits, hipStream_t stream) {
-    dim3 grid((unsigned)(splits * a.groups));
-    const bool half = a.grp <= 8;
+    const dim3 grid((unsigned)(splits * a.groups));
+    const bool asym = g.asymmetric != 0;
     if (g.head_dim == 128) {
-        if (half) hipLaunchKernelGGL((decode_attn_kernel<128, true, FUSED>), grid, dim3(kWaves * 64), 0, stream, a.bt,
-                           FUSED ? a.pos : a.ctx_len, a.q, a.groups, a.H, a.max_pages, a.pps, a.Hq, a.grp, a);
-        else hipLaunchKernelGGL((decode_attn_kernel<128, false, FUSED>), grid, dim3(kWaves * 64), 0, stream, a.bt,
-                           FUSED ? a.pos : a.ctx_len, a.q, a.groups, a.H, a.max_pages, a.pps, a.Hq, a.grp, a);
+        if (asym) launch_d<128, FUSED, true>(a, grid, stream);
+        else launch_d<128, FUSED, false>(a, grid, stream);
     } else {
-        if (half) hipLaunchKernelGGL((decode_attn_kernel<64, true, FUSED>), grid, dim3(kWaves * 64), 0, stream, a.bt,
-                           FUSED ? a.pos : a.ctx_len, a.q, a.groups, a.H, a.max_pages, a.pps, a.Hq, a.grp, a);
-        else hipLaunchKernelGGL((decode_attn_kernel<64, false, FUSED>), grid, dim3(kWaves * 64), 0, stream, a.bt,
-                           FUSED ? a.pos : a.ctx_len, a.q, a.groups, a.H, a.max_pages, a.pps, a.Hq, a.grp, a);
+        if (asym) launch_d<64, FUSED, true>(a, grid, stream);
+        else launch_d<64, FUSED, false>(a, grid, stream);
     }
     return hipGetLastError();
 }

@@ -73,17 +73,6 @@ __device__ __forceinline__ void group_logits(const float* qs, const float* keys,
     }
 }
 
-// smallest fp16 >= x for finite x > 0 given in binary64: a nearby fp16 value, then one step
-// toward x's side (the double-to-single-to-half rounding lands at most one step away)
-__device__ inline uint16_t f64_to_f16_up(double x) {
-    uint16_t b = f16_bits((_Float16)(float)x);
-    if ((double)f16_val(b) < x)
-        b = (uint16_t)(b + 1);
-    else if (b > 0 && (double)f16_val((uint16_t)(b - 1)) >= x)
-        b = (uint16_t)(b - 1);
-    return b;
-}
-
 template <int D, bool ASYM, int NL>
 __global__ __launch_bounds__(kThreads) void canary_kernel(CanaryArgs<NL> a) {
     extern __shared__ float smem[];
@@ -161,9 +150,7 @@ __global__ __launch_bounds__(kThreads) void canary_kernel(CanaryArgs<NL> a) {
                 mn = fminf(mn, kref[k * (D + 1) + c]);
                 mx = fmaxf(mx, kref[k * (D + 1) + c]);
             }
-            const double range = (double)mx - (double)mn;      // exact for fp16 inputs
-            sc[pg * D + c] =
-                range > 0.0 ? f16_val(f64_to_f16_up(range / (double)((1 << bits) - 1))) : 0.f;
+            sc[pg * D + c] = f16_val(asym_scale(mn, mx, bits));
             zp[pg * D + c] = mn;
         } else {
             float amax = 0.f;

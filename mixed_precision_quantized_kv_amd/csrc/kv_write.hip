@@ -11,7 +11,8 @@
 // memory once. Channel maxima over the
 // page's tokens reduce across the four token lanes of a wave (shuffles) and the four waves
 // (LDS); token maxima over D reduce across the 16 lanes of a token (shuffles). Codes are packed
-// in registers; words shared by several threads are OR-reduced with shuffles.
+// in registers; words shared by several threads are OR-reduced with shuffles. A geometry with the
+// asymmetric format gives each group a zero point and a scale from its minimum and maximum.
 //
 // The workgroup of the first page touched is the only reader of the ring (the page's earlier
 // keys live there), so it also performs the ring update, after a barrier.
@@ -24,12 +25,12 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <int D>
+template <int D, bool ASYM>
 __global__ __launch_bounds__(kThreads) void quant_write_kernel(WriteArgs a) {
-    __shared__ float chan_max[4][D];            // per-wave channel maxima of |K|
+    __shared__ float chan_red[ASYM ? 8 : 4][D];   // per-wave channel maxima of |K| (ASYM: of K, then minima)
     const int j = blockIdx.x, kv = blockIdx.y, s = blockIdx.z;
     const int p0 = a.pos[s];
-    write_page<D>(a, s, kv, p0, j, threadIdx.x, true, chan_max);
+    write_page<D, ASYM>(a, s, kv, p0, j, threadIdx.x, true, chan_red);
     if (j == 0 && p0 / kPage * kPage < p0 + a.n_new) {   // the first page's workgroup
         __syncthreads();                                  // its ring reads are done
         write_ring<D>(a, s, kv, p0, threadIdx.x, kThreads);
@@ -54,10 +55,14 @@ hipError_t launch_quant_write(const kv_geometry& g, PoolPtrs pools, const uint32
     a.R = g.ring_size;
     // pages touched per sequence: at most ceil(n_new / P) + 1 (the first may be partial)
     dim3 grid((unsigned)((n_new + kPage - 1) / kPage + 1), (unsigned)g.num_kv_heads, (unsigned)batch);
-    if (g.head_dim == 128)
-        hipLaunchKernelGGL(quant_write_kernel<128>, grid, dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL(quant_write_kernel<64>, grid, dim3(kThreads), 0, stream, a);
+    const bool asym = g.asymmetric != 0;
+    if (g.head_dim == 128) {
+        if (asym) hipLaunchKernelGGL((quant_write_kernel<128, true>), grid, dim3(kThreads), 0, stream, a);
+        else hipLaunchKernelGGL((quant_write_kernel<128, false>), grid, dim3(kThreads), 0, stream, a);
+    } else {
+        if (asym) hipLaunchKernelGGL((quant_write_kernel<64, true>), grid, dim3(kThreads), 0, stream, a);
+        else hipLaunchKernelGGL((quant_write_kernel<64, false>), grid, dim3(kThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

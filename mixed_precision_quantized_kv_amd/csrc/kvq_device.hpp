@@ -23,24 +23,31 @@ typedef float __attribute__((ext_vector_type(4), may_alias)) ma_f32x4;
 constexpr int kPage = 16;
 constexpr int kMaxGroup = 16;   // query heads per KV head handled by one MFMA tile
 
-// byte layout of one (block, KV head) section for b-bit codes
+// byte layout of one (block, KV head) section for b-bit codes. The asymmetric format puts a
+// zero point before each group's scale: K zero points (D fp16) then K scales, V zero points
+// (P fp16) then V scales.
 struct Section {
     uint32_t code_bytes;   // P*D*b/8
+    uint32_t kzero_off;    // K zero points (D fp16; asymmetric format only)
     uint32_t kscale_off;   // K scales (D fp16)
     uint32_t vcode_off;    // V codes
+    uint32_t vzero_off;    // V zero points (P fp16; asymmetric format only)
     uint32_t vscale_off;   // V scales (P fp16)
     uint32_t bytes;        // whole section
 };
 
-// (b = 16, the FP16 tier: K values then V values, no scales)
-__host__ __device__ inline Section section_layout(int D, int bits) {
+// (b = 16, the FP16 tier: K values then V values, no scales, in either format)
+__host__ __device__ inline Section section_layout(int D, int bits, bool asym = false) {
     Section s;
     const uint32_t scales = bits == 16 ? 0u : 1u;
+    const uint32_t per = (asym ? 2u : 1u) * scales;      // fp16 parameters per group
     s.code_bytes = (uint32_t)(kPage * D * bits / 8);
-    s.kscale_off = s.code_bytes;
-    s.vcode_off = s.code_bytes + scales * 2u * D;
-    s.vscale_off = 2u * s.code_bytes + scales * 2u * D;
-    s.bytes = 2u * s.code_bytes + scales * (2u * D + 2u * kPage);
+    s.kzero_off = s.code_bytes;
+    s.kscale_off = s.code_bytes + (per - scales) * 2u * D;
+    s.vcode_off = s.code_bytes + per * 2u * D;
+    s.vzero_off = 2u * s.code_bytes + per * 2u * D;
+    s.vscale_off = s.vzero_off + (per - scales) * 2u * kPage;
+    s.bytes = 2u * s.code_bytes + per * (2u * D + 2u * kPage);
     return s;
 }
 
@@ -77,6 +84,38 @@ __device__ inline int quant_code(float x, float s, int bits) {
     float q = rintf(__fdiv_rn(x, s));
     q = fminf(fmaxf(q, -qmax), qmax);
     return (int)q;
+}
+
+// ---------------------------------------------------------------- asymmetric quantizer
+// EchoKV, "Show the math": KIVI-style asymmetric groups. Zero point m = the group minimum (an
+// fp16 value, +0 for a zero minimum), scale s = the least fp16 >= (max - m) / (2^b - 1) (0 for
+// a constant group), code u = round-half-even((x - m) / s) in [0, 2^b - 1]; every decision in
+// binary64, where the difference of two fp16 values and the quotients are exact enough that no
+// rounding crosses a boundary.
+
+// smallest fp16 >= x for finite x > 0 given in binary64: a nearby fp16 value, then one step
+// toward x's side (the double-to-single-to-half rounding lands at most one step away)
+__device__ inline uint16_t f64_to_f16_up(double x) {
+    uint16_t b = f16_bits((_Float16)(float)x);
+    if ((double)f16_val(b) < x)
+        b = (uint16_t)(b + 1);
+    else if (b > 0 && (double)f16_val((uint16_t)(b - 1)) >= x)
+        b = (uint16_t)(b - 1);
+    return b;
+}
+
+__device__ inline uint16_t asym_zero(float mn) { return mn == 0.f ? (uint16_t)0 : f16_bits((_Float16)mn); }
+
+__device__ inline uint16_t asym_scale(float mn, float mx, int bits) {
+    const double range = (double)mx - (double)mn;        // exact for fp16 inputs
+    return range > 0.0 ? f64_to_f16_up(range / (double)((1 << bits) - 1)) : (uint16_t)0;
+}
+
+// code of x in a group with zero point m and scale s (s == 0: the constant group, code 0)
+__device__ inline uint32_t asym_code(float x, float m, float s, int bits) {
+    if (s == 0.f) return 0u;
+    const double q = rint(((double)x - (double)m) / (double)s);
+    return (uint32_t)fmin(fmax(q, 0.0), (double)((1 << bits) - 1));
 }
 
 // Max / sum over all 64 lanes of a wave, every lane active: within each row of 16 lanes by DPP

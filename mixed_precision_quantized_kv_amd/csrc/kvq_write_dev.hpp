@@ -13,6 +13,10 @@
 // reduce across the four token lanes of a wave (shuffles) and the four waves (LDS); token maxima
 // over D reduce across the 16 lanes of a token (shuffles). Codes are packed in registers; words
 // shared by several threads are OR-reduced with shuffles.
+//
+// The asymmetric format (ASYM) keeps the groups and gives each a zero point and a scale from its
+// minimum and maximum (EchoKV, "Show the math": KIVI-style asymmetric groups; "Future work":
+// per-token KIVI storage in the paged cache); the channel reduction then carries both extremes.
 #pragma once
 
 #include "kvq_device.hpp"
@@ -54,6 +58,21 @@ __device__ __forceinline__ void load_f16(const uint16_t* p, float* out) {
     }
 }
 
+// CPT (4 or 8) fp16 bit patterns to 8- or 16-byte aligned memory
+template <int CPT>
+__device__ __forceinline__ void store_f16s(ma_u16* dst, const uint16_t* v) {
+    if constexpr (CPT == 8) {
+        uint4 w;
+        w.x = v[0] | ((uint32_t)v[1] << 16); w.y = v[2] | ((uint32_t)v[3] << 16);
+        w.z = v[4] | ((uint32_t)v[5] << 16); w.w = v[6] | ((uint32_t)v[7] << 16);
+        *reinterpret_cast<ma_uint4*>(dst) = w;
+    } else {
+        uint2 w;
+        w.x = v[0] | ((uint32_t)v[1] << 16); w.y = v[2] | ((uint32_t)v[3] << 16);
+        *reinterpret_cast<ma_uint2*>(dst) = w;
+    }
+}
+
 // pool base of a tier, by arithmetic (a select chain would become a lookup table in scratch)
 __device__ __forceinline__ uint8_t* pool_base(const PoolPtrs& pools, int tier) {
     const uintptr_t b0 = reinterpret_cast<uintptr_t>(pools.base[0]);
@@ -67,10 +86,11 @@ __device__ __forceinline__ uint8_t* pool_base(const PoolPtrs& pools, int tier) {
 // the page's K scales and the codes of all its present tokens from their FP16 originals (ring
 // for positions < p0, k_new after), the new tokens' V codes and scales. `tid` is 0..255 within
 // the 256 threads doing this page; `active` false (or a page past the call) writes nothing.
-// Every thread of the workgroup must call this (it holds one workgroup barrier).
-template <int D>
+// Every thread of the workgroup must call this (it holds one workgroup barrier). chan_red holds
+// 4 rows of D floats (the four waves' channel maxima), 8 for ASYM (then the minima follow).
+template <int D, bool ASYM = false>
 __device__ __forceinline__ void write_page(const WriteArgs& a, int s, int kv, int p0, int j, int tid,
-                                           bool active, float (*chan_max)[D]) {
+                                           bool active, float (*chan_red)[D]) {
     constexpr int P = kPage;
     constexpr int CPT = D / 16;                 // channels per thread
     const int t = tid >> 4, g = tid & 15, c0 = g * CPT;
@@ -105,9 +125,9 @@ __device__ __forceinline__ void write_page(const WriteArgs& a, int s, int kv, in
     const int tier = (int)(handle >> 30);
     const int bits = bits_of_tier(tier);
     const bool fp16 = tier == kFp16Tier;
-    const Section L = section_layout(D, bits);
+    const Section L = section_layout(D, bits, ASYM);
     uint8_t* sec = pool_base(a.pools, tier) + ((size_t)(handle & 0x3fffffffu) * a.H + kv) * L.bytes;
-    const uint32_t qoff = 1u << (bits - 1);
+    const uint32_t qoff = ASYM ? 0u : 1u << (bits - 1);   // the field of the zero code
     const uint32_t fmask = (1u << bits) - 1u;
 
     // ---- V code words this lane will store. V codes are grouped by token quads: code index
@@ -133,17 +153,26 @@ __device__ __forceinline__ void write_page(const WriteArgs& a, int s, int kv, in
         }
     }
 
-    // ---- K: channel maxima over the present tokens (empty slots hold zeros)
-    float m[CPT];
+    // ---- K: channel maxima of |x| over the present tokens (empty slots hold zeros); ASYM: the
+    // channel maxima and minima of x over the present tokens
+    float m[CPT], mn[CPT];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-        float x = fabsf(kf[i]);
+        float x = ASYM ? (present ? kf[i] : -INFINITY) : fabsf(kf[i]);
         x = fmaxf(x, __shfl_xor(x, 16, 64));
         m[i] = fmaxf(x, __shfl_xor(x, 32, 64));
+        if constexpr (ASYM) {
+            float y = present ? kf[i] : INFINITY;
+            y = fminf(y, __shfl_xor(y, 16, 64));
+            mn[i] = fminf(y, __shfl_xor(y, 32, 64));
+        }
     }
     if ((tid & 63) < 16) {
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) chan_max[wave][c0 + i] = m[i];
+        for (int i = 0; i < CPT; ++i) {
+            chan_red[wave][c0 + i] = m[i];
+            if constexpr (ASYM) chan_red[4 + wave][c0 + i] = mn[i];
+        }
     }
     __syncthreads();
     if (!active) return;
@@ -167,15 +196,24 @@ __device__ __forceinline__ void write_page(const WriteArgs& a, int s, int kv, in
         }
         return;
     }
-    uint16_t ks[CPT];
+    uint16_t ks[CPT], kz[CPT];
     uint32_t ku[CPT];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-        const float amax = fmaxf(fmaxf(chan_max[0][c0 + i], chan_max[1][c0 + i]),
-                                 fmaxf(chan_max[2][c0 + i], chan_max[3][c0 + i]));
-        ks[i] = group_scale(amax, bits);
-        ku[i] = (present && ks[i]) ? (uint32_t)(quant_code(kf[i], f16_val(ks[i]), bits) + (int)qoff)
-                                   : qoff;
+        const float amax = fmaxf(fmaxf(chan_red[0][c0 + i], chan_red[1][c0 + i]),
+                                 fmaxf(chan_red[2][c0 + i], chan_red[3][c0 + i]));
+        if constexpr (ASYM) {
+            const float amin = fminf(fminf(chan_red[4][c0 + i], chan_red[5][c0 + i]),
+                                     fminf(chan_red[6][c0 + i], chan_red[7][c0 + i]));
+            kz[i] = asym_zero(amin);
+            ks[i] = asym_scale(amin, amax, bits);
+            ku[i] = present ? asym_code(kf[i], f16_val(kz[i]), f16_val(ks[i]), bits) : 0u;
+        } else {
+            kz[i] = 0;
+            ks[i] = group_scale(amax, bits);
+            ku[i] = (present && ks[i]) ? (uint32_t)(quant_code(kf[i], f16_val(ks[i]), bits) + (int)qoff)
+                                       : qoff;
+        }
     }
 
     // ---- K codes: row t holds D codes, 32/b per word; this thread's CPT codes fill CPT*b bits
@@ -202,29 +240,28 @@ __device__ __forceinline__ void write_page(const WriteArgs& a, int s, int kv, in
             if (g % share == 0) row[c0 / per_word] = word;
         }
     }
-    // K scales (one slot row writes them)
+    // K scales, and ASYM zero points (slot row 0 writes them)
     if (t == 0) {
-        ma_u16* dst = reinterpret_cast<ma_u16*>(sec + L.kscale_off) + c0;
-        if constexpr (CPT == 8) {
-            uint4 v;
-            v.x = ks[0] | ((uint32_t)ks[1] << 16); v.y = ks[2] | ((uint32_t)ks[3] << 16);
-            v.z = ks[4] | ((uint32_t)ks[5] << 16); v.w = ks[6] | ((uint32_t)ks[7] << 16);
-            *reinterpret_cast<ma_uint4*>(dst) = v;
-        } else {
-            uint2 v;
-            v.x = ks[0] | ((uint32_t)ks[1] << 16); v.y = ks[2] | ((uint32_t)ks[3] << 16);
-            *reinterpret_cast<ma_uint2*>(dst) = v;
-        }
+        store_f16s<CPT>(reinterpret_cast<ma_u16*>(sec + L.kscale_off) + c0, ks);
+        if constexpr (ASYM) store_f16s<CPT>(reinterpret_cast<ma_u16*>(sec + L.kzero_off) + c0, kz);
     }
 
-    // ---- V: one scale per new token over its D channels (the token's 16 lanes)
-    float vm = 0.f;
+    // ---- V: one scale (ASYM: and zero point) per new token over its D channels (the token's
+    // 16 lanes)
+    float vm = ASYM ? -INFINITY : 0.f, vn = INFINITY;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) vm = fmaxf(vm, fabsf(vf[i]));
+    for (int i = 0; i < CPT; ++i) {
+        vm = fmaxf(vm, ASYM ? vf[i] : fabsf(vf[i]));
+        vn = fminf(vn, vf[i]);
+    }
 #pragma unroll
-    for (int msk = 1; msk < 16; msk <<= 1) vm = fmaxf(vm, __shfl_xor(vm, msk, 64));
-    const uint16_t vs = is_new ? group_scale(vm, bits) : 0;
-    const float vsf = f16_val(vs);
+    for (int msk = 1; msk < 16; msk <<= 1) {
+        vm = fmaxf(vm, __shfl_xor(vm, msk, 64));
+        if constexpr (ASYM) vn = fminf(vn, __shfl_xor(vn, msk, 64));
+    }
+    const uint16_t vs = !is_new ? (uint16_t)0 : ASYM ? asym_scale(vn, vm, bits) : group_scale(vm, bits);
+    const uint16_t vz = ASYM && is_new ? asym_zero(vn) : (uint16_t)0;
+    const float vsf = f16_val(vs), vzf = f16_val(vz);
     // this token's fields (new tokens: their codes; empty slots: the zero code) and the mask of
     // fields the call writes
     uint32_t part[8], mask[8];
@@ -233,8 +270,11 @@ __device__ __forceinline__ void write_page(const WriteArgs& a, int s, int kv, in
     if (t >= told) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            const uint32_t u = (is_new && vs) ? (uint32_t)(quant_code(vf[i], vsf, bits) + (int)qoff)
-                                              : qoff;
+            uint32_t u;
+            if constexpr (ASYM)
+                u = is_new ? asym_code(vf[i], vzf, vsf, bits) : 0u;
+            else
+                u = (is_new && vs) ? (uint32_t)(quant_code(vf[i], vsf, bits) + (int)qoff) : qoff;
             const int w = i / cw;
             const int fb = field_bit((i % cw) * 4 + r, bits);
             part[w] |= u << fb;
@@ -263,9 +303,12 @@ __device__ __forceinline__ void write_page(const WriteArgs& a, int s, int kv, in
             }
         }
     }
-    // V scales: new tokens get theirs, empty slots zero; earlier tokens keep theirs
-    if (g == 0 && t >= told)
+    // V scales (ASYM: and zero points): new tokens get theirs, empty slots zero; earlier tokens
+    // keep theirs
+    if (g == 0 && t >= told) {
         reinterpret_cast<ma_u16*>(sec + L.vscale_off)[t] = vs;
+        if constexpr (ASYM) reinterpret_cast<ma_u16*>(sec + L.vzero_off)[t] = vz;
+    }
 }
 
 // The ring update for sequence s, KV head kv: the newest min(n_new, R) keys into their slots.

@@ -33,10 +33,11 @@ def f16_bits(t: torch.Tensor) -> np.ndarray:
 class LayerPair:
     """One layer: GPU pools + ring (via libkvq) and oracle pools + ring, same block table."""
 
-    def __init__(self, hq, hkv, d, batch, max_pages, page_tiers, capacity=None, seed=0, R=64):
+    def __init__(self, hq, hkv, d, batch, max_pages, page_tiers, capacity=None, seed=0, R=64,
+                 asymmetric=False):
         self.hq, self.hkv, self.d, self.batch, self.R = hq, hkv, d, batch, R
-        self.g = kvq.geometry(1, hq, hkv, d, batch, max_pages, ring_size=R)
-        self.og = oracle.geom(hq, hkv, d, 16, R)
+        self.g = kvq.geometry(1, hq, hkv, d, batch, max_pages, ring_size=R, asymmetric=asymmetric)
+        self.og = oracle.geom(hq, hkv, d, 16, R, asymmetric=asymmetric)
         if capacity is None:
             capacity = [max(1, sum(t == tier for row in page_tiers for t in row)) for tier in range(4)]
         self.capacity = list(capacity)

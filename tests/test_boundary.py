@@ -32,7 +32,7 @@ def test_exports_every_header_symbol():
     L = kvq.lib()
     for n in names:
         assert getattr(L, n) is not None
-    assert kvq.kv_abi_version() == 2                  # four tier pools (FP16 added)
+    assert kvq.kv_abi_version() == 3                  # the geometry carries the storage format
 
 
 def geom(**kw):
