@@ -893,6 +893,8 @@ struct FastPair {
     uint32_t ka[KW], kb[KW], va[KW], vb[KW];
     uint32_t ksa, ksb;                           // K-scale dwords (channels 2*lane, 2*lane+1)
     u32x2 vsa, vsb;                              // V scales, quad G of pages A and B
+    uint32_t kza, kzb;                           // asymmetric format: K zero points, as ksa, ksb
+    u32x2 vza, vzb;                              // asymmetric format: V zero points, as vsa, vsb
     int ntok_a, ntok_b;                          // valid tokens; 0 for an absent page
 };
 
@@ -914,18 +916,21 @@ __device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* w) {
 
 // this lane's byte offsets inside a section
 struct LaneOffsets {
-    uint32_t k, v, ks, vs;
+    uint32_t k, v, ks, vs, kz, vz;
 };
 
-template <int D, int BITS>
+template <int D, int BITS, bool ASYM>
 __device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
+    constexpr uint32_t kpar = (ASYM ? 4 : 2) * D, vpar = (ASYM ? 4 : 2) * kPage;   // group parameters
     constexpr uint32_t code_bytes = kPage * D * BITS / 8;
     const int t = lane & 15, G = lane >> 4;
     LaneOffsets o;
     o.k = t * (D * BITS / 8) + G * (D * BITS / 32);
-    o.v = code_bytes + 2 * D + (G * D + t * (D / 16)) * BITS / 2;
-    o.ks = code_bytes + 4 * (lane & (D / 2 - 1));
-    o.vs = 2 * code_bytes + 2 * D + 8 * G;
+    o.v = code_bytes + kpar + (G * D + t * (D / 16)) * BITS / 2;
+    o.kz = code_bytes + 4 * (lane & (D / 2 - 1));
+    o.ks = o.kz + (kpar - 2 * D);
+    o.vz = 2 * code_bytes + kpar + 8 * G;
+    o.vs = o.vz + (vpar - 2 * kPage);
     return o;
 }
 
@@ -949,12 +954,12 @@ __device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t r, uint32_t of
 // the last pair and carry no tokens. Each page section is read through a buffer resource
 // built in scalar registers, so the lane offsets stay fixed VGPR offsets and no per-load
 // address arithmetic runs on the vector unit.
-template <int D, int BITS>
+template <int D, int BITS, bool ASYM>
 __device__ __forceinline__ void load_pair_fast(const uint8_t* base, uint32_t hv, int H, int kv,
                                                int cb, int npg, int q, int nq, int ctx,
                                                const LaneOffsets& lo, bool side,
                                                FastPair<D, BITS>& P) {
-    constexpr uint32_t sec_bytes = 2 * (kPage * D * BITS / 8) + 2 * D + 2 * kPage;
+    constexpr uint32_t sec_bytes = 2 * (kPage * D * BITS / 8) + (ASYM ? 2 : 1) * (2 * D + 2 * kPage);
     constexpr int KW = FastPair<D, BITS>::KW;
     const bool real = q < nq;
     const int pa = 2 * min(q, nq - 1);
@@ -974,6 +979,12 @@ __device__ __forceinline__ void load_pair_fast(const uint8_t* base, uint32_t hv,
     // the V scales of both pages (one cache line each); the round picks its side's
     P.vsa = __builtin_amdgcn_raw_buffer_load_b64(ra, lo.vs, 0, 0);
     P.vsb = __builtin_amdgcn_raw_buffer_load_b64(rb, lo.vs, 0, 0);
+    if constexpr (ASYM) {
+        P.kza = __builtin_amdgcn_raw_buffer_load_b32(ra, lo.kz, 0, 0);
+        P.kzb = __builtin_amdgcn_raw_buffer_load_b32(rb, lo.kz, 0, 0);
+        P.vza = __builtin_amdgcn_raw_buffer_load_b64(ra, lo.vz, 0, 0);
+        P.vzb = __builtin_amdgcn_raw_buffer_load_b64(rb, lo.vz, 0, 0);
+    }
     const int page = cb + pa;
     P.ntok_a = real ? min(kPage, ctx - page * kPage) : 0;
     P.ntok_b = real && has_b ? min(kPage, ctx - (page + 1) * kPage) : 0;
@@ -993,8 +1004,10 @@ __device__ __forceinline__ uint32_t hfma(uint32_t x, float mul, float add) {
 // sitting at bit 2^k inside the low ten bits is turned into the fp16 value 1024 + 2^k * f by one
 // AND-OR with the exponent bits of 1024; one exact fused multiply-add, x * 2^-k - (1024 * 2^-k
 // + 2^(b-1)), then gives the signed code. Fields above bit 9 are shifted down by 8 first.
-template <int D, int BITS>
+// ASYM: the offset removed is 1024 * 2^-k alone, leaving the unsigned code u.
+template <int D, int BITS, bool ASYM = false>
 __device__ __forceinline__ void unpack_k_fast(const uint32_t* w, uint32_t* out) {
+    constexpr float o = ASYM ? 0.0f : (float)(1 << (BITS - 1));   // the code offset 2^(b-1)
     // the exponent bits of 1024 in a VGPR: gfx9 VOP3 instructions take no literals, so with a
     // register operand the AND-OR is one v_and_or_b32 (mask from an SGPR) instead of two ops
     uint32_t E;
@@ -1003,26 +1016,26 @@ __device__ __forceinline__ void unpack_k_fast(const uint32_t* w, uint32_t* out) 
 #pragma unroll
         for (int i = 0; i < D / 64; ++i) {
             const uint32_t s = w[i] >> 8;
-            out[8 * i + 0] = hsub(and_or(w[i], 0x00030003u, E), 1026.0f);
-            out[8 * i + 1] = hfma(and_or(w[i], 0x000C000Cu, E), 0.25f, -258.0f);
-            out[8 * i + 2] = hfma(and_or(w[i], 0x00300030u, E), 0.0625f, -66.0f);
-            out[8 * i + 3] = hfma(and_or(w[i], 0x00C000C0u, E), 0.015625f, -18.0f);
-            out[8 * i + 4] = hfma(and_or(w[i], 0x03000300u, E), 0.00390625f, -6.0f);
-            out[8 * i + 5] = hfma(and_or(s, 0x000C000Cu, E), 0.25f, -258.0f);
-            out[8 * i + 6] = hfma(and_or(s, 0x00300030u, E), 0.0625f, -66.0f);
-            out[8 * i + 7] = hfma(and_or(s, 0x00C000C0u, E), 0.015625f, -18.0f);
+            out[8 * i + 0] = hsub(and_or(w[i], 0x00030003u, E), 1024.0f + o);
+            out[8 * i + 1] = hfma(and_or(w[i], 0x000C000Cu, E), 0.25f, -256.0f - o);
+            out[8 * i + 2] = hfma(and_or(w[i], 0x00300030u, E), 0.0625f, -64.0f - o);
+            out[8 * i + 3] = hfma(and_or(w[i], 0x00C000C0u, E), 0.015625f, -16.0f - o);
+            out[8 * i + 4] = hfma(and_or(w[i], 0x03000300u, E), 0.00390625f, -4.0f - o);
+            out[8 * i + 5] = hfma(and_or(s, 0x000C000Cu, E), 0.25f, -256.0f - o);
+            out[8 * i + 6] = hfma(and_or(s, 0x00300030u, E), 0.0625f, -64.0f - o);
+            out[8 * i + 7] = hfma(and_or(s, 0x00C000C0u, E), 0.015625f, -16.0f - o);
         }
     } else if constexpr (BITS == 4) {
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) {
             const uint32_t s = w[i] >> 8;
-            out[4 * i + 0] = hsub(and_or(w[i], 0x000F000Fu, E), 1032.0f);
-            out[4 * i + 1] = hfma(and_or(w[i], 0x00F000F0u, E), 0.0625f, -72.0f);
-            out[4 * i + 2] = hsub(and_or(s, 0x000F000Fu, E), 1032.0f);
-            out[4 * i + 3] = hfma(and_or(s, 0x00F000F0u, E), 0.0625f, -72.0f);
+            out[4 * i + 0] = hsub(and_or(w[i], 0x000F000Fu, E), 1024.0f + o);
+            out[4 * i + 1] = hfma(and_or(w[i], 0x00F000F0u, E), 0.0625f, -64.0f - o);
+            out[4 * i + 2] = hsub(and_or(s, 0x000F000Fu, E), 1024.0f + o);
+            out[4 * i + 3] = hfma(and_or(s, 0x00F000F0u, E), 0.0625f, -64.0f - o);
         }
     } else {
-        unpack_k<D>(w, 8, out);
+        unpack_k<D, ASYM>(w, 8, out);
     }
 }
 
@@ -1054,16 +1067,26 @@ __device__ __forceinline__ void read_kscales(const uint32_t* ks_lds, int slot, i
 
 // S^T of one pair for this lane's side (tokens 4G..4G+3 of its page, head h % 8), log2 units
 // SINGLE: page B is absent (a chunk's odd last page): its keys are neither decoded nor multiplied
-template <int D, int BITS, bool SINGLE = false>
+// ASYM: the zero-point parts of both pages first (their zero points staged in slots 2, 3)
+template <int D, int BITS, bool SINGLE = false, bool ASYM = false>
 __device__ __forceinline__ float4v pair_logits(const FastPair<D, BITS>& P, const uint32_t* qf,
                                                const uint32_t* ks_lds, int lane, bool side,
                                                float scale_log2) {
     const int G = lane >> 4;
     float4v acca = {0.f, 0.f, 0.f, 0.f}, accb = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (ASYM) {
+        uint32_t kz[D / 8];
+        read_kscales<D>(ks_lds, 2, G, kz);
+        acca = zero_point_logits<D>(kz, qf);
+        if constexpr (!SINGLE) {
+            read_kscales<D>(ks_lds, 3, G, kz);
+            accb = zero_point_logits<D>(kz, qf);
+        }
+    }
     uint32_t kfa[D / 8], kfb[D / 8];
-    unpack_k_fast<D, BITS>(P.ka, kfa);
-    if constexpr (!SINGLE) unpack_k_fast<D, BITS>(P.kb, kfb);
-    if constexpr (BITS == 2) {
+    unpack_k_fast<D, BITS, ASYM>(P.ka, kfa);
+    if constexpr (!SINGLE) unpack_k_fast<D, BITS, ASYM>(P.kb, kfb);
+    if constexpr (BITS == 2 && !ASYM) {
         // codes -1, 0, 1: code * scale is exact in fp16, so the scales fold into the keys
         uint32_t ksa[D / 8], ksb[D / 8];
         read_kscales<D>(ks_lds, 0, G, ksa);
@@ -1148,7 +1171,7 @@ __device__ __forceinline__ float max2(float a, float b, float pinf) {
 }
 
 // one page pair: QK, the running maxima, then PV (SINGLE: page B is absent)
-template <int D, int BITS, bool SINGLE = false>
+template <int D, int BITS, bool SINGLE = false, bool ASYM = false>
 __device__ __forceinline__ void round_fast(const FastPair<D, BITS>& P, const uint32_t* qf,
                                            uint32_t* ks_lds, int lane, int bp16, int bp32, float pinf,
                                            float scale_log2, WaveState<D>& st) {
@@ -1161,8 +1184,12 @@ __device__ __forceinline__ void round_fast(const FastPair<D, BITS>& P, const uin
     __builtin_amdgcn_wave_barrier();
     stage_kscale<D>(ks_lds, 0, lane, P.ksa);
     stage_kscale<D>(ks_lds, 1, lane, P.ksb);
+    if constexpr (ASYM) {
+        stage_kscale<D>(ks_lds, 2, lane, P.kza);
+        stage_kscale<D>(ks_lds, 3, lane, P.kzb);
+    }
     __builtin_amdgcn_wave_barrier();
-    float4v lg = pair_logits<D, BITS, SINGLE>(P, qf, ks_lds, lane, side, scale_log2);
+    float4v lg = pair_logits<D, BITS, SINGLE, ASYM>(P, qf, ks_lds, lane, side, scale_log2);
     if (partial) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -1180,6 +1207,7 @@ __device__ __forceinline__ void round_fast(const FastPair<D, BITS>& P, const uin
         const float m_new = fmaxf(st.m, mx + kLazy);
         const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);   // 0 on the first round
         st.l *= alpha;
+        if constexpr (ASYM) st.z *= alpha;
 #pragma unroll
         for (int k = 0; k < D / 16; ++k) st.o[k] *= alpha;
         st.m = m_new;
@@ -1188,18 +1216,22 @@ __device__ __forceinline__ void round_fast(const FastPair<D, BITS>& P, const uin
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(lg[i] - st.m);
     st.l += (p[0] + p[1]) + (p[2] + p[3]);
+    if constexpr (ASYM) {
+        const u32x2 vza = P.vza, vzb = P.vzb;
+        st.z += zero_point_mass(p, side ? vzb[0] : vza[0], side ? vzb[1] : vza[1], ntok, G);
+    }
     const u32x2 vsa = P.vsa, vsb = P.vsb;          // values, so the selects stay in registers
     const uint32_t vs0 = side ? vsb[0] : vsa[0], vs1 = side ? vsb[1] : vsa[1];
     const half8 wop = pair_weights(p, vs0, vs1, side, partial, ntok, G);
     // V codes as exact fp16 integers, decoded like the K codes (the two word layouts put codes
     // in the same positions)
     uint32_t va[D / 8], vb[D / 8];
-    unpack_k_fast<D, BITS>(P.va, va);
+    unpack_k_fast<D, BITS, ASYM>(P.va, va);
     if constexpr (SINGLE) {
 #pragma unroll
         for (int i = 0; i < D / 8; ++i) vb[i] = 0u;
     } else {
-        unpack_k_fast<D, BITS>(P.vb, vb);
+        unpack_k_fast<D, BITS, ASYM>(P.vb, vb);
     }
 #pragma unroll
     for (int k = 0; k < D / 16; ++k)
@@ -1207,14 +1239,14 @@ __device__ __forceinline__ void round_fast(const FastPair<D, BITS>& P, const uin
             make_half8(va[2 * k], va[2 * k + 1], vb[2 * k], vb[2 * k + 1]), wop, st.o[k], 0, 0, 0);
 }
 
-template <int D, int BITS, int DEPTH>
+template <int D, int BITS, int DEPTH, bool ASYM = false>
 __device__ __forceinline__ void wave_chunk_fast(const uint8_t* base, uint32_t hv, int H, int kv,
                                                 int cb, int npg, int ctx, int lane,
                                                 const uint32_t* qf, uint32_t* ks_lds,
                                                 float scale_log2, WaveState<D>& st) {
     const int nq = (npg + 1) / 2;
     const bool side = (lane & 8) != 0;
-    const LaneOffsets lo = lane_offsets<D, BITS>(lane);
+    const LaneOffsets lo = lane_offsets<D, BITS, ASYM>(lane);
     const int bp16 = (lane ^ 16) << 2, bp32 = (lane ^ 32) << 2;   // row-exchange addresses
     float pinf;
     asm("v_mov_b32 %0, 0x7f800000" : "=v"(pinf));
@@ -1227,7 +1259,7 @@ __device__ __forceinline__ void wave_chunk_fast(const uint8_t* base, uint32_t hv
     FastPair<D, BITS> b[DEPTH];
 #pragma unroll
     for (int j = 0; j < DEPTH - 1; ++j)
-        load_pair_fast<D, BITS>(base, hv, H, kv, cb, npg, j, nq, ctx, lo, side, b[j]);
+        load_pair_fast<D, BITS, ASYM>(base, hv, H, kv, cb, npg, j, nq, ctx, lo, side, b[j]);
     // The scheduling barriers keep each round's instructions between its loads and the next
     // round's: the scheduler would otherwise start decoding the pair just requested inside
     // this round, and the waits for that data would stall the round.
@@ -1235,10 +1267,10 @@ __device__ __forceinline__ void wave_chunk_fast(const uint8_t* base, uint32_t hv
     for (int r = 0; r < nfull * DEPTH; r += DEPTH) {
 #pragma unroll
         for (int i = 0; i < DEPTH; ++i) {
-            load_pair_fast<D, BITS>(base, hv, H, kv, cb, npg, r + i + DEPTH - 1, nq, ctx, lo, side,
+            load_pair_fast<D, BITS, ASYM>(base, hv, H, kv, cb, npg, r + i + DEPTH - 1, nq, ctx, lo, side,
                                     b[(i + DEPTH - 1) % DEPTH]);
             __builtin_amdgcn_sched_barrier(0);
-            round_fast<D, BITS>(b[i], qf, ks_lds, lane, bp16, bp32, pinf, scale_log2, st);
+            round_fast<D, BITS, false, ASYM>(b[i], qf, ks_lds, lane, bp16, bp32, pinf, scale_log2, st);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -1248,9 +1280,9 @@ __device__ __forceinline__ void wave_chunk_fast(const uint8_t* base, uint32_t hv
     for (int i = 0; i < DEPTH - 1; ++i) {
         if (i < nq - nfull * DEPTH) {
             if ((npg & 1) && i == nq - nfull * DEPTH - 1)
-                round_fast<D, BITS, true>(b[i], qf, ks_lds, lane, bp16, bp32, pinf, scale_log2, st);
+                round_fast<D, BITS, true, ASYM>(b[i], qf, ks_lds, lane, bp16, bp32, pinf, scale_log2, st);
             else
-                round_fast<D, BITS>(b[i], qf, ks_lds, lane, bp16, bp32, pinf, scale_log2, st);
+                round_fast<D, BITS, false, ASYM>(b[i], qf, ks_lds, lane, bp16, bp32, pinf, scale_log2, st);
         }
     }
 }
@@ -1274,7 +1306,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
     // the K scales of a pair's pages (ASYM: then their zero points), staged per wave
     __shared__ __attribute__((aligned(16))) uint32_t lds_ks[kWaves][ASYM ? 4 : 2][64];
     // the K scales of the uniform-width loop's page pairs, staged per wave (stage_kscale)
-    __shared__ __attribute__((aligned(16))) uint32_t lds_ksr[kWaves][2 * kKsSlot<D>];
+    __shared__ __attribute__((aligned(16))) uint32_t lds_ksr[kWaves][(ASYM ? 4 : 2) * kKsSlot<D>];
     // per-wave partials, one padded row per head: channel c of head h sits at h*kORow + c +
     // 4*(c/32), so the float4 writes of a wave's 64 lanes (16 heads x 4 channel quarters) spread
     // over all LDS banks instead of landing on the same four
@@ -1371,15 +1403,14 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
             uniform = __builtin_amdgcn_ballot_w64((int)(hv >> 30) != tier0) == 0;
         }
         uint32_t* ks_round = &lds_ksr[wave][0];
-        // the asymmetric format takes the general loops (constexpr: no fast path is compiled)
-        if (!ASYM && HALF && uniform && tier0 == 0)
-            wave_chunk_fast<D, 2, kDepth2>(a.pools.base[0], hv, a.H, kv, cb, npg, ctx, lane, qf,
+        if (HALF && uniform && tier0 == 0)
+            wave_chunk_fast<D, 2, kDepth2, ASYM>(a.pools.base[0], hv, a.H, kv, cb, npg, ctx, lane, qf,
                                            ks_round, a.scale_log2, st);
-        else if (!ASYM && HALF && uniform && tier0 == 1)
-            wave_chunk_fast<D, 4, kDepth4>(a.pools.base[1], hv, a.H, kv, cb, npg, ctx, lane, qf,
+        else if (HALF && uniform && tier0 == 1)
+            wave_chunk_fast<D, 4, kDepth4, ASYM>(a.pools.base[1], hv, a.H, kv, cb, npg, ctx, lane, qf,
                                            ks_round, a.scale_log2, st);
-        else if (!ASYM && HALF && uniform && tier0 == 2)
-            wave_chunk_fast<D, 8, kDepth8>(a.pools.base[2], hv, a.H, kv, cb, npg, ctx, lane, qf,
+        else if (HALF && uniform && tier0 == 2)
+            wave_chunk_fast<D, 8, kDepth8, ASYM>(a.pools.base[2], hv, a.H, kv, cb, npg, ctx, lane, qf,
                                            ks_round, a.scale_log2, st);
         else if (uniform && tier0 == 0)
             wave_chunk_uniform<D, 2, 2, HALF, ASYM>(a.pools.base[0], hv, a.H, kv, cb, npg, ctx, lane, qf, ks_slot,
