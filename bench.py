@@ -11,11 +11,12 @@ step's launches. The step time is the window of K steps divided by K plus one ca
 timed in windows of its own, divided by 64 -- the same charge whatever K is.
 
     python bench.py [--gpus 1] [--steps 256] [--warmup 10] [--workload qwen14b_32k]
-                    [--also llama70b_128k]
+                    [--also llama70b_128k] [--asymmetric] [--no-asym-leg]
 
 Prints one JSON line. `value` is the effective cache bytes the attention kernels must read per
 step divided by the step time (GB/s); steps/s is reported beside it. `also` holds the same
-figures for a second workload (by default the 70B shape at 128K context).
+figures for a second workload (by default the 70B shape at 128K context), `asymmetric_format`
+for the workload stored in the asymmetric format (a zero point beside every scale).
 """
 from __future__ import annotations
 
@@ -104,20 +105,26 @@ def parse():
     ap.add_argument("--also", default="llama70b_128k",
                     help="a second workload measured after the first and reported under 'also' "
                          "('' to skip)")
+    ap.add_argument("--asymmetric", action="store_true",
+                    help="run the workload with the asymmetric cache format (zero point + scale)")
+    ap.add_argument("--no-asym-leg", action="store_true",
+                    help="skip the 'asymmetric_format' leg (the workload again, asymmetric format)")
     return ap.parse_args()
 
 
-def attn_bytes(w, ctx: int, bits: int) -> int:
+def attn_bytes(w, ctx: int, bits: int, asym: bool = False) -> int:
     """effective cache bytes one attention launch must read for one sequence of length ctx: the
     valid tokens' K and V codes and V scales, one K-scale vector per page and kv head, and the
-    block-table entries (queries, outputs and workspace are not counted)"""
+    block-table entries (queries, outputs and workspace are not counted); the asymmetric format
+    adds a zero point beside every scale"""
     D, H = w.head_dim, w.num_kv_heads
     pages = (ctx + 15) // 16
-    per_kv = ctx * (D * bits // 4 + 2) + pages * 2 * D
+    par = 4 if asym else 2                           # bytes of a group's fp16 parameters
+    per_kv = ctx * (D * bits // 4 + par) + pages * par * D
     return H * per_kv + 4 * pages
 
 
-def write_bytes(w, pos: int, n: int, bits: int) -> int:
+def write_bytes(w, pos: int, n: int, bits: int, asym: bool = False) -> int:
     """bytes the write of n tokens at pos must move for one sequence: the touched pages' present
     keys (ring or input) and the new values in, the pages' K codes and scales, the new tokens' V
     codes and scales, and the new keys into the ring out"""
@@ -125,24 +132,27 @@ def write_bytes(w, pos: int, n: int, bits: int) -> int:
     lo = pos // P * P
     present = pos + n - lo                           # keys the touched pages hold afterwards
     pages = (pos + n - 1) // P - pos // P + 1
+    par = 4 if asym else 2                           # bytes of a group's fp16 parameters
     per_kv = (present * D * 2 + n * D * 2 +          # keys and new values in
-              pages * (P * D * bits // 8 + 2 * D) +  # K codes and scales out
-              n * (D * bits // 8 + 2) + n * D * 2)   # V codes and scales, ring out
+              pages * (P * D * bits // 8 + par * D) +  # K codes and scales out
+              n * (D * bits // 8 + par) + n * D * 2)   # V codes and scales, ring out
     return H * per_kv
 
 
 class Model:
     """All layers of one workload: pools, block tables (from the library's allocator), rings."""
 
-    def __init__(self, w, steps_total: int, torch, kvq, synth, dev):
+    def __init__(self, w, steps_total: int, torch, kvq, synth, dev, asym=False):
         self.w = w
+        self.asym = asym
         self.torch = torch
         L, B = w.num_layers, w.batch
         self.lens0 = synth.seq_lengths(w)                 # tokens at the first decode step
         self.max_ctx = int(self.lens0.max()) + steps_total * w.new_tokens
         self.max_pages = (self.max_ctx + 15) // 16 + 1
         self.bits = synth.layer_bits(w)
-        self.g = kvq.geometry(L, w.num_q_heads, w.num_kv_heads, w.head_dim, B, self.max_pages)
+        self.g = kvq.geometry(L, w.num_q_heads, w.num_kv_heads, w.head_dim, B, self.max_pages,
+                              asymmetric=asym)
         need = int(sum((int(n) + steps_total * w.new_tokens + 15) // 16 + 1 for n in self.lens0))
         cap = np.zeros((L, 3), dtype=np.uint32)
         for l, b in enumerate(self.bits):
@@ -192,7 +202,7 @@ def prefill(m: Model, kvq, synth, dev):
 
 
 def measure(w, steps: int, warmup: int, pages_per_split: int, unfused_flag: bool, fused_flag: bool,
-            torch, kvq, synth, dev) -> dict:
+            torch, kvq, synth, dev, asym: bool = False) -> dict:
     """GPU timings of one workload: the steps window, the attention launches, the canary firing"""
     L, B, nn = w.num_layers, w.batch, w.new_tokens
     # the fused step takes up to 64 new tokens, but with more than 16 (over two pages, written
@@ -200,7 +210,7 @@ def measure(w, steps: int, warmup: int, pages_per_split: int, unfused_flag: bool
     unfused = unfused_flag or (nn > 16 and not fused_flag)
     steps_total = warmup + steps
     t0 = time.time()
-    m = Model(w, steps_total, torch, kvq, synth, dev)
+    m = Model(w, steps_total, torch, kvq, synth, dev, asym)
     prefill(m, kvq, synth, dev)
     t_setup = time.time() - t0
 
@@ -326,10 +336,10 @@ def measure(w, steps: int, warmup: int, pages_per_split: int, unfused_flag: bool
     for j in range(steps):
         ctx = lens + (warmup + j) * nn
         for l, b in enumerate(m.bits):
-            per_launch_bytes[j, l] = sum(attn_bytes(w, int(c), b) for c in ctx)
+            per_launch_bytes[j, l] = sum(attn_bytes(w, int(c), b, asym) for c in ctx)
             if not unfused:
-                per_launch_bytes[j, l] += sum(write_bytes(w, int(c) - nn, nn, b) for c in ctx)
-        step_bytes.append(sum(attn_bytes(w, int(c), b) for c in ctx for b in m.bits))
+                per_launch_bytes[j, l] += sum(write_bytes(w, int(c) - nn, nn, b, asym) for c in ctx)
+        step_bytes.append(sum(attn_bytes(w, int(c), b, asym) for c in ctx for b in m.bits))
     step_bytes = float(np.mean(step_bytes))
     avg_launch_bytes = float(per_launch_bytes.mean())
     avg_attn_ms = float(attn_group_ms.mean()) / L
@@ -351,7 +361,7 @@ def run(args):
     w = synth.WORKLOADS[args.workload]
     L, B = w.num_layers, w.batch
     r = measure(w, args.steps, args.warmup, args.pages_per_split, args.unfused, args.fused,
-                torch, kvq, synth, dev)
+                torch, kvq, synth, dev, args.asymmetric)
     m, unfused, pps = r["m"], r["unfused"], r["pps"]
     ms_step, step_bytes, achieved = r["ms_step"], r["step_bytes"], r["achieved"]
     value = step_bytes / (ms_step * 1e-3) / 1e9
@@ -361,7 +371,7 @@ def run(args):
     probes = hbm_probes(torch, dev)
     traffic = None
     if (ATTN_TRAFFIC["source_sha256"] == source_digest(ATTN_SRC) and not unfused
-            and args.workload == "qwen14b_32k" and not args.pages_per_split):
+            and args.workload == "qwen14b_32k" and not args.pages_per_split and not args.asymmetric):
         traffic = ATTN_TRAFFIC["bytes_per_launch"]      # taken on the fused kernel, default workload
     tiers = {b: bits.count(b) for b in (2, 4, 8)}
     res = {
@@ -384,7 +394,9 @@ def run(args):
             "page": 16, "ring": w.ring_size, "layer_bits": {f"int{b}": n for b, n in tiers.items()},
             "pages_per_split": pps, "canary_every": CANARY_EVERY,
         },
-        "storage": "packed int2/int4/int8 codes + fp16 scales; f16 MFMA, f32 accumulate",
+        "storage": ("packed int2/int4/int8 codes + fp16 zero points and scales (asymmetric format)"
+                    if args.asymmetric else "packed int2/int4/int8 codes + fp16 scales")
+                   + "; f16 MFMA, f32 accumulate",
         "step_time": "ms_per_step = the window of K steps (every layer's write and attention) / K "
                      "+ one canary firing (every layer, one launch, own event window) / 64",
         "attn_bytes_per_step": int(step_bytes),
@@ -422,6 +434,19 @@ def run(args):
             "attn_kernel_us": round(ra["avg_attn_ms"] * 1e3, 3),
             "canary_ms_per_firing": round(ra["canary_ms"], 5),
             "roofline_frac": round(ra["achieved"] / HBM_PEAK_GBS, 4),
+        }
+    if not args.no_asym_leg and not args.asymmetric:
+        rs = measure(w, min(args.steps, 64), min(args.warmup, 4), 0, args.unfused, args.fused,
+                     torch, kvq, synth, dev, True)
+        del rs["m"]
+        torch.cuda.empty_cache()
+        res["asymmetric_format"] = {
+            "workload": w.name, "storage": "zero point + scale per group (KIVI-style)",
+            "steps": min(args.steps, 64), "value": round(rs["step_bytes"] / (rs["ms_step"] * 1e-3) / 1e9, 2),
+            "unit": "GB/s", "ms_per_step": round(rs["ms_step"], 5),
+            "steps_per_s": round(1000.0 / rs["ms_step"], 2),
+            "attn_kernel_us": round(rs["avg_attn_ms"] * 1e3, 3),
+            "roofline_frac": round(rs["achieved"] / HBM_PEAK_GBS, 4),
         }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, bits, args.cpu_layers, args.cpu_reps, step_bytes)

@@ -56,14 +56,28 @@ def check_attention_and_canary(L, q):
 
 @pytest.mark.parametrize("name,layer,bits", CASES, ids=[f"{n}-L{l}-int{b}" for n, l, b in CASES])
 def test_full_context_layer(name, layer, bits):
+    full_context_layer(name, layer, bits, asymmetric=False)
+
+
+ASYM_CASES = first_layer_of_each_width("qwen14b_32k")
+
+
+@pytest.mark.parametrize("name,layer,bits", ASYM_CASES, ids=[f"{n}-L{l}-int{b}" for n, l, b in ASYM_CASES])
+def test_full_context_layer_asymmetric(name, layer, bits):
+    """the same at 32K with the asymmetric cache format (zero point and scale per group)"""
+    full_context_layer(name, layer, bits, asymmetric=True)
+
+
+def full_context_layer(name, layer, bits, asymmetric):
     w = synth.WORKLOADS[name]
     N = w.context
     B = w.batch
-    print(f"\n[case] {name} layer {layer} INT{bits}: batch {B}, context {N}", flush=True)
+    print(f"\n[case] {name} layer {layer} INT{bits}{' asymmetric' if asymmetric else ''}: "
+          f"batch {B}, context {N}", flush=True)
     pages = synth.pages_for(N)
     tier = synth.TIER_OF_BITS[bits]
     L = LayerPair(w.num_q_heads, w.num_kv_heads, w.head_dim, B, pages + 1, [[tier] * pages] * B,
-                  seed=w.config_id * 100 + layer)
+                  seed=w.config_id * 100 + layer, asymmetric=asymmetric)
     K, V = synth.keys_values(w, layer, N, synth.S_PREFILL_K, synth.S_PREFILL_V)
     L.write(K[:, :N - 1], V[:, :N - 1])                 # prefill in one call per layer
     k1, v1 = K[:, N - 1:].copy(), V[:, N - 1:].copy()
