@@ -43,8 +43,8 @@ ATTN_SRC = [os.path.join(ROOT, "mixed_precision_quantized_kv_amd", "csrc", f)
 # (FETCH_SIZE, WRITE_SIZE) scaled by the same counters' reading for a plain copy kernel of known
 # size. It describes the kernel sources with this digest only; after any change to them
 # the bench reports traffic as null until the counters are taken again.
-ATTN_TRAFFIC = {"source_sha256": "b2002cf902dc18fcbfc50c4110fc678ce82c4e522fa806371c07f56281d4cfc6",
-                "bytes_per_launch": 45360672,
+ATTN_TRAFFIC = {"source_sha256": "4e78593fb65c05944118036e95550e23721a7da9780cf0ebb0fc549fde2340e8",
+                "bytes_per_launch": 45372317,
                 # the bench's algorithmic bytes per launch at the counter run's contexts
                 "algorithmic_bytes_per_launch": 41804027}
 
