@@ -29,7 +29,7 @@ def step_fn(L, pos, k1, v1, ctx, q, ws, out, kl, rows, cws, pps):
     return run
 
 
-@pytest.mark.parametrize("case", ["tiny_int8", "ragged_mixed"])
+@pytest.mark.parametrize("case", ["tiny_int8", "ragged_mixed", "ragged_mixed_asymmetric"])
 def test_graph_replays_match_eager(case):
     print(f"\n[case] graph {case}", flush=True)
     g = np.random.default_rng(7)
@@ -38,7 +38,8 @@ def test_graph_replays_match_eager(case):
     else:
         hq, hkv, d, lens, pps = 32, 8, 128, [300, 1000, 777], 16
         tiers = [list(g.integers(0, 3, size=66)) for _ in lens]
-    L = LayerPair(hq, hkv, d, len(lens), 66 if case != "tiny_int8" else 20, tiers, seed=3)
+    L = LayerPair(hq, hkv, d, len(lens), 66 if case != "tiny_int8" else 20, tiers, seed=3,
+                  asymmetric=case.endswith("asymmetric"))
     for s, n in enumerate(lens):
         K = synth.normal_f16(g, (1, n - 1, hkv, d))
         V = synth.normal_f16(g, (1, n - 1, hkv, d))
