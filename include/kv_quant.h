@@ -182,7 +182,8 @@ void      kv_controller_destroy(kv_controller* c);
  * For every page touched, the K scales and codes of all its present tokens are recomputed from
  * their FP16 originals (ring for positions < pos, k_new after), so writing token by token gives
  * the same bytes as writing at once. Each new value vector gets its own scale; codes of earlier
- * tokens are kept. Afterwards the ring holds the new keys. n_new == 0 is a no-op. */
+ * tokens are kept. Afterwards the ring holds the new keys. n_new == 0 is a no-op. A geometry
+ * with asymmetric = 1 writes the asymmetric format (a zero point and a scale per group). */
 kv_status kv_quant_write(const kv_geometry* g, const kv_layer_pools* pools, const uint32_t* bt,
                          const int32_t* pos, int batch, int n_new, const uint16_t* k_new,
                          const uint16_t* v_new, uint16_t* ring, void* stream);
@@ -193,7 +194,8 @@ kv_status kv_quant_write(const kv_geometry* g, const kv_layer_pools* pools, cons
  * h reads KV head h / (H_q/H_kv).
  *   out[s][h][:] = sum_t w_t V^_t / sum_t w_t,  w_t = exp(l_t - max l),
  *   l_t = softmax_scale * sum_c q[s][h][c] K^_t[c],  t in [0, ctx_len[s]),
- *   K^_t[c] = code * K scale of (page of t, c),  V^_t[c] = code * V scale of t.
+ *   K^_t[c] = code * K scale of (page of t, c),  V^_t[c] = code * V scale of t
+ *   (asymmetric format: zero point + code * scale, with the same groups).
  *   ctx_len  dev int32 [batch], each in [0, max_ctx_len]; a zero length gives a zero row
  *   q        dev fp16 [batch][H_q][D] (4-byte aligned);  out  dev fp32 [batch][H_q][D] (16-byte aligned)
  *   max_ctx_len    host upper bound on ctx_len, sizes the launch (<= max_pages_per_seq * P)
