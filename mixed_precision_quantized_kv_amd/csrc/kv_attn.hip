@@ -27,6 +27,12 @@
 // KV head) to finish -- found with an atomic ticket -- combines the partials in split order, so
 // results do not depend on scheduling. Split s and group g map to blockIdx s * groups + g, which
 // keeps all splits of a group on one XCD when groups % 8 == 0.
+//
+// The asymmetric format (ASYM; EchoKV, "Future work": per-token KIVI storage) adds a zero point
+// m beside every scale: a logit over m + u*s is the zero-point part sum_c q_c m_c -- four more
+// MFMAs per page with the zero points in every row of the A operand against q itself, exact in
+// fp32 -- plus the code part on the unsigned codes u; the value side adds sum_t p_t m_t, one
+// number per head, to every channel of the head after the loop.
 #include "kvq_device.hpp"
 #include "kvq_launch.hpp"
 #include "kvq_write_dev.hpp"
@@ -1287,7 +1293,8 @@ __device__ __forceinline__ void wave_chunk_fast(const uint8_t* base, uint32_t hv
     }
 }
 
-// HALF: the group has at most 8 query heads (see process_pair_half). FUSED: the kernel first
+// HALF: the group has at most 8 query heads (see process_pair_half). ASYM: the asymmetric
+// storage format. FUSED: the kernel first
 // writes the step's new tokens (at most 64 per sequence, so at most five pages): the workgroup
 // whose split holds a touched page quantizes it (256 threads a page, two pages at a time) and,
 // for the first page, updates the ring, then makes its writes visible to its own loads and
@@ -1305,7 +1312,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_attn_kernel(const uint32_t
                                                                   AttnArgs a) {
     // the K scales of a pair's pages (ASYM: then their zero points), staged per wave
     __shared__ __attribute__((aligned(16))) uint32_t lds_ks[kWaves][ASYM ? 4 : 2][64];
-    // the K scales of the uniform-width loop's page pairs, staged per wave (stage_kscale)
+    // the K scales (ASYM: then the zero points) of the uniform-width loop's page pairs, staged
+    // per wave (stage_kscale)
     __shared__ __attribute__((aligned(16))) uint32_t lds_ksr[kWaves][(ASYM ? 4 : 2) * kKsSlot<D>];
     // per-wave partials, one padded row per head: channel c of head h sits at h*kORow + c +
     // 4*(c/32), so the float4 writes of a wave's 64 lanes (16 heads x 4 channel quarters) spread
