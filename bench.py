@@ -43,8 +43,8 @@ ATTN_SRC = [os.path.join(ROOT, "mixed_precision_quantized_kv_amd", "csrc", f)
 # (FETCH_SIZE, WRITE_SIZE) scaled by the same counters' reading for a plain copy kernel of known
 # size. It describes the kernel sources with this digest only; after any change to them
 # the bench reports traffic as null until the counters are taken again.
-ATTN_TRAFFIC = {"source_sha256": "4e78593fb65c05944118036e95550e23721a7da9780cf0ebb0fc549fde2340e8",
-                "bytes_per_launch": 45372317,
+ATTN_TRAFFIC = {"source_sha256": "e67f8a86712c139e65774a47ccd39a255ca36915d7cfd4b552ca4f56cf707282",
+                "bytes_per_launch": 45371011,
                 # the bench's algorithmic bytes per launch at the counter run's contexts
                 "algorithmic_bytes_per_launch": 41804027}
 
@@ -415,6 +415,8 @@ def run(args):
                                          if traffic else None),
         },
         "hbm_probes": probes,
+        # the same achieved rate against what a plain streaming sum over 4 GiB reaches on this GPU
+        "frac_of_sum_probe": round(achieved / probes["sum_4GiB_GBps"], 4),
         "attn_source_sha256": source_digest(ATTN_SRC),
         "setup_s": round(r["setup_s"], 1),
     }
