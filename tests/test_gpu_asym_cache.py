@@ -100,19 +100,20 @@ def test_attention_14b_shape(tier):
         assert L.tickets_zero(ws)
 
 
-def test_attention_wide_group_mixed_widths_and_fp16():
+@pytest.mark.parametrize("d", [128, 64])
+def test_attention_wide_group_mixed_widths_and_fp16(d):
     """a 16-head group (the two-page-per-tile layout does not apply), pages striped over INT8,
     INT2, FP16 and INT4, two sequences of different lengths"""
-    banner("group 16, striped widths")
+    banner(f"group 16, striped widths, D {d}")
     widths = [2, 0, 3, 1, 0, 2, 1, 3, 0, 1, 2, 0]
-    L = LayerPair(32, 2, 128, 2, 14, [widths, widths[::-1]], seed=5, asymmetric=True)
+    L = LayerPair(32, 2, d, 2, 14, [widths, widths[::-1]], seed=5, asymmetric=True)
     rng = np.random.default_rng(5)
-    K, V = kv_inputs(rng, 2, 190, 2, 128)
+    K, V = kv_inputs(rng, 2, 190, 2, d)
     L.write(K[:, :150], V[:, :150])
     L.write(K[:1, 150:190], V[:1, 150:190], rows=[0])
     bad, ring_ok = L.compare_bytes()
     assert not bad and ring_ok
-    q = synth.normal_f16(rng, (2, 32, 128))
+    q = synth.normal_f16(rng, (2, 32, d))
     ref = L.oracle_attn(q)
     for pps in (0, 2, 4):
         got, _ = L.attn(q, pages_per_split=pps)
