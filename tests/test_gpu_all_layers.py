@@ -8,6 +8,8 @@ block and the ring are compared bit for bit with the oracle and every attention 
 (per row: max |err| / max |ref|). The one-layer-per-width cases of test_gpu_fullsize.py add the
 two-launch comparison, the other split plans and the canary.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -54,3 +56,19 @@ def test_layer_decode_step(name, layer, bits):
     print(f"  blocks {len(L.used_blocks())} bit-exact; rows {err.size}: max rel err {err.max():.3e}",
           flush=True)
     assert err.max() <= ATTN_TOL, (err.max(), np.unravel_index(np.argmax(err), err.shape))
+
+
+BATCHED = synth.WORKLOADS["qwen7b_batched"]
+BATCHED_CASES = list(zip(range(BATCHED.num_layers), synth.layer_bits(BATCHED),
+                         synth.layer_bits(BATCHED, redraw=1)))
+
+
+@pytest.mark.skipif(os.environ.get("KVQ_ALL_LAYERS") != "1",
+                    reason="every layer of the batched shape takes ~10 minutes; KVQ_ALL_LAYERS=1 runs it")
+@pytest.mark.parametrize("layer,b0,b1", BATCHED_CASES,
+                         ids=[f"qwen7b_batched-L{l}-int{a}-int{b}" for l, a, b in BATCHED_CASES])
+def test_batched_layer(layer, b0, b1):
+    """every layer of the batched 7B shape: 64 ragged sequences, two steps of 64 new tokens with
+    the layer's mid-run redraw between them (test_gpu_fullsize.batched_layer)"""
+    from test_gpu_fullsize import batched_layer
+    batched_layer(BATCHED, layer, b0, b1)

@@ -131,6 +131,12 @@ def test_batched_ragged_tier_switch():
     switch come from the new pool, blocks written before it stay byte-identical"""
     w = synth.WORKLOADS["qwen7b_batched"]
     layer, b0, b1 = switching_layer(w)
+    batched_layer(w, layer, b0, b1)
+
+
+def batched_layer(w, layer, b0, b1):
+    """the two steps of the batched workload on one layer whose width is b0 before the mid-run
+    redraw and b1 after it (b0 == b1: no switch)"""
     t0, t1 = synth.TIER_OF_BITS[b0], synth.TIER_OF_BITS[b1]
     lens = synth.seq_lengths(w)                         # tokens at the first step's attention
     B, nn = w.batch, w.new_tokens
