@@ -58,6 +58,15 @@ def test_geometry_validation(kw, status):
     assert kvq.lib().kv_last_error().decode()
 
 
+def test_format_flag_validation():
+    g = geom()
+    g.asymmetric = 2                      # the C struct field, past the binding's normalisation
+    with pytest.raises(kvq.KVError) as e:
+        kvq.kv_validate(g)
+    assert e.value.status == kvq.KV_EINVAL and "asymmetric" in kvq.lib().kv_last_error().decode()
+    assert kvq.kv_block_bytes(g, 4) == 0
+
+
 def test_sizes_match_format():
     g = geom(head_dim=128, num_q_heads=40, num_kv_heads=8)
     # S_b = P*D*b/4 + 2D + 2P per KV head; the FP16 tier 4*P*D (keys and values, no scales)
@@ -74,10 +83,19 @@ def test_sizes_match_format():
     assert kvq.kv_cache_bytes_per_token(g, [16, 16]) == 2 * kvq.kv_block_bytes(g, 16) / 16
 
 
-def test_sizes_agree_with_oracle(orc):
+def test_sizes_asymmetric_format():
+    g = geom(head_dim=128, num_q_heads=40, num_kv_heads=8, asymmetric=True)
+    # S_b = P*D*b/4 + 4D + 4P: a zero point beside every scale; the FP16 tier unchanged
+    assert [kvq.kv_block_bytes(g, b) for b in (2, 4, 8)] == [8 * 1600, 8 * 2624, 8 * 4672]
+    assert kvq.kv_block_bytes(g, 16) == 8 * 4 * 16 * 128
+    assert kvq.kv_cache_bytes_per_token(g, [2, 8]) == 8 * (1600 + 4672) / 16
+
+
+@pytest.mark.parametrize("asym", [False, True])
+def test_sizes_agree_with_oracle(orc, asym):
     for hq, hkv, d in ((8, 2, 64), (40, 8, 128), (28, 4, 128)):
-        g = geom(num_q_heads=hq, num_kv_heads=hkv, head_dim=d)
-        og = orc.geom(hq, hkv, d)
+        g = geom(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, asymmetric=asym)
+        og = orc.geom(hq, hkv, d, asymmetric=asym)
         for b in (2, 4, 8, 16):
             assert kvq.kv_block_bytes(g, b) == orc.block_bytes(og, b)
         bits = [2, 16]
