@@ -276,7 +276,8 @@ int       kv_decode_step_pages_per_split_for(const kv_geometry* g, int batch, co
  * summed over keys, averaged over queries; one number per b in {2, 4, 8}. K_ref is the ring:
  * for each sequence the n = min(seq_len[s], R) newest keys (positions seq_len-n .. seq_len-1).
  * quant_b is the cache's own quantizer, grouped by each key's page (one scale per page and
- * channel); the copies are temporary. Rows use the softmax_scale of attention.
+ * channel): the symmetric one, or the asymmetric one (as kv_canary_kl_asym) for a geometry with
+ * asymmetric = 1; the copies are temporary. Rows use the softmax_scale of attention.
  *   ring     dev fp16 [max_seqs][R][H_kv][D] (16-byte aligned);  seq_len dev int32 [batch], >= 0
  *   q        dev fp16 [batch][H_q][D] (16-byte aligned)
  *   kl_out   dev fp32 [3]: mean over batch*H_q rows for b = 2, 4, 8

@@ -568,8 +568,9 @@ static kv_status canary(const kv_geometry* g, const uint16_t* ring, const int32_
 kv_status kv_canary_kl(const kv_geometry* g, const uint16_t* ring, const int32_t* seq_len,
                        int batch, const uint16_t* q, float softmax_scale, float* kl_out,
                        float* kl_rows, void* workspace, size_t workspace_bytes, void* stream) {
-    return canary(g, ring, seq_len, batch, q, softmax_scale, false, kl_out, kl_rows, workspace,
-                  workspace_bytes, stream, "kv_canary_kl");
+    // the cache's own quantizer: the asymmetric copies for a geometry in the asymmetric format
+    return canary(g, ring, seq_len, batch, q, softmax_scale, g && g->asymmetric == 1, kl_out,
+                  kl_rows, workspace, workspace_bytes, stream, "kv_canary_kl");
 }
 
 kv_status kv_canary_kl_layers(const kv_geometry* g, int num_layers, const uint16_t* const* rings,

@@ -22,6 +22,8 @@
 // instance builds the copies that way, over the same groups: zero point = the group minimum m, scale
 // s = RU16((max - m) / (2^b - 1)), code = round-half-even((x - m) / s) in [0, 2^b - 1], value
 // m + code * s. These decisions are taken in binary64, where they are exact for fp16 inputs.
+// kv_canary_kl and kv_canary_kl_layers build the copies with the cache's own quantizer: the
+// symmetric one, or the asymmetric one for a geometry in the asymmetric storage format.
 #include "kvq_device.hpp"
 #include "kvq_launch.hpp"
 
@@ -325,10 +327,12 @@ hipError_t launch_canary_layers(const kv_geometry& g, int num_layers,
     for (int l = 0; l < kMaxCanaryLayers; ++l)
         a.layer[l] = l < num_layers ? CanaryLayer{rings[l], q[l]} : CanaryLayer{nullptr, nullptr};
     const int D = g.head_dim;
-    const size_t lds = canary_lds_bytes(a.R, D, false);
+    const bool asym = g.asymmetric != 0;          // the cache's own quantizer
+    const size_t lds = canary_lds_bytes(a.R, D, asym);
     dim3 grid((unsigned)(batch * g.num_kv_heads), 3u, (unsigned)num_layers);
-    if (D == 128) return launch_one<128, false>(a, grid, lds, stream);
-    return launch_one<64, false>(a, grid, lds, stream);
+    if (D == 128) return asym ? launch_one<128, true>(a, grid, lds, stream)
+                              : launch_one<128, false>(a, grid, lds, stream);
+    return asym ? launch_one<64, true>(a, grid, lds, stream) : launch_one<64, false>(a, grid, lds, stream);
 }
 
 }  // namespace kvq

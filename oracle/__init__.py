@@ -243,7 +243,11 @@ def decode_attn_row(g: Geom, pools: Pools, bt_row: np.ndarray, ctx_len: int, q_r
 
 
 def canary_kl(g: Geom, ring: np.ndarray, seq_len: np.ndarray, q: np.ndarray,
-              softmax_scale: float, asymmetric: bool = False):
+              softmax_scale: float, asymmetric=None):
+    """asymmetric None: the cache's own quantizer (the geometry's format); True / False force
+    the asymmetric or the symmetric copies"""
+    if asymmetric is None:
+        asymmetric = bool(g.asymmetric)
     ring = np.ascontiguousarray(ring, dtype=np.uint16)
     seq_len = np.ascontiguousarray(seq_len, dtype=np.int32)
     q = np.ascontiguousarray(q, dtype=np.uint16)

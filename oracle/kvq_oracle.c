@@ -470,7 +470,8 @@ double orc_kl_logits(const double* l, const double* m, int n) {
 
 void orc_canary_kl(const orc_geom* g, const uint16_t* ring, const int32_t* seq_len, int batch,
                    const uint16_t* q, float softmax_scale, double* kl3, double* rows) {
-    orc_canary_kl_mode(g, ring, seq_len, batch, q, softmax_scale, 0, kl3, rows);
+    /* the cache's own quantizer: asymmetric copies for a geometry in the asymmetric format */
+    orc_canary_kl_mode(g, ring, seq_len, batch, q, softmax_scale, g->asymmetric != 0, kl3, rows);
 }
 
 void orc_canary_kl_mode(const orc_geom* g, const uint16_t* ring, const int32_t* seq_len, int batch,

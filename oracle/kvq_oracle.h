@@ -119,7 +119,8 @@ int orc_decode_attn_row(const orc_geom* g, uint8_t* const pools[4], const uint32
                         int ctx_len, const uint16_t* q_row, int h, float softmax_scale, double* out);
 
 /* ---- canary: kl3[b] = mean over batch*H_q rows of KL(P_ref || P_b), b = 2,4,8;
- * rows (optional) [batch][H_q][3]. ring [batch][R][H_kv][D]; q [batch][H_q][D]. */
+ * rows (optional) [batch][H_q][3]. ring [batch][R][H_kv][D]; q [batch][H_q][D]. The copies are
+ * built with the cache's own quantizer (asymmetric when g->asymmetric). */
 void orc_canary_kl(const orc_geom* g, const uint16_t* ring, const int32_t* seq_len, int batch,
                    const uint16_t* q, float softmax_scale, double* kl3, double* rows);
 /* the same with the temporary copies built by the asymmetric quantizer when asymmetric != 0

@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import mixed_precision_quantized_kv_amd as kvq
+import oracle
 from mixed_precision_quantized_kv_amd import synth
 
 from gpu_cases import DEV, LayerPair, rowwise_rel_err, to_dev_f16, to_dev_i32
@@ -181,3 +182,41 @@ def test_fused_step_equals_write_then_attention(n_new):
                                float(np.float32(1 / math.sqrt(128))), out)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().astype(np.float64), rows_fused)
+
+
+def test_canary_uses_the_cache_quantizer():
+    """on a geometry in the asymmetric format the canary builds asymmetric copies: kv_canary_kl
+    equals kv_canary_kl_asym bit for bit and the oracle's asymmetric canary within 1e-4, and the
+    one-launch firing over several layers equals the single-layer calls"""
+    banner("canary follows the format")
+    L = LayerPair(10, 2, 128, 3, 12, [[1] * 10] * 3, seed=11, asymmetric=True)
+    rng = np.random.default_rng(11)
+    K, V = kv_inputs(rng, 3, 150, 2, 128)
+    for s, n in enumerate((150, 40, 97)):
+        L.write(K[s:s + 1, :n], V[s:s + 1, :n], rows=[s])
+    q = synth.normal_f16(rng, (3, 10, 128))
+    kl, rows = L.canary(q)
+    okl, orows = L.oracle_canary(q)
+    assert np.abs(kl - okl).max() <= 1e-4 and np.abs(rows - orows).max() <= 1e-4
+    scale = float(np.float32(1 / math.sqrt(128)))
+    wsb = kvq.kv_canary_workspace_bytes(L.g, 3)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    ka = torch.zeros(3, dtype=torch.float32, device=DEV)
+    ra = torch.zeros((3, 10, 3), dtype=torch.float32, device=DEV)
+    seq = to_dev_i32(L.len)
+    kvq.kv_canary_kl_asym(L.g, L.ring, seq, 3, to_dev_f16(q), scale, ka, ra, ws, wsb)
+    torch.cuda.synchronize()
+    assert np.array_equal(ka.cpu().numpy().astype(np.float64), kl)
+    assert np.array_equal(ra.cpu().numpy().astype(np.float64), rows)
+    # the symmetric copies differ (the format matters)
+    sk, _ = oracle.canary_kl(L.og, L.oring, L.len, q, np.float32(scale), asymmetric=False)
+    assert np.abs(sk - okl).max() > 1e-6
+    # one launch for two layers (the same ring and queries twice) equals the single calls
+    g2 = kvq.geometry(2, 10, 2, 128, 3, 12, asymmetric=True)
+    lwsb = kvq.kv_canary_layers_workspace_bytes(g2, 2, 3)
+    lws = torch.zeros(lwsb, dtype=torch.uint8, device=DEV)
+    kl2 = torch.zeros((2, 3), dtype=torch.float32, device=DEV)
+    qd = to_dev_f16(q)
+    kvq.kv_canary_kl_layers(g2, [L.ring, L.ring], seq, 3, [qd, qd], scale, kl2, None, lws, lwsb)
+    torch.cuda.synchronize()
+    assert np.array_equal(kl2.cpu().numpy().astype(np.float64), np.stack([kl, kl]))
