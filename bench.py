@@ -547,8 +547,8 @@ def cpu_baseline(w, bits, n_layers: int, reps: int, step_bytes: float) -> dict:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported "
-                                   "(multi-GPU sharding is a design note only)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus above 1 is not supported "
+                                   "(sharding over GPUs is not implemented)", "n_gpus": args.gpus}))
         sys.exit(2)
     run(args)
 
