@@ -124,7 +124,7 @@ int orc_decode_attn_row(const orc_geom* g, uint8_t* const pools[4], const uint32
 void orc_canary_kl(const orc_geom* g, const uint16_t* ring, const int32_t* seq_len, int batch,
                    const uint16_t* q, float softmax_scale, double* kl3, double* rows);
 /* the same with the temporary copies built by the asymmetric quantizer when asymmetric != 0
- * (EchoKV names its canary quantizer "KIVI-style asymmetric per-group"); same groups */
+ * (EchoKV describes its canary quantizer as asymmetric per group, after KIVI); same groups */
 void orc_canary_kl_mode(const orc_geom* g, const uint16_t* ring, const int32_t* seq_len, int batch,
                         const uint16_t* q, float softmax_scale, int asymmetric, double* kl3,
                         double* rows);

@@ -1,7 +1,7 @@
 """Pins for the oracle's asymmetric (KIVI-style) quantizer and the canary built on it.
 
-EchoKV, "Show the math - what the canary actually computes": the canary's quant_b is "KIVI-style
-asymmetric per-group" quantization -- per group a zero point and a scale spanning [min, max].
+EchoKV, "Show the math - what the canary actually computes": the canary's quant_b quantizes each
+group asymmetrically, after KIVI -- per group a zero point and a scale spanning [min, max].
 The oracle's reading: zero point = the group minimum m, scale s = RU16((max - m) / (2^b - 1)),
 codes round-half-even((x - m) / s) in [0, 2^b - 1], value m + code * s.
 
