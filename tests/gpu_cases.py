@@ -34,7 +34,7 @@ class LayerPair:
     """One layer: GPU pools + ring (via libkvq) and oracle pools + ring, same block table."""
 
     def __init__(self, hq, hkv, d, batch, max_pages, page_tiers, capacity=None, seed=0, R=64,
-                 asymmetric=False):
+                 asymmetric=False, fill=0):
         self.hq, self.hkv, self.d, self.batch, self.R = hq, hkv, d, batch, R
         self.g = kvq.geometry(1, hq, hkv, d, batch, max_pages, ring_size=R, asymmetric=asymmetric)
         self.og = oracle.geom(hq, hkv, d, 16, R, asymmetric=asymmetric)
@@ -43,8 +43,10 @@ class LayerPair:
         self.capacity = list(capacity)
         self.bt = synth.block_table(page_tiers, max_pages, self.capacity,
                                     np.random.default_rng(seed + 1000))
-        self.pools_t = [torch.zeros(max(16, c * kvq.kv_block_bytes(self.g, b)), dtype=torch.uint8,
-                                    device=DEV) for c, b in zip(self.capacity, kvq.TIER_BITS)]
+        # fill: the byte the GPU pools start with (the oracle's start at zero); a fill other than 0
+        # leaves those bytes in every slot no token has been written to yet
+        self.pools_t = [torch.full((max(16, c * kvq.kv_block_bytes(self.g, b)),), fill, dtype=torch.uint8,
+                                   device=DEV) for c, b in zip(self.capacity, kvq.TIER_BITS)]
         self.pools = kvq.layer_pools(self.pools_t, self.capacity)
         self.bt_dev = to_dev_i32(self.bt)
         self.ring = torch.zeros((batch, R, hkv, d), dtype=torch.float16, device=DEV)
