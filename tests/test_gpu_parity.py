@@ -243,6 +243,7 @@ def test_workspace_reused_across_batch_sizes():
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
     for b in (2, B, 2, B):
         assert np.array_equal(call(b, ws), fresh[b]), b
+    assert not ws.any()                             # every ticket counter is left at zero
 
 
 def test_softmax_scale_zero_and_identical_keys():
@@ -256,3 +257,35 @@ def test_softmax_scale_zero_and_identical_keys():
     for scale in (0.0, 0.125, 3.0):
         got, _ = L.attn(q, scale=scale)
         assert rowwise_rel_err(got, L.oracle_attn(q, scale=scale)).max() <= ATTN_TOL
+
+
+@pytest.mark.parametrize("zero_values", [True, False])
+def test_split_partials_that_are_exactly_zero(zero_values):
+    """split partials whose running maximum is exactly +0.0 (every logit -3 in log2 units, the
+    lazy maximum's margin above it) and, with zero values, whose accumulators are +0.0 too, at
+    32 and 8 splits: the merge takes them like any other (zero rows, or the mean of the values).
+    INT2 keys [-1, 0, ..., 0] quantize exactly (scale 1), so q . k = -1 exactly."""
+    case_banner(f"exactly-zero split partials, zero values {zero_values}")
+    N, hq, hkv, d = 2000, 8, 2, 64
+    pages = synth.pages_for(N)
+    K = np.zeros((1, N, hkv, d), dtype=np.float16)
+    K[..., 0] = -1.0
+    g = np.random.default_rng(77)
+    V = np.zeros((1, N, hkv, d), dtype=np.float16) if zero_values else \
+        g.standard_normal((1, N, hkv, d)).astype(np.float16)
+    L = LayerPair(hq, hkv, d, 1, pages + 2, [[0] * pages], seed=77)
+    L.write(K.view(np.uint16), V.view(np.uint16))
+    qf = np.zeros((1, hq, d), dtype=np.float16)
+    qf[..., 0] = 1.0
+    q = qf.view(np.uint16)
+    scale = float(np.float32(3 / 1.4426950408889634))
+    assert np.float32(scale) * np.float32(1.4426950408889634) == np.float32(3.0)
+    ref = L.oracle_attn(q, scale=scale)
+    for pps in (4, 16):
+        got, ws = L.attn(q, scale=scale, pages_per_split=pps)
+        assert np.isfinite(got).all(), pps
+        if zero_values:
+            assert not got.any(), pps
+        else:
+            assert rowwise_rel_err(got, ref).max() <= ATTN_TOL, pps
+        assert L.tickets_zero(ws), pps
