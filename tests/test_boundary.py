@@ -125,6 +125,12 @@ def test_kernel_calls_reject_bad_arguments_without_launching():
     with pytest.raises(kvq.KVError):
         kvq.kv_canary_kl(g, 256, 256, 1, 256, 0.1, 256, None, 256, 4, stream=0)
     kvq.kv_quant_write(g, pools, 0, 0, 1, 0, 0, 0, 0, stream=0)   # n_new == 0: a no-op
+    g600 = kvq.geometry(1, 8, 2, 64, 1, 600)
+    ctx = 513 * 16                                  # 513 pages at 2 per split: 257 splits
+    wsb = kvq.kv_decode_workspace_bytes(g600, 1, ctx, 2)
+    with pytest.raises(kvq.KVError) as e:           # past the limit of 256 splits
+        kvq.kv_decode_attn(g600, pools, 256, 256, 1, ctx, 256, 0.1, 256, 256, wsb, 2, stream=0)
+    assert e.value.status == kvq.KV_EINVAL and "257 splits" in str(e.value)
 
 
 def test_canary_layers_validation_and_workspace():

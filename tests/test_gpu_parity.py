@@ -289,3 +289,26 @@ def test_split_partials_that_are_exactly_zero(zero_values):
         else:
             assert rowwise_rel_err(got, ref).max() <= ATTN_TOL, pps
         assert L.tickets_zero(ws), pps
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(40, 8, 128), (8, 2, 64)])
+@pytest.mark.parametrize("mix", ["int4", "mixed"])
+def test_split_counts_up_to_the_limit(hq, hkv, d, mix):
+    """the merge at its widest: 512 pages of one sequence at 2 pages per split give the limit of
+    256 splits (the (max, sum) pairs take four lanes' rounds, the partials several batches of a
+    lane's run), 4 give 128, and 6 give 86 (a ragged last batch)"""
+    case_banner(f"split-count limit hq={hq} hkv={hkv} d={d} {mix}")
+    g = np.random.default_rng(d + len(mix))
+    N = 512 * 16
+    pages = synth.pages_for(N)
+    tiers = [list(g.integers(0, 4, size=pages))] if mix == "mixed" else [[1] * pages]
+    L = LayerPair(hq, hkv, d, 1, pages, tiers, seed=d + 7)
+    L.write(synth.normal_f16(g, (1, N, hkv, d)), synth.normal_f16(g, (1, N, hkv, d)))
+    q = synth.normal_f16(g, (1, hq, d))
+    ref = L.oracle_attn(q)
+    for pps in (2, 4, 6):
+        got, ws = L.attn(q, pages_per_split=pps)
+        err = rowwise_rel_err(got, ref)
+        print(f"  attn pps={pps} splits={-(-pages // pps)} max rel err {err.max():.3e}")
+        assert err.max() <= ATTN_TOL, (pps, err.max())
+        assert L.tickets_zero(ws), pps
