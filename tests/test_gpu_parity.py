@@ -243,7 +243,7 @@ def test_workspace_reused_across_batch_sizes():
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
     for b in (2, B, 2, B):
         assert np.array_equal(call(b, ws), fresh[b]), b
-    assert not ws.any()                             # every ticket counter is left at zero
+    assert L.tickets_zero(ws)                       # every ticket counter is left at zero
 
 
 def test_softmax_scale_zero_and_identical_keys():
