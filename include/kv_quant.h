@@ -182,8 +182,9 @@ void      kv_controller_destroy(kv_controller* c);
  * For every page touched, the K scales and codes of all its present tokens are recomputed from
  * their FP16 originals (ring for positions < pos, k_new after), so writing token by token gives
  * the same bytes as writing at once. Each new value vector gets its own scale; codes of earlier
- * tokens are kept. Afterwards the ring holds the new keys. n_new == 0 is a no-op. A geometry
- * with asymmetric = 1 writes the asymmetric format (a zero point and a scale per group). */
+ * tokens are kept. Afterwards the ring holds the new keys. batch is 0 .. max_seqs; batch == 0
+ * or n_new == 0 is a no-op. A geometry with asymmetric = 1 writes the asymmetric format (a zero
+ * point and a scale per group). */
 kv_status kv_quant_write(const kv_geometry* g, const kv_layer_pools* pools, const uint32_t* bt,
                          const int32_t* pos, int batch, int n_new, const uint16_t* k_new,
                          const uint16_t* v_new, uint16_t* ring, void* stream);
@@ -196,7 +197,8 @@ kv_status kv_quant_write(const kv_geometry* g, const kv_layer_pools* pools, cons
  *   l_t = softmax_scale * sum_c q[s][h][c] K^_t[c],  t in [0, ctx_len[s]),
  *   K^_t[c] = code * K scale of (page of t, c),  V^_t[c] = code * V scale of t
  *   (asymmetric format: zero point + code * scale, with the same groups).
- *   ctx_len  dev int32 [batch], each in [0, max_ctx_len]; a zero length gives a zero row
+ *   batch    1 .. max_seqs (rows 0..batch-1 of bt and ctx_len); 0 is KV_EINVAL
+*   ctx_len  dev int32 [batch], each in [0, max_ctx_len]; a zero length gives a zero row
  *   q        dev fp16 [batch][H_q][D] (4-byte aligned);  out  dev fp32 [batch][H_q][D] (16-byte aligned)
  *   max_ctx_len    host upper bound on ctx_len, sizes the launch (<= max_pages_per_seq * P)
  *   pages_per_split  pages one workgroup reads (even, >= 2); 0 = chosen by the library
@@ -278,6 +280,7 @@ int       kv_decode_step_pages_per_split_for(const kv_geometry* g, int batch, co
  * quant_b is the cache's own quantizer, grouped by each key's page (one scale per page and
  * channel): the symmetric one, or the asymmetric one (as kv_canary_kl_asym) for a geometry with
  * asymmetric = 1; the copies are temporary. Rows use the softmax_scale of attention.
+ *   batch    1 .. max_seqs (a mean over no rows is undefined); 0 is KV_EINVAL
  *   ring     dev fp16 [max_seqs][R][H_kv][D] (16-byte aligned);  seq_len dev int32 [batch], >= 0
  *   q        dev fp16 [batch][H_q][D] (16-byte aligned)
  *   kl_out   dev fp32 [3]: mean over batch*H_q rows for b = 2, 4, 8

@@ -125,6 +125,14 @@ def test_kernel_calls_reject_bad_arguments_without_launching():
     with pytest.raises(kvq.KVError):
         kvq.kv_canary_kl(g, 256, 256, 1, 256, 0.1, 256, None, 256, 4, stream=0)
     kvq.kv_quant_write(g, pools, 0, 0, 1, 0, 0, 0, 0, stream=0)   # n_new == 0: a no-op
+    kvq.kv_quant_write(g, pools, 0, 0, 0, 1, 0, 0, 0, stream=0)   # batch == 0: a no-op
+    for call in (lambda: kvq.kv_decode_attn(g, pools, 256, 256, 0, 16, 256, 0.1, 256, 256, 1 << 20, 0, stream=0),
+                 lambda: kvq.kv_decode_step(g, pools, 256, 256, 0, 1, 256, 256, 256, 16, 256, 0.1, 256, 256,
+                                            1 << 20, 0, stream=0),
+                 lambda: kvq.kv_canary_kl(g, 256, 256, 0, 256, 0.1, 256, None, 256, 1 << 16, stream=0)):
+        with pytest.raises(kvq.KVError) as e:       # attention and canary take 1..max_seqs rows
+            call()
+        assert e.value.status == kvq.KV_EINVAL and "batch 0" in str(e.value)
     g600 = kvq.geometry(1, 8, 2, 64, 1, 600)
     ctx = 513 * 16                                  # 513 pages at 2 per split: 257 splits
     wsb = kvq.kv_decode_workspace_bytes(g600, 1, ctx, 2)
