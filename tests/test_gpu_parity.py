@@ -312,3 +312,39 @@ def test_split_counts_up_to_the_limit(hq, hkv, d, mix):
         print(f"  attn pps={pps} splits={-(-pages // pps)} max rel err {err.max():.3e}")
         assert err.max() <= ATTN_TOL, (pps, err.max())
         assert L.tickets_zero(ws), pps
+
+
+@pytest.mark.parametrize("R", [16, 48, 128])
+@pytest.mark.parametrize("d", [64, 128])
+def test_ring_sizes(R, d):
+    """the ring at the sizes the geometry allows besides 64: the write reads an open page's
+    earlier keys from it (token by token, and in chunks longer than the ring), the canary
+    quantizes its newest min(N, R) keys (the oldest fragment of a page included); bytes, ring,
+    attention and canary against the oracle"""
+    case_banner(f"ring R={R} d={d}")
+    g = np.random.default_rng(R + d)
+    lens = [3, 37, 150]
+    max_pages = synth.pages_for(max(lens)) + 1
+    tiers = [list(g.integers(0, 3, size=max_pages)) for _ in lens]
+    L = LayerPair(8, 2, d, len(lens), max_pages, tiers, seed=R + d, R=R)
+    for s, n in enumerate(lens):
+        K = synth.normal_f16(g, (1, n, 2, d), np.where(np.arange(d) % 5 == 0, 8, 1).astype(np.float32))
+        V = synth.normal_f16(g, (1, n, 2, d))
+        p = 0
+        for step in (1, 1, 1, 17, R + 5, 2 * R + 1):        # single tokens, then chunks past R
+            m = min(step, n - p)
+            if m <= 0:
+                break
+            L.write(K[:, p:p + m], V[:, p:p + m], rows=[s])
+            p += m
+        if p < n:
+            L.write(K[:, p:n], V[:, p:n], rows=[s])
+    bad, ring_ok = L.compare_bytes()
+    assert not bad and ring_ok, bad[:3]
+    q = synth.normal_f16(g, (len(lens), 8, d))
+    got, _ = L.attn(q)
+    assert rowwise_rel_err(got, L.oracle_attn(q)).max() <= ATTN_TOL
+    kl, rows = L.canary(q)
+    okl, orows = L.oracle_canary(q)
+    print(f"  canary {kl} oracle {okl}")
+    assert np.abs(kl - okl).max() <= KL_TOL and np.abs(rows - orows).max() <= KL_TOL
