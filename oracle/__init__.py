@@ -144,8 +144,15 @@ def quantize_group_asym(x_bits: np.ndarray, bits: int):
     return int(scale[0]), int(zero[0]), codes
 
 
+def _whole_words(n: int, bits: int) -> None:
+    # the format packs codes into 32-bit words (32 / bits codes a word)
+    if n % (32 // bits):
+        raise ValueError(f"{n} codes of {bits} bits do not fill whole 32-bit words")
+
+
 def pack(q: np.ndarray, bits: int) -> np.ndarray:
     q = np.ascontiguousarray(q, dtype=np.int32)
+    _whole_words(q.size, bits)
     out = np.zeros(q.size * bits // 8, dtype=np.uint8)
     lib().orc_pack(_ptr(q), q.size, bits, _ptr(out))
     return out
@@ -153,6 +160,9 @@ def pack(q: np.ndarray, bits: int) -> np.ndarray:
 
 def unpack(b: np.ndarray, n: int, bits: int) -> np.ndarray:
     b = np.ascontiguousarray(b, dtype=np.uint8)
+    _whole_words(n, bits)
+    if b.size < n * bits // 8:
+        raise ValueError(f"{b.size} bytes hold fewer than {n} codes of {bits} bits")
     q = np.zeros(n, dtype=np.int32)
     lib().orc_unpack(_ptr(b), n, bits, _ptr(q))
     return q
