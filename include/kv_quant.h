@@ -110,6 +110,8 @@ double      kv_cache_bytes_per_token(const kv_geometry* g, const int* bits_per_l
  * to the right pool; "What happens to old blocks...": already-allocated blocks keep their
  * admit-time width). One pool per (layer, tier); each hands out its blocks in a seeded random
  * order (shuffled physical block tables). Not thread-safe; the library owns the object.
+ * The allocator and the controller below hold host memory only; a call that finds none left
+ * returns KV_EINVAL and changes nothing.
  * Block tables are host arrays bt_host[L][max_seqs][max_pages_per_seq] of handles; the caller
  * copies the rows it needs to the device (one [max_seqs][max_pages_per_seq] table per layer). */
 typedef struct kv_alloc kv_alloc;
@@ -124,14 +126,17 @@ kv_status kv_alloc_set_layer_bits(kv_alloc* a, int layer, int bits);
 /* grow sequence `seq` to new_len tokens in every layer (all-or-nothing: KV_ENOBLOCKS leaves
    the allocator and bt_host untouched); writes the new handles into bt_host */
 kv_status kv_alloc_extend(kv_alloc* a, int seq, int32_t new_len, uint32_t* bt_host);
-/* return every block of `seq` to its pool and reset its bt_host rows to KV_NO_BLOCK */
+/* return every block of `seq` to its pool and reset its bt_host rows to KV_NO_BLOCK; the
+   allocator keeps its own record of the handles it handed out and returns those, whatever
+   bt_host holds */
 kv_status kv_alloc_free_seq(kv_alloc* a, int seq, uint32_t* bt_host);
 int32_t   kv_alloc_seq_len(const kv_alloc* a, int seq);              /* -1 if seq invalid */
 int64_t   kv_alloc_free_blocks(const kv_alloc* a, int layer, int bits); /* -1 if invalid */
 int       kv_alloc_layer_bits(const kv_alloc* a, int layer);          /* 0 if invalid */
 void      kv_alloc_destroy(kv_alloc* a);
 /* CPU check of a host block table against the allocator: every page below the sequence
-   length holds a valid handle, no block is used twice, every other entry is KV_NO_BLOCK */
+   length holds the handle the allocator handed out for it (so no block appears twice), every
+   other entry is KV_NO_BLOCK */
 kv_status kv_check_block_table(const kv_alloc* a, const uint32_t* bt_host);
 
 /* ---------------------------------------------------------------- controller (host)

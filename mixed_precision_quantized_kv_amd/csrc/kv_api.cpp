@@ -153,6 +153,7 @@ struct kv_alloc {
     std::vector<int> bits;                       // current tier of each layer
     std::vector<uint32_t> capacity;              // [L][kTiers]
     std::vector<std::vector<uint32_t>> free;     // [L*kTiers]: free block indices, next at back
+    std::vector<std::vector<uint32_t>> owned;    // [L*max_seqs]: the handles handed out, by page
     std::vector<int32_t> len;                    // tokens per sequence
 };
 
@@ -216,19 +217,25 @@ kv_status kv_alloc_create(const kv_geometry* g, const uint32_t* capacity, const 
     }
     kv_alloc* a = new (std::nothrow) kv_alloc;
     if (!a) return fail(KV_EINVAL, "out of host memory");
-    a->g = *g;
-    a->bits.assign(bits, bits + g->num_layers);
-    a->capacity.assign(capacity, capacity + kTiers * g->num_layers);
-    a->free.resize(kTiers * (size_t)g->num_layers);
-    uint64_t x = shuffle_seed;
-    for (size_t i = 0; i < a->free.size(); ++i) {
-        std::vector<uint32_t>& f = a->free[i];
-        f.resize(a->capacity[i]);
-        for (uint32_t j = 0; j < a->capacity[i]; ++j) f[j] = j;
-        for (size_t j = f.size(); j > 1; --j) std::swap(f[j - 1], f[splitmix64(x) % j]);
-        std::reverse(f.begin(), f.end());     // handed out from the back
+    try {
+        a->g = *g;
+        a->bits.assign(bits, bits + g->num_layers);
+        a->capacity.assign(capacity, capacity + kTiers * g->num_layers);
+        a->free.resize(kTiers * (size_t)g->num_layers);
+        uint64_t x = shuffle_seed;
+        for (size_t i = 0; i < a->free.size(); ++i) {
+            std::vector<uint32_t>& f = a->free[i];
+            f.resize(a->capacity[i]);
+            for (uint32_t j = 0; j < a->capacity[i]; ++j) f[j] = j;
+            for (size_t j = f.size(); j > 1; --j) std::swap(f[j - 1], f[splitmix64(x) % j]);
+            std::reverse(f.begin(), f.end());     // handed out from the back
+        }
+        a->owned.resize((size_t)g->num_layers * g->max_seqs);
+        a->len.assign(g->max_seqs, 0);
+    } catch (const std::bad_alloc&) {
+        delete a;
+        return fail(KV_EINVAL, "out of host memory for the pools' free lists");
     }
-    a->len.assign(g->max_seqs, 0);
     *out = a;
     return ok();
 }
@@ -258,12 +265,20 @@ kv_status kv_alloc_extend(kv_alloc* a, int seq, int32_t new_len, uint32_t* bt) {
             return fail(KV_ENOBLOCKS, "layer %d: %lld free %d-bit blocks, %lld needed", l,
                         (long long)f.size(), a->bits[l], (long long)need);
     }
+    try {              // room for the new handles in every layer's record before anything moves
+        for (int l = 0; l < g.num_layers; ++l)
+            a->owned[(size_t)l * g.max_seqs + seq].reserve((size_t)new_pages);
+    } catch (const std::bad_alloc&) {
+        return fail(KV_EINVAL, "out of host memory");
+    }
     for (int l = 0; l < g.num_layers; ++l) {
         const int t = tier_of_bits(a->bits[l]);
         std::vector<uint32_t>& f = a->free[(size_t)l * kTiers + t];
+        std::vector<uint32_t>& mine = a->owned[(size_t)l * g.max_seqs + seq];
         uint32_t* row = bt + ((size_t)l * g.max_seqs + seq) * g.max_pages_per_seq;
         for (int64_t p = old_pages; p < new_pages; ++p) {
             row[p] = ((uint32_t)t << 30) | f.back();
+            mine.push_back(row[p]);
             f.pop_back();
         }
     }
@@ -275,16 +290,15 @@ kv_status kv_alloc_free_seq(kv_alloc* a, int seq, uint32_t* bt) {
     if (!a || !bt) return fail(KV_EINVAL, "NULL argument");
     const kv_geometry& g = a->g;
     if (seq < 0 || seq >= g.max_seqs) return fail(KV_EINVAL, "seq %d", seq);
-    const int64_t pages = (a->len[seq] + g.page_size - 1) / g.page_size;
+    // the blocks come back from the allocator's own record, whatever the table now holds, so
+    // an edited table cannot return a block twice; a pool's free list never outgrows the
+    // storage it was created with, so the returns allocate nothing
     for (int l = 0; l < g.num_layers; ++l) {
+        std::vector<uint32_t>& mine = a->owned[(size_t)l * g.max_seqs + seq];
+        for (const uint32_t h : mine)
+            a->free[(size_t)l * kTiers + (h >> 30)].push_back(h & 0x3fffffffu);
+        mine.clear();
         uint32_t* row = bt + ((size_t)l * g.max_seqs + seq) * g.max_pages_per_seq;
-        for (int64_t p = 0; p < pages; ++p) {
-            const uint32_t h = row[p];
-            if (h == KV_NO_BLOCK) continue;
-            const uint32_t t = h >> 30;
-            if (t < (uint32_t)kTiers && (h & 0x3fffffffu) < a->capacity[(size_t)l * kTiers + t])
-                a->free[(size_t)l * kTiers + t].push_back(h & 0x3fffffffu);
-        }
         for (int64_t p = 0; p < g.max_pages_per_seq; ++p) row[p] = KV_NO_BLOCK;
     }
     a->len[seq] = 0;
@@ -312,25 +326,21 @@ kv_status kv_check_block_table(const kv_alloc* a, const uint32_t* bt) {
     if (!a || !bt) return fail(KV_EINVAL, "NULL argument");
     const kv_geometry& g = a->g;
     for (int l = 0; l < g.num_layers; ++l) {
-        std::vector<std::vector<uint8_t>> used(kTiers);
-        for (int t = 0; t < kTiers; ++t) used[t].assign(a->capacity[(size_t)l * kTiers + t], 0);
         for (int s = 0; s < g.max_seqs; ++s) {
             const uint32_t* row = bt + ((size_t)l * g.max_seqs + s) * g.max_pages_per_seq;
-            const int64_t pages = (a->len[s] + g.page_size - 1) / g.page_size;
+            const std::vector<uint32_t>& mine = a->owned[(size_t)l * g.max_seqs + s];
             for (int64_t p = 0; p < g.max_pages_per_seq; ++p) {
                 const uint32_t h = row[p];
-                if (p >= pages) {
+                if (p >= (int64_t)mine.size()) {
                     if (h != KV_NO_BLOCK)
                         return fail(KV_EINVAL, "layer %d seq %d page %lld: stale handle", l, s,
                                     (long long)p);
                     continue;
                 }
-                const uint32_t t = h >> 30, i = h & 0x3fffffffu;
-                if (h == KV_NO_BLOCK || t >= (uint32_t)kTiers || i >= a->capacity[(size_t)l * kTiers + t])
-                    return fail(KV_EINVAL, "layer %d seq %d page %lld: invalid handle 0x%08x", l,
-                                s, (long long)p, h);
-                if (used[t][i]++)
-                    return fail(KV_EINVAL, "layer %d: block %u of tier %u used twice", l, i, t);
+                if (h != mine[p])
+                    return fail(KV_EINVAL,
+                                "layer %d seq %d page %lld: handle 0x%08x, but block 0x%08x was "
+                                "handed out for it", l, s, (long long)p, h, mine[p]);
             }
         }
     }

@@ -64,9 +64,14 @@ kv_status kv_controller_create(int num_layers, const int* initial_bits, double a
     c->alpha = alpha;
     c->tau0 = tau0;
     c->l0 = l0;
-    c->ema.assign(3 * (size_t)num_layers, 0.0);
-    c->seen.assign(3 * (size_t)num_layers, 0);
-    c->bits.assign(initial_bits, initial_bits + num_layers);
+    try {
+        c->ema.assign(3 * (size_t)num_layers, 0.0);
+        c->seen.assign(3 * (size_t)num_layers, 0);
+        c->bits.assign(initial_bits, initial_bits + num_layers);
+    } catch (const std::bad_alloc&) {
+        delete c;
+        return kvq::fail(KV_EINVAL, "out of host memory");
+    }
     *out = c;
     return kvq::ok();
 }

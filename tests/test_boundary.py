@@ -335,6 +335,40 @@ def test_check_block_table_catches_corruption():
         a.kv_check_block_table(bad)
 
 
+def test_check_block_table_catches_swapped_handles():
+    """two sequences' valid, distinct handles exchanged: every handle is still valid and used
+    once, but neither is the one handed out for that page"""
+    a = make_alloc()
+    a.kv_alloc_extend(0, 40)
+    a.kv_alloc_extend(1, 40)
+    bad = a.bt.copy()
+    bad[1, 0, 2], bad[1, 1, 2] = a.bt[1, 1, 2], a.bt[1, 0, 2]
+    with pytest.raises(kvq.KVError) as e:
+        a.kv_check_block_table(bad)
+    assert "handed out" in str(e.value)
+
+
+def test_free_returns_the_allocators_own_blocks_whatever_the_table_holds():
+    """a table edited after the blocks were handed out (here: one handle copied over another)
+    cannot make the free return a block twice: the pools come back to their capacity and later
+    sequences still get distinct blocks"""
+    a = make_alloc(cap=8)
+    a.kv_alloc_extend(0, 48)
+    a.kv_alloc_extend(1, 32)
+    a.bt[0, 0, 1] = a.bt[0, 0, 0]               # corrupt seq 0's row in layer 0
+    a.kv_alloc_free_seq(0)
+    assert np.all(a.bt[:, 0] == kvq.KV_NO_BLOCK)
+    assert a.kv_alloc_free_blocks(0, 4) == 6 and a.kv_alloc_free_blocks(1, 8) == 6
+    a.kv_alloc_free_seq(1)
+    assert a.kv_alloc_free_blocks(0, 4) == 8 and a.kv_alloc_free_blocks(1, 8) == 8
+    a.kv_alloc_extend(0, 64)
+    a.kv_alloc_extend(1, 64)                    # all 8 blocks of each pool
+    a.kv_check_block_table()
+    for l in range(2):
+        idx = sorted(int(h) & 0x3FFFFFFF for h in a.bt[l, :2, :4].ravel())
+        assert idx == list(range(8))
+
+
 def test_extend_argument_errors():
     a = make_alloc()
     with pytest.raises(kvq.KVError):
