@@ -402,7 +402,12 @@ int kv_decode_step_pages_per_split_for(const kv_geometry* g, int batch, const in
     if (check_geometry(g) != KV_OK || batch < 1 || batch > g->max_seqs || !pos_host ||
         n_new < 0 || n_new > kMaxFusedNew)
         return 0;
-    std::vector<int32_t> ctx(batch);
+    std::vector<int32_t> ctx;
+    try {
+        ctx.resize(batch);
+    } catch (const std::bad_alloc&) {
+        return 0;
+    }
     int64_t longest = 0, shortest = INT64_MAX;
     for (int s = 0; s < batch; ++s) {
         if (pos_host[s] < 0) return 0;
