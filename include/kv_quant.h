@@ -40,8 +40,8 @@
  *   Quantizer over a group with absolute maximum a: scale s = smallest fp16 >= a/qmax_b
  *   (0 if a == 0), code = round-half-even(x/s); both decided in IEEE binary32, which equals the
  *   exact rational result for fp16 inputs ([Kaizen] "symmetric uniform quantization").
- * Asymmetric format (kv_geometry.asymmetric = 1; [EchoKV] "Future work": per-token KIVI
- *   INT2/4/8 storage in the paged cache, with the KIVI-style quantizer of "Show the math"):
+ * Asymmetric format (kv_geometry.asymmetric = 1; [EchoKV] "Future work": the paged cache
+ *   itself held at INT2/4/8 in KIVI's form, with the KIVI-style quantizer of "Show the math"):
  *   the same groups; a section of S_b = P*D*b/4 + 4*D + 4*P bytes holds K codes, K zero points
  *   (D fp16), K scales (D fp16), V codes, V zero points (P fp16), V scales (P fp16). A group
  *   with minimum m and maximum M gets the zero point m (+0 for a zero minimum), the scale

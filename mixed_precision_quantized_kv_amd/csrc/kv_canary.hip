@@ -3,8 +3,9 @@
 // EchoKV, "Show the math": for each layer and each candidate width b in {2, 4, 8},
 //   delta_b = KL( softmax(Q K_ref^T) || softmax(Q quant_b(K_ref)^T) ),
 // summed over keys and averaged over the queries. K_ref is the per-layer FP16 ring of the
-// newest keys ("The absolute canary"); "Do we store the whole cache in FP16?": the canary
-// compares the ring against a temporary INT2/INT4/INT8 copy of those same keys.
+// newest keys ("The absolute canary"); "Do we store the whole cache in FP16?": only the ring
+// is kept at full precision, and the canary measures it against short-lived quantized copies
+// of its own keys at each candidate width.
 // quant_b is the cache's own quantizer (one scale per page and channel), so complete pages in
 // the ring get exactly the codes the cache stores.
 //

@@ -7,8 +7,8 @@
  *
  * What it computes (sources are the three web pages studied for this project):
  *   - EchoKV (jaizunt.github.io/echokv.html), "How EchoKV works": every decode step the key is
- *     written into a per-layer FP16 ring of the last 64 keys before it is quantized into the paged
- *     cache; "What happens to old blocks...": a block keeps the bit-width it was admitted with and
+ *     first goes to the layer's FP16 ring (its 64 newest keys), and only then is it quantized
+ *     into the paged cache; "What happens to old blocks...": a block keeps the bit-width it was admitted with and
  *     paged attention reads each block at its stored width; "Show the math": the canary
  *     KL(softmax(Q K^T) || softmax(Q quant_b(K)^T)), summed over keys, averaged over queries,
  *     one number per (layer, b) for b in {2,4,8}.
@@ -40,9 +40,9 @@
  *   tier 3 <-> b = 16, plain FP16 (EchoKV, "How EchoKV works": a layer's initial state before
  *   the canary first fires): a section is 4*P*D bytes, the keys at index t*D + c then the values
  *   at index ((t/4)*D + c)*4 + t%4, fp16 each, no scales; empty slots are +0.
- * Asymmetric format (geometry flag `asymmetric`; EchoKV, "Future work": per-token KIVI INT2/4/8
- *   storage in the paged cache): the same groups (K per page and channel, V per token) with
- *   the asymmetric quantizer below; a section is S_b = P*D*b/4 + 4*D + 4*P bytes:
+ * Asymmetric format (geometry flag `asymmetric`; EchoKV, "Future work": the paged cache itself
+ *   held at INT2/4/8 in KIVI's asymmetric form): the same groups (K per page and channel, V per
+ *   token) with the asymmetric quantizer below; a section is S_b = P*D*b/4 + 4*D + 4*P bytes:
  *     K codes, K zero points (D fp16), K scales (D fp16), V codes, V zero points (P fp16),
  *     V scales (P fp16);
  *   the field of a code is the code u in [0, 2^b - 1] itself, and an element is z + u * s.

@@ -1,6 +1,6 @@
 """GPU parity of the asymmetric cache format (kv_geometry.asymmetric = 1) against the oracle.
 
-EchoKV, "Future work": per-token KIVI INT2/4/8 storage in the paged cache; "Show the math": the
+EchoKV, "Future work": the paged cache itself held at INT2/4/8 in KIVI's form; "Show the math": the
 KIVI-style quantizer (zero point and scale from a group's minimum and maximum). Same bar as the
 symmetric format: packed codes, zero points, scales and the ring bit-exact; attention rows within
 2e-3 of the oracle's fp64 result (per row: max |err| / max |ref|); the fused step equal to the
