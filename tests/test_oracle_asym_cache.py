@@ -1,7 +1,7 @@
 """Pins for the oracle's asymmetric cache format (the geometry flag `asymmetric`).
 
-EchoKV, "Future work" (upstreaming into vLLM): its fork stores the paged cache in per-token KIVI
-INT2/4/8 form, i.e. with the asymmetric quantizer ("Show the math": zero point and scale from a
+EchoKV, "Future work" (upstreaming into vLLM): its fork keeps the paged cache itself at INT2/4/8
+in KIVI's form, i.e. with the asymmetric quantizer ("Show the math": zero point and scale from a
 group's minimum and maximum). The reading here keeps the cache's groups (Behavior-Guided KV-Cache
 Quantization, "K/V Role-Aware Low-Bit Quantization": keys per page and channel, values per token)
 and gives every group a zero point m (its minimum), a scale s = RU16((max - m) / (2^b - 1)) and
