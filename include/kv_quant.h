@@ -206,6 +206,8 @@ kv_status kv_quant_write(const kv_geometry* g, const kv_layer_pools* pools, cons
 *   ctx_len  dev int32 [batch], each in [0, max_ctx_len]; a zero length gives a zero row
  *   q        dev fp16 [batch][H_q][D] (4-byte aligned);  out  dev fp32 [batch][H_q][D] (16-byte aligned)
  *   max_ctx_len    host upper bound on ctx_len, sizes the launch (<= max_pages_per_seq * P)
+ *   softmax_scale  finite, of either sign (0 gives the mean of V^ over the context); a NaN or
+ *                  infinite scale is KV_EINVAL
  *   pages_per_split  pages one workgroup reads (even, >= 2); 0 = chosen by the library
  *   workspace  dev, >= kv_decode_workspace_bytes(...) bytes, zero-filled before its first use;
  *              the call leaves it ready for the next call on the same geometry, whatever that
@@ -284,7 +286,8 @@ int       kv_decode_step_pages_per_split_for(const kv_geometry* g, int batch, co
  * for each sequence the n = min(seq_len[s], R) newest keys (positions seq_len-n .. seq_len-1).
  * quant_b is the cache's own quantizer, grouped by each key's page (one scale per page and
  * channel): the symmetric one, or the asymmetric one (as kv_canary_kl_asym) for a geometry with
- * asymmetric = 1; the copies are temporary. Rows use the softmax_scale of attention.
+ * asymmetric = 1; the copies are temporary. Rows use the softmax_scale of attention (finite;
+ * otherwise KV_EINVAL).
  *   batch    1 .. max_seqs (a mean over no rows is undefined); 0 is KV_EINVAL
  *   ring     dev fp16 [max_seqs][R][H_kv][D] (16-byte aligned);  seq_len dev int32 [batch], >= 0
  *   q        dev fp16 [batch][H_q][D] (16-byte aligned)

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -469,7 +470,8 @@ kv_status kv_decode_attn(const kv_geometry* g, const kv_layer_pools* pools, cons
     const size_t need = kvq::decode_workspace_bytes(*g, batch, splits);
     if (workspace_bytes < need)
         return fail(KV_EINVAL, "workspace %zu bytes, %zu needed", workspace_bytes, need);
-    if (!(softmax_scale == softmax_scale)) return fail(KV_EINVAL, "softmax_scale is NaN");
+    if (!std::isfinite(softmax_scale))
+        return fail(KV_EINVAL, "softmax_scale %g is not finite", (double)softmax_scale);
     return hip_status(kvq::launch_decode_attn(*g, pool_ptrs(pools), bt, ctx_len, batch, splits, pps,
                                               q, softmax_scale, out, workspace,
                                               static_cast<hipStream_t>(stream)),
@@ -500,7 +502,8 @@ kv_status kv_decode_step(const kv_geometry* g, const kv_layer_pools* pools, cons
     const size_t need = kvq::decode_workspace_bytes(*g, batch, splits);
     if (workspace_bytes < need)
         return fail(KV_EINVAL, "workspace %zu bytes, %zu needed", workspace_bytes, need);
-    if (!(softmax_scale == softmax_scale)) return fail(KV_EINVAL, "softmax_scale is NaN");
+    if (!std::isfinite(softmax_scale))
+        return fail(KV_EINVAL, "softmax_scale %g is not finite", (double)softmax_scale);
     return hip_status(kvq::launch_decode_step(*g, pool_ptrs(pools), bt, pos, batch, n_new, k_new,
                                               v_new, ring, splits, pps, q, softmax_scale, out,
                                               workspace, static_cast<hipStream_t>(stream)),
@@ -537,7 +540,8 @@ kv_status kv_decode_step_noalloc(const kv_geometry* g, const kv_layer_pools* poo
         return fail(KV_EINVAL,
                     "the split partials need %zu bytes (%d splits); the static scratch holds %zu",
                     need, splits, room);
-    if (!(softmax_scale == softmax_scale)) return fail(KV_EINVAL, "softmax_scale is NaN");
+    if (!std::isfinite(softmax_scale))
+        return fail(KV_EINVAL, "softmax_scale %g is not finite", (double)softmax_scale);
     return hip_status(kvq::launch_decode_step_static(*g, pool_ptrs(pools), bt, pos, batch, n_new,
                                                      k_new, v_new, ring, splits, pps, q,
                                                      softmax_scale, out,
@@ -573,7 +577,8 @@ static kv_status canary(const kv_geometry* g, const uint16_t* ring, const int32_
     const size_t need = kvq::canary_workspace_bytes(*g, 1, 1, batch);
     if (workspace_bytes < need)
         return fail(KV_EINVAL, "workspace %zu bytes, %zu needed", workspace_bytes, need);
-    if (!(softmax_scale == softmax_scale)) return fail(KV_EINVAL, "softmax_scale is NaN");
+    if (!std::isfinite(softmax_scale))
+        return fail(KV_EINVAL, "softmax_scale %g is not finite", (double)softmax_scale);
     return hip_status(kvq::launch_canary(*g, ring, seq_len, batch, q, softmax_scale, asymmetric,
                                          kl_out, kl_rows, workspace,
                                          static_cast<hipStream_t>(stream)),
@@ -611,7 +616,8 @@ kv_status kv_canary_kl_layers(const kv_geometry* g, int num_layers, const uint16
         kvq::canary_workspace_bytes(*g, kvq::canary_counter_layers(*g), num_layers, batch);
     if (workspace_bytes < need)
         return fail(KV_EINVAL, "workspace %zu bytes, %zu needed", workspace_bytes, need);
-    if (!(softmax_scale == softmax_scale)) return fail(KV_EINVAL, "softmax_scale is NaN");
+    if (!std::isfinite(softmax_scale))
+        return fail(KV_EINVAL, "softmax_scale %g is not finite", (double)softmax_scale);
     return hip_status(kvq::launch_canary_layers(*g, num_layers, rings, seq_len, batch, q,
                                                 softmax_scale, kl_out, kl_rows, workspace,
                                                 static_cast<hipStream_t>(stream)),

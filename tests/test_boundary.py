@@ -5,6 +5,7 @@ EchoKV, "How EchoKV works": the tier vector routes future blocks to the right po
 happens to old blocks...": already-allocated blocks keep their admit-time width.
 """
 import ctypes
+import math
 import os
 import subprocess
 
@@ -133,6 +134,23 @@ def test_kernel_calls_reject_bad_arguments_without_launching():
         with pytest.raises(kvq.KVError) as e:       # attention and canary take 1..max_seqs rows
             call()
         assert e.value.status == kvq.KV_EINVAL and "batch 0" in str(e.value)
+    need = kvq.kv_decode_workspace_bytes(g, 1, 16)
+    cneed = kvq.kv_canary_workspace_bytes(g, 1)
+    for bad_scale in (math.inf, -math.inf, math.nan):   # the scale must be finite, of either sign
+        for call in (lambda: kvq.kv_decode_attn(g, pools, 256, 256, 1, 16, 256, bad_scale, 256, 256,
+                                                need, 0, stream=0),
+                     lambda: kvq.kv_decode_step(g, pools, 256, 256, 1, 1, 256, 256, 256, 16, 256,
+                                                bad_scale, 256, 256, need, 0, stream=0),
+                     lambda: kvq.kv_decode_step_noalloc(g, pools, 256, 256, 1, 1, 256, 256, 256, 16,
+                                                        256, bad_scale, 256, 0, stream=0),
+                     lambda: kvq.kv_canary_kl(g, 256, 256, 1, 256, bad_scale, 256, None, 256, cneed,
+                                              stream=0),
+                     lambda: kvq.kv_canary_kl_layers(g, [256], 256, 1, [256], bad_scale, 256, None,
+                                                     256, kvq.kv_canary_layers_workspace_bytes(g, 1, 1),
+                                                     stream=0)):
+            with pytest.raises(kvq.KVError) as e:
+                call()
+            assert e.value.status == kvq.KV_EINVAL and "softmax_scale" in str(e.value)
     g600 = kvq.geometry(1, 8, 2, 64, 1, 600)
     ctx = 513 * 16                                  # 513 pages at 2 per split: 257 splits
     wsb = kvq.kv_decode_workspace_bytes(g600, 1, ctx, 2)

@@ -259,6 +259,26 @@ def test_softmax_scale_zero_and_identical_keys():
         assert rowwise_rel_err(got, L.oracle_attn(q, scale=scale)).max() <= ATTN_TOL
 
 
+def test_negative_softmax_scale():
+    """a scale of either sign is a valid softmax temperature: with a negative one the weights
+    favour the smallest logits; attention over mixed widths and the canary against the oracle"""
+    case_banner("negative softmax scale")
+    g = np.random.default_rng(4)
+    tiers = [[0, 1, 2, 3, 1, 0, 2, 1, 2, 0]]
+    L = LayerPair(16, 4, 128, 1, 10, tiers, seed=4)
+    K = synth.normal_f16(g, (1, 150, 4, 128))
+    V = synth.normal_f16(g, (1, 150, 4, 128))
+    L.write(K, V)
+    q = synth.normal_f16(g, (1, 16, 128))
+    for scale in (-0.088, -1.0):
+        for pps in (0, 2):
+            got, _ = L.attn(q, scale=scale, pages_per_split=pps)
+            assert rowwise_rel_err(got, L.oracle_attn(q, scale=scale)).max() <= ATTN_TOL
+        kl, rows = L.canary(q, scale=scale)
+        okl, orows = L.oracle_canary(q, scale=scale)
+        assert np.abs(kl - okl).max() <= 1e-4 and np.abs(rows - orows).max() <= 1e-4
+
+
 @pytest.mark.parametrize("zero_values", [True, False])
 def test_split_partials_that_are_exactly_zero(zero_values):
     """split partials whose running maximum is exactly +0.0 (every logit -3 in log2 units, the
