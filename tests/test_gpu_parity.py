@@ -334,6 +334,39 @@ def test_split_counts_up_to_the_limit(hq, hkv, d, mix):
         assert L.tickets_zero(ws), pps
 
 
+@pytest.mark.parametrize("hq,hkv,d", [(40, 8, 128), (8, 2, 64)])
+@pytest.mark.parametrize("mix", ["int2", "mixed"])
+def test_splits_longer_than_a_wave_chunk_of_64_pages(hq, hkv, d, mix):
+    """a caller's plan of more than 512 pages per split gives each of the eight waves more than
+    64 pages, which the register-held handle chunk cannot hold: the wave then walks its pages
+    through the general loop, reading handles from the table as it goes. 1100 pages (a ragged
+    last page) at 1100 pages per split (one split, about 137 pages a wave) and at 520 (three
+    splits), through the attention and through a fused step of three tokens"""
+    case_banner(f"splits beyond 512 pages hq={hq} hkv={hkv} d={d} {mix}")
+    g = np.random.default_rng(d + 3 * len(mix))
+    N = 1100 * 16 - 5
+    pages = synth.pages_for(N + 3)
+    tiers = [list(g.integers(0, 4, size=pages))] if mix == "mixed" else [[0] * pages]
+    L = LayerPair(hq, hkv, d, 1, pages, tiers, seed=d + 11)
+    L.write(synth.normal_f16(g, (1, N, hkv, d)), synth.normal_f16(g, (1, N, hkv, d)))
+    q = synth.normal_f16(g, (1, hq, d))
+    ref = L.oracle_attn(q)
+    for pps in (1100, 520):
+        got, ws = L.attn(q, pages_per_split=pps)
+        err = rowwise_rel_err(got, ref)
+        print(f"  attn pps={pps} max rel err {err.max():.3e}", flush=True)
+        assert err.max() <= ATTN_TOL, (pps, err.max())
+        assert L.tickets_zero(ws), pps
+    got, ws = L.step(synth.normal_f16(g, (1, 3, hkv, d)), synth.normal_f16(g, (1, 3, hkv, d)), q,
+                     pages_per_split=1100)
+    bad, ring_ok = L.compare_bytes()
+    assert not bad and ring_ok, bad[:3]
+    err = rowwise_rel_err(got, L.oracle_attn(q))
+    print(f"  fused step pps=1100 max rel err {err.max():.3e}", flush=True)
+    assert err.max() <= ATTN_TOL
+    assert L.tickets_zero(ws)
+
+
 @pytest.mark.parametrize("R", [16, 48, 128])
 @pytest.mark.parametrize("d", [64, 128])
 def test_ring_sizes(R, d):
