@@ -5,7 +5,9 @@
  * kv_canary_kl fires the canary. Device memory comes from hipMalloc; the results are compared
  * with the oracle (libkvq_oracle) on the same inputs: pool bytes and the ring bit for bit,
  * attention rows within 2e-3 of the oracle (relative to the row's largest value), canary KL
- * within 1e-4. Prints one line per failed check and exits with the number of failures. */
+ * within 1e-4. Prints one line per failed check and exits with the number of failures.
+ * Arguments: "asym" stores the cache in the asymmetric format (zero point + scale per group);
+ * "noalloc" takes the step through kv_decode_step_noalloc (no workspace argument). */
 #include <hip/hip_runtime_api.h>
 #include <math.h>
 #include <stdint.h>
@@ -81,7 +83,7 @@ static void* dev_alloc(size_t bytes) {
     return p;
 }
 
-int main(void) {
+int main(int argc, char** argv) {
     const int prefill[SEQS] = {200, 17, 330};
     const int widths_in_order[4] = {16, 8, 4, 2};
     /* each sequence's length after each width's turn: its pages come from that width's pool */
@@ -99,6 +101,18 @@ int main(void) {
     kv_layer_pools pools;
     int t, s, i, w;
     const float scale = 1.0f / sqrtf((float)D);
+    int asym = 0, noalloc = 0;
+
+    for (i = 1; i < argc; ++i) {
+        if (strcmp(argv[i], "asym") == 0) asym = 1;
+        else if (strcmp(argv[i], "noalloc") == 0) noalloc = 1;
+        else {
+            printf("unknown argument %s\n", argv[i]);
+            return 102;
+        }
+    }
+    printf("format %s, step %s\n", asym ? "asymmetric" : "symmetric",
+           noalloc ? "kv_decode_step_noalloc" : "kv_decode_step");
 
     memset(&g, 0, sizeof g);
     g.num_layers = 1;
@@ -109,14 +123,14 @@ int main(void) {
     g.ring_size = R;
     g.max_seqs = SEQS;
     g.max_pages_per_seq = MAXP;
-    g.asymmetric = 0;
+    g.asymmetric = asym;
     memset(&og, 0, sizeof og);
     og.num_q_heads = HQ;
     og.num_kv_heads = HKV;
     og.head_dim = D;
     og.page_size = P;
     og.ring_size = R;
-    og.asymmetric = 0;
+    og.asymmetric = asym;
 
     /* the block table: every tier gets pages, in the order FP16 -> INT8 -> INT4 -> INT2 */
     for (t = 0; t < KV_NUM_TIERS; ++t) capacity[t] = SEQS * MAXP;
@@ -208,8 +222,12 @@ int main(void) {
             ws_bytes = kv_decode_workspace_bytes(&g, SEQS, max_ctx, 0);
             CHECK(ws_bytes > 0, "workspace size");
             ws_d = dev_alloc(ws_bytes);
-            KV_OK_(kv_decode_step(&g, &pools, bt_d, pos_d, SEQS, NEW, knew_d, vnew_d, ring_d,
-                                  max_ctx, q_d, scale, out_d, ws_d, ws_bytes, 0, NULL));
+            if (noalloc)
+                KV_OK_(kv_decode_step_noalloc(&g, &pools, bt_d, pos_d, SEQS, NEW, knew_d, vnew_d,
+                                              ring_d, max_ctx, q_d, scale, out_d, 0, NULL));
+            else
+                KV_OK_(kv_decode_step(&g, &pools, bt_d, pos_d, SEQS, NEW, knew_d, vnew_d, ring_d,
+                                      max_ctx, q_d, scale, out_d, ws_d, ws_bytes, 0, NULL));
             HIP_OK(hipDeviceSynchronize());
             HIP_OK(hipFree(knew_d));
             HIP_OK(hipFree(vnew_d));
