@@ -103,6 +103,7 @@ class Pools:
 
     def __init__(self, g: Geom, capacity):
         cap = [int(c) for c in capacity] + [0] * (4 - len(capacity))
+        self.capacity = cap
         self.arrays = [np.zeros(max(1, cap[t] * block_bytes(g, TIER_BITS[t])), dtype=np.uint8)
                        for t in range(4)]
         self._ptrs = (ctypes.c_void_p * 4)(*[a.ctypes.data for a in self.arrays])
@@ -201,6 +202,22 @@ def v_zero(g, sec: np.ndarray, bits, t):
 
 
 # ---- the three path operations ----
+def _check_pages(g: Geom, pools: Pools, bt: np.ndarray, first: np.ndarray, end: np.ndarray,
+                 what: str) -> None:
+    """every page p in [first[s], end[s]) of row s lies in the table and holds a handle of a
+    block its pool has, so that the C code never reaches outside the host arrays"""
+    for s in range(bt.shape[0]):
+        if end[s] <= first[s]:
+            continue
+        if first[s] < 0 or end[s] > bt.shape[1]:
+            raise ValueError(f"{what}: row {s} pages {first[s]}..{end[s] - 1} outside the table")
+        h = bt[s, first[s]:end[s]].astype(np.int64)
+        tier, idx = h >> 30, h & 0x3FFFFFFF
+        cap = np.array(pools.capacity, dtype=np.int64)[tier]
+        if (h == 0xFFFFFFFF).any() or (idx >= cap).any():
+            raise ValueError(f"{what}: row {s} has a page without a block of its pool")
+
+
 def quant_write(g: Geom, pools: Pools, bt: np.ndarray, pos: np.ndarray, k_new: np.ndarray,
                 v_new: np.ndarray, ring: np.ndarray) -> None:
     """In place on pools and ring. bt [B][max_pages] uint32; k_new/v_new [B][n][Hkv][D] uint16."""
@@ -210,6 +227,13 @@ def quant_write(g: Geom, pools: Pools, bt: np.ndarray, pos: np.ndarray, k_new: n
     v_new = np.ascontiguousarray(v_new, dtype=np.uint16)
     assert ring.dtype == np.uint16 and ring.flags["C_CONTIGUOUS"]
     B, n = k_new.shape[0], k_new.shape[1]
+    hd = (g.num_kv_heads, g.head_dim)
+    if k_new.shape[2:] != hd or v_new.shape != k_new.shape or pos.shape != (B,) or \
+            bt.shape[0] < B or ring.shape[0] < B or ring.shape[1:] != (g.ring_size,) + hd:
+        raise ValueError("oracle write: shapes do not match the geometry")
+    P = g.page_size
+    _check_pages(g, pools, bt[:B], pos // P, (pos + n + P - 1) // P if n else pos // P,
+                 "oracle write")
     rc = lib().orc_quant_write(ctypes.byref(g), pools.ptr, _ptr(bt), bt.shape[1], _ptr(pos), B, n,
                                _ptr(k_new), _ptr(v_new), _ptr(ring))
     if rc != 0:
@@ -232,6 +256,10 @@ def decode_attn(g: Geom, pools: Pools, bt: np.ndarray, ctx_len: np.ndarray, q: n
     ctx_len = np.ascontiguousarray(ctx_len, dtype=np.int32)
     q = np.ascontiguousarray(q, dtype=np.uint16)
     B = q.shape[0]
+    if q.shape[1:] != (g.num_q_heads, g.head_dim) or ctx_len.shape != (B,) or bt.shape[0] < B:
+        raise ValueError("oracle attention: shapes do not match the geometry")
+    _check_pages(g, pools, bt[:B], np.zeros(B, np.int64), (ctx_len + g.page_size - 1) // g.page_size,
+                 "oracle attention")
     out = np.zeros((B, g.num_q_heads, g.head_dim), dtype=np.float64)
     rc = lib().orc_decode_attn(ctypes.byref(g), pools.ptr, _ptr(bt), bt.shape[1], _ptr(ctx_len), B,
                                _ptr(q), float(softmax_scale), _ptr(out))

@@ -242,3 +242,28 @@ def test_section_layout_hand_offsets(orc):
     assert int(sec[1030]) | (int(sec[1031]) << 8) == 0x3800
     assert sec[1422] == nn[5, 3] + 128
     assert int(sec[2186]) | (int(sec[2187]) << 8) == 0x3400
+
+
+def test_oracle_calls_refuse_pages_outside_their_pools(orc):
+    """the oracle's wrappers check the pages a call touches before the C code runs: a missing
+    block, an index past its pool, a page past the table and a wrong shape raise ValueError"""
+    g = orc.geom(8, 2, 64)
+    pools = orc.Pools(g, [2, 2, 2, 2])
+    K = np.zeros((1, 20, 2, 64), dtype=np.uint16)
+    ring = np.zeros((1, g.ring_size, 2, 64), dtype=np.uint16)
+    pos = np.zeros(1, np.int32)
+    good = np.array([[(1 << 30) | 0, (1 << 30) | 1, 0xFFFFFFFF]], dtype=np.uint32)
+    orc.quant_write(g, pools, good, pos, K, K, ring)                    # pages 0 and 1
+    for bt in (np.array([[(1 << 30) | 0, 0xFFFFFFFF, 0xFFFFFFFF]], dtype=np.uint32),   # no block
+               np.array([[(1 << 30) | 0, (1 << 30) | 2, 0xFFFFFFFF]], dtype=np.uint32),  # past pool
+               np.array([[(1 << 30) | 0]], dtype=np.uint32)):                          # past table
+        with pytest.raises(ValueError):
+            orc.quant_write(g, pools, bt, pos, K, K, ring)
+    with pytest.raises(ValueError):
+        orc.quant_write(g, pools, good, pos, K, K, ring[:, :16])       # ring of the wrong size
+    q = np.zeros((1, 8, 64), dtype=np.uint16)
+    orc.decode_attn(g, pools, good, np.array([20], np.int32), q, 0.125)
+    with pytest.raises(ValueError):
+        orc.decode_attn(g, pools, good, np.array([40], np.int32), q, 0.125)   # page 2 has no block
+    with pytest.raises(ValueError):
+        orc.decode_attn(g, pools, good, np.array([20], np.int32), q[:, :4], 0.125)
