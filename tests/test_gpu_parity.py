@@ -367,6 +367,42 @@ def test_splits_longer_than_a_wave_chunk_of_64_pages(hq, hkv, d, mix):
     assert L.tickets_zero(ws)
 
 
+def test_many_short_sequences():
+    """a wide batch of short, ragged sequences: 300 sequences of 0..120 tokens and 8 KV heads
+    give 2400 (sequence, head) groups, one split each under the library's plan (and up to four
+    at two pages a split), widths mixed per page; attention, a fused step and the canary against
+    the oracle"""
+    case_banner("300 short sequences")
+    g = np.random.default_rng(300)
+    B, hq, hkv, d = 300, 32, 8, 128
+    lens = g.integers(0, 121, size=B)
+    lens[:3] = (0, 1, 16)
+    max_pages = 10
+    tiers = [list(g.integers(0, 4, size=max_pages)) for _ in range(B)]
+    L = LayerPair(hq, hkv, d, B, max_pages, tiers, seed=300)
+    for s_, n in enumerate(lens):
+        if n:
+            L.write(synth.normal_f16(g, (1, int(n), hkv, d)), synth.normal_f16(g, (1, int(n), hkv, d)),
+                    rows=[s_])
+    q = synth.normal_f16(g, (B, hq, d))
+    ref = L.oracle_attn(q)
+    for pps in (0, 2):
+        got, ws = L.attn(q, pages_per_split=pps)
+        err = rowwise_rel_err(got, ref)
+        print(f"  attn pps={pps} max rel err {err.max():.3e}", flush=True)
+        assert err.max() <= ATTN_TOL and not got[lens == 0].any()
+        assert L.tickets_zero(ws)
+    got, ws = L.step(synth.normal_f16(g, (B, 3, hkv, d)), synth.normal_f16(g, (B, 3, hkv, d)), q)
+    bad, ring_ok = L.compare_bytes()
+    assert not bad and ring_ok, bad[:3]
+    err = rowwise_rel_err(got, L.oracle_attn(q))
+    print(f"  fused step max rel err {err.max():.3e}", flush=True)
+    assert err.max() <= ATTN_TOL and L.tickets_zero(ws)
+    kl, rows = L.canary(q)
+    okl, orows = L.oracle_canary(q)
+    assert np.abs(kl - okl).max() <= 1e-4 and np.abs(rows - orows).max() <= 1e-4
+
+
 @pytest.mark.parametrize("R", [16, 48, 128])
 @pytest.mark.parametrize("d", [64, 128])
 def test_ring_sizes(R, d):
