@@ -75,3 +75,52 @@ def test_graph_replays_match_eager(case):
             assert torch.equal(a, b), f"replay {rep} differs"
         _ = (out * 2).sum().item()                        # eager work between replays
     assert L.tickets_zero(ws) and not cws[:768].any()    # tickets left at zero
+
+
+def test_graph_replays_of_the_allocation_free_step():
+    """kv_decode_step_noalloc -- the entry point for callers that cannot allocate, such as code
+    under graph capture -- captured after one eager call and replayed four times with eager work
+    between the replays: every replay gives the eager call's outputs, ring and pools bit for
+    bit, and the captured step equals kv_decode_step with a caller workspace"""
+    print("\n[case] graph of kv_decode_step_noalloc", flush=True)
+    g = np.random.default_rng(8)
+    hq, hkv, d, lens = 32, 8, 128, [300, 1000, 777]
+    tiers = [list(g.integers(0, 4, size=66)) for _ in lens]
+    L = LayerPair(hq, hkv, d, len(lens), 66, tiers, seed=5)
+    for s, n in enumerate(lens):
+        L.write(synth.normal_f16(g, (1, n - 1, hkv, d)), synth.normal_f16(g, (1, n - 1, hkv, d)),
+                rows=[s])
+    B = len(lens)
+    pos_np = L.len.copy()
+    pos = to_dev_i32(pos_np)
+    k1_np = synth.normal_f16(g, (B, 1, hkv, d))
+    v1_np = synth.normal_f16(g, (B, 1, hkv, d))
+    q_np = synth.normal_f16(g, (B, hq, d))
+    k1, v1, q = to_dev_f16(k1_np), to_dev_f16(v1_np), to_dev_f16(q_np)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    max_ctx = int(L.len.max()) + 1
+    out = torch.zeros((B, hq, d), dtype=torch.float32, device="cuda")
+
+    def run():
+        kvq.kv_decode_step_noalloc(L.g, L.pools, L.bt_dev, pos, B, 1, k1, v1, L.ring, max_ctx, q,
+                                   scale, out, 0, stream=torch.cuda.current_stream().cuda_stream)
+
+    run()                                                 # eager
+    torch.cuda.synchronize()
+    ref = [out.clone(), L.ring.clone()] + [p.clone() for p in L.pools_t]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip([out, L.ring] + list(L.pools_t), ref):
+            assert torch.equal(a, b), f"replay {rep} differs"
+        _ = (out * 2).sum().item()                        # eager work between replays
+    # the same step through kv_decode_step with a caller workspace, on the same (already
+    # written: the write is idempotent) cache
+    got, ws = L.step(k1_np, v1_np, q_np)
+    assert np.array_equal(got, ref[0].cpu().numpy().astype(np.float64))
+    assert L.tickets_zero(ws)
